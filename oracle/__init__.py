@@ -1,0 +1,38 @@
+"""Plain float64 CPU oracle for layer-packed selective recompute with the
+mixed-cache logit bias.
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+package.  The product path (the HIP library and its Python binding) never
+imports it, and this package imports nothing from the product path.  The two
+share only the seeded input generators in ``workloads``.
+
+Sources (cited by title and section; no line numbers):
+* "Budgeted KV-Cache Repair for Evolving Contexts" (page 1): exact budget
+  (section 7.1, Eq. 3), sort-and-coalesce into execution intervals (section
+  3.2, Algorithm 1), sequential maximal-interval replay (section 7.1),
+  mixed-cache recurrence (section 13.2, Eq. 21-22), reusable tile plan
+  (section 13.2, Eq. 23-24).
+* The cross-attention reuse specification page (page 4): blocks (section
+  6.1), mixed cache and metadata (section 6.2), the seam set T_tau with the
+  asymmetric true-prefix rule (section 6.3), the biased operator F and its
+  degeneration (section 6.4).
+
+Arithmetic is float64 throughout (inputs are widened from their float32 /
+bf16 storage).  Matrix products use numpy's matmul as a library step; there
+is no blocking, fusion or reordering beyond the definitions.
+
+Readings where the pages are silent are listed in the design doc; every function
+here is pinned by tests under ``tests/`` (no function is parity-unpinned).
+"""
+from .repair_set import (BadBlocks, BadSupport, attn_tile_plan, budget, check_support,
+                         runs, seam_set, validate_blocks)
+from .layer import (FLAG_LOCAL, FLAG_SINK, attention_bias, biased_attention_row,
+                    interval_major, layer_repair, rms_norm, rope, silu, stack_repair)
+
+__all__ = [
+    "BadBlocks", "BadSupport", "attn_tile_plan", "budget", "check_support", "runs",
+    "seam_set", "validate_blocks", "FLAG_LOCAL", "FLAG_SINK", "attention_bias",
+    "biased_attention_row", "interval_major", "layer_repair", "rms_norm", "rope", "silu",
+    "stack_repair",
+]
