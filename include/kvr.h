@@ -1,0 +1,265 @@
+/*
+ * kvr.h - C ABI of libkvr: layer-packed selective recompute of a mixed
+ * KV cache (budgeted KV-cache repair) on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources cited by page title and section):
+ *   - "Budgeted KV-Cache Repair for Evolving Contexts", section 13.2
+ *     (mixed-cache recurrence, Eq. 21-22; reusable execution plan,
+ *     Eq. 23-24), section 3.3 (layer-major packed schedule), section 7.1
+ *     (exact budget, Eq. 3; only retained-suffix positions are selectable).
+ *   - The cross-attention reuse specification page, sections 6.1-6.4:
+ *     blocks [s_i, e_i), mixed cache L[t,l] = (K, V, m_t) with
+ *     m_t = (type, block id, global position), the seam set T_tau with the
+ *     asymmetric true-prefix rule, and the biased operator F whose logits
+ *     are <q,k>/sqrt(d) + alpha*[type=local] + beta*[key in S'].
+ *
+ * Conventions shared by every entry point:
+ *   - Every buffer is owned by the caller.  The library allocates no device
+ *     memory; scratch comes from the caller's workspace.  It keeps no pointer
+ *     after a call returns.
+ *   - "device" pointers point to GPU memory of the current HIP device;
+ *     "host" pointers to CPU memory.  Device pointers must be 16-byte
+ *     aligned.
+ *   - Calls enqueue work on `stream` (0 = the null stream) in order and
+ *     return; only the calls that say so synchronise.
+ *   - Host-side validation runs first and returns an error without touching
+ *     the device.  A failed HIP call returns KVR_ERR_HIP; the HIP error text
+ *     is then in kvr_last_error().
+ *   - The cache row index is the global position g_t (the mixed cache is
+ *     indexed by global position); RoPE angles and causal visibility both
+ *     use it.
+ */
+#ifndef KVR_H
+#define KVR_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVR_OK = 0,
+  KVR_ERR_INVALID_ARGUMENT = -1, /* null/misaligned pointer, bad size, non-finite scalar */
+  KVR_ERR_UNSUPPORTED = -2,      /* shape outside what the kernels implement        */
+  KVR_ERR_BAD_BLOCKS = -3,       /* blocks do not tile [0, N)                        */
+  KVR_ERR_BAD_SUPPORT = -4,      /* support not strictly increasing / out of range   */
+  KVR_ERR_CAPACITY = -5,         /* output arrays too small                          */
+  KVR_ERR_WORKSPACE = -6,        /* workspace smaller than kvr_workspace_bytes()     */
+  KVR_ERR_HIP = -7               /* a HIP runtime call or launch failed              */
+} kvr_status;
+
+/* Storage type of layer weights and the KV cache.  Activations crossing the
+ * boundary (x_in, x_out), RMSNorm gains and q/k/v biases are always float32.
+ * KVR_BF16 computes matrix products on bf16 operands with float32
+ * accumulation; KVR_F32 is float32 end to end. */
+typedef enum { KVR_F32 = 0, KVR_BF16 = 1 } kvr_dtype;
+
+/* Per-position metadata byte m_t (cross-attention reuse page, 6.2 / 6.4):
+ * bit 0 set = type local (KV does not match a full prefill), clear = global;
+ * bit 1 set = position is in the spurious-sink set S'. */
+enum { KVR_FLAG_LOCAL = 1u, KVR_FLAG_SINK = 2u };
+
+/* mode bits of kvr_build_repair_set */
+enum {
+  KVR_SEAM_ASYMMETRIC = 1u, /* true-prefix rule: skip B_1's trailing window, add B_m's (6.3) */
+  KVR_INIT_META = 2u        /* also write load-time metadata for all N positions           */
+};
+
+/* Attention tiling used by kvr_build_plan and the packed attention kernel:
+ * a query tile holds KVR_ATTN_QROWS (packed row, query head) pairs of one KV
+ * head group (pair p = r*G + h with G = n_q_heads / n_kv_heads), keys are
+ * visited in tiles of KVR_ATTN_KV_TILE positions. */
+enum { KVR_ATTN_QROWS = 128, KVR_ATTN_KV_TILE = 64 };
+
+typedef struct {
+  int32_t hidden;        /* model width; multiple of 64                            */
+  int32_t n_q_heads;     /* query heads Hq                                          */
+  int32_t n_kv_heads;    /* KV heads Hkv; Hq % Hkv == 0 (query head h reads h/(Hq/Hkv)) */
+  int32_t head_dim;      /* d: 64 or 128                                            */
+  int32_t intermediate;  /* SwiGLU width; multiple of 64                            */
+  float rms_eps;         /* RMSNorm epsilon (finite, >= 0)                          */
+  double rope_theta;     /* RoPE base; rotate-half pairing (i, i + d/2)             */
+  float alpha;           /* logit bias on local keys (finite)                       */
+  float beta;            /* logit bias on spurious-sink keys (finite)               */
+  kvr_dtype dtype;       /* storage of weights and cache                            */
+} kvr_config;
+
+/* One decoder layer.  Matrices are device, row-major [out, in] (PyTorch
+ * Linear), in cfg.dtype: wq [Hq*d, hidden] (head h owns rows h*d..h*d+d-1),
+ * wk / wv [Hkv*d, hidden], wo [hidden, Hq*d], w_gate / w_up
+ * [intermediate, hidden], w_down [hidden, intermediate].  attn_norm and
+ * mlp_norm are float32 [hidden]; bq [Hq*d], bk / bv [Hkv*d] are float32 and
+ * may all be NULL (no projection bias). */
+typedef struct {
+  const void *attn_norm, *wq, *wk, *wv, *bq, *bk, *bv, *wo, *mlp_norm, *w_gate, *w_up, *w_down;
+} kvr_layer_weights;
+
+/* One layer's cache: device K and V, each [N, Hkv, d] contiguous, cfg.dtype.
+ * Keys are stored after RoPE; values are not rotated. */
+typedef struct {
+  void *k, *v;
+} kvr_kv;
+
+/* Mixed-cache metadata shared by all layers (m_t has no layer index).
+ * flags: device uint8 [n_tokens] (KVR_FLAG_* bits); block_id: device int32
+ * [n_tokens] or NULL (only written by KVR_INIT_META). */
+typedef struct {
+  uint8_t* flags;
+  int32_t* block_id;
+  int32_t n_tokens;
+} kvr_meta;
+
+/* Output of kvr_build_repair_set; all device arrays.  T, run_start and
+ * run_len hold `cap` int32 each; counts holds 3 int32:
+ * counts[0] = |T|, counts[1] = R (number of maximal runs), counts[2] =
+ * status of the build (KVR_OK, KVR_ERR_BAD_BLOCKS or KVR_ERR_CAPACITY). */
+typedef struct {
+  int32_t *T, *run_start, *run_len, *counts;
+  int32_t cap;
+} kvr_repair_set;
+
+/*
+ * kvr_build_repair_set - recomputation set T_tau from block boundaries
+ * (cross-attention reuse page, 6.3), its maximal runs (the execution
+ * intervals of Budgeted KV-Cache Repair, section 3.2), and optionally the
+ * load-time metadata (6.2).
+ *
+ *   d_s, d_e   device int32 [m]: block starts / exclusive ends.  They must
+ *              tile [0, n_tokens): s_1 = 0, e_i = s_{i+1}, e_m = n_tokens,
+ *              every block non-empty; otherwise counts[2] = BAD_BLOCKS.
+ *   tau        seam half-width (>= 0).  Window at seam i|i+1: the last tau
+ *              positions of B_i and the first tau of B_{i+1}, each clipped to
+ *              its block.  With KVR_SEAM_ASYMMETRIC, B_1's trailing window is
+ *              dropped and B_m's trailing tau positions are added.  T is the
+ *              ascending set union.  m = 1 or tau = 0 gives T empty.
+ *   meta       needed (non-NULL, meta->n_tokens == n_tokens) with
+ *              KVR_INIT_META: flags[t] = LOCAL for t >= e_1, plus SINK at
+ *              every s_i with i >= 2; block_id[t] = i - 1 (when non-NULL).
+ *   out        device arrays (see kvr_repair_set).  |T| > out->cap gives
+ *              counts[2] = CAPACITY with T, runs and counts[0..1] undefined.
+ *   h_counts   host int32 [3] or NULL.  When given, counts are copied back,
+ *              the stream is synchronised and the device status is returned.
+ *              When NULL the call does not synchronise and returns KVR_OK
+ *              after the launch; the status is then only in counts[2].
+ */
+kvr_status kvr_build_repair_set(const int32_t* d_s, const int32_t* d_e, int32_t m,
+                                int32_t n_tokens, int32_t tau, uint32_t mode,
+                                const kvr_meta* meta, const kvr_repair_set* out,
+                                int32_t* h_counts, hipStream_t stream);
+
+/*
+ * kvr_check_support - checks an explicit support before execution, as the
+ * budgeted-repair page requires (section 13.2 / 7.1): d_T (device int32 [B])
+ * strictly increasing and inside [first_selectable, n_tokens).  d_result is
+ * a device int32 scratch word.  Synchronises the stream.  Returns KVR_OK or
+ * KVR_ERR_BAD_SUPPORT.  B = 0 is valid.
+ */
+kvr_status kvr_check_support(const int32_t* d_T, int32_t B, int32_t n_tokens,
+                             int32_t first_selectable, int32_t* d_result, hipStream_t stream);
+
+/*
+ * kvr_build_plan - reusable attention plan (Budgeted KV-Cache Repair,
+ * section 13.2, Eq. 23-24) for a sorted support d_T [B] and GQA group size
+ * `group` (= Hq/Hkv).  Query tile t covers pairs [t*QROWS, min(B*group,
+ * (t+1)*QROWS)); with u_min / u_max the positions of its first / last pair:
+ * d_n_full[t] = floor((u_min+1)/KV_TILE), d_n_total[t] =
+ * ceil((u_max+1)/KV_TILE).  Both outputs are device int32
+ * [ceil(B*group/QROWS)].  kvr_layer_repair / kvr_stack_repair build the
+ * same plan in their workspace; this entry point exposes it for checking.
+ */
+kvr_status kvr_build_plan(const int32_t* d_T, int32_t B, int32_t group, int32_t* d_n_full,
+                          int32_t* d_n_total, hipStream_t stream);
+
+/* Workspace bytes needed by kvr_layer_repair / kvr_stack_repair for this
+ * shape, support size B and context length; 0 on invalid arguments. */
+size_t kvr_workspace_bytes(const kvr_config* cfg, int32_t B, int32_t n_tokens);
+
+/*
+ * kvr_layer_repair - one layer of the layer-major packed recurrence
+ * (Budgeted KV-Cache Repair, section 13.2) with the biased operator F in
+ * physical-repair mode (cross-attention reuse page, 6.4):
+ *
+ *   n = RMSNorm(x) * attn_norm; q, k, v = n Wq^T (+bq), n Wk^T (+bk),
+ *   n Wv^T (+bv); RoPE on q, k at each row's position u_r = T[r];
+ *   before attention: cache.k[u_r] = k, cache.v[u_r] = v (rounded to
+ *   cfg.dtype), flags[u_r] &= ~(LOCAL | SINK)  (Eq. 21; type <- global);
+ *   o = softmax_j(<q, k_j>/sqrt(d) + alpha*local_j + beta*sink_j) v_j over
+ *   j = 0..u_r inclusive (Eq. 22 with the 6.4 logit form), query head h
+ *   reading KV head h / (Hq/Hkv);
+ *   h1 = x + o Wo^T;  y = h1 + Wdown(SiLU(n2 Wgate^T) * (n2 Wup^T)),
+ *   n2 = RMSNorm(h1) * mlp_norm.
+ *
+ *   d_T        device int32 [B], strictly increasing, in [0, N) (checked by
+ *              kvr_check_support, not here).
+ *   x_in       device float32 [x_in_rows, hidden]: x_in_rows == B means the
+ *              rows are already packed in the order of T; x_in_rows ==
+ *              meta->n_tokens means row r is gathered from x_in[T[r]].
+ *   x_out      device float32 [B, hidden], packed in the order of T.  It may
+ *              alias x_in when x_in_rows == B.
+ *   cache, meta  updated in place at the rows T only; every other cache row
+ *              and flag byte is left bit-identical.
+ *   ws         device workspace of at least kvr_workspace_bytes() bytes.
+ *
+ * Errors (before any device work): null or misaligned pointers;
+ * head_dim not 64/128, Hq % Hkv != 0, hidden or intermediate not a multiple
+ * of 64 -> UNSUPPORTED; B < 0, B > N, x_in_rows not in {B, N}, non-finite
+ * alpha/beta/eps -> INVALID_ARGUMENT; ws_bytes too small -> WORKSPACE.
+ * B = 0 is a successful no-op.
+ */
+kvr_status kvr_layer_repair(const kvr_config* cfg, const kvr_layer_weights* w, kvr_kv cache,
+                            const kvr_meta* meta, const int32_t* d_T, int32_t B,
+                            const float* x_in, int32_t x_in_rows, float* x_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * kvr_stack_repair - the layer-major traversal (Budgeted KV-Cache Repair,
+ * section 3.3): rows T are gathered once and advance through layers
+ * 0..n_layers-1 together, each layer as in kvr_layer_repair, reusing one
+ * plan and one RoPE table built once per call.  w and caches are host
+ * arrays of n_layers entries.  x_out receives the last layer's packed output
+ * and is also the packed residual stream between layers.  Same argument
+ * rules and errors as kvr_layer_repair.
+ */
+kvr_status kvr_stack_repair(const kvr_config* cfg, int32_t n_layers, const kvr_layer_weights* w,
+                            const kvr_kv* caches, const kvr_meta* meta, const int32_t* d_T,
+                            int32_t B, const float* x_in, int32_t x_in_rows, float* x_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Human-readable name of a status. */
+const char* kvr_status_string(kvr_status s);
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* kvr_last_error(void);
+
+/*
+ * Kernel timing probe.  kvr_timing_begin(mask) makes the library bracket
+ * every later launch of the kernels whose KVR_KERNEL_* bit is in `mask` with
+ * a pair of HIP events on the launch stream.  kvr_timing_end() waits for
+ * them and writes, for each of the KVR_KERNEL_COUNT kernels, the summed
+ * elapsed milliseconds (host double [KVR_KERNEL_COUNT]) and the number of
+ * launches (host int32 [KVR_KERNEL_COUNT]); either may be NULL.  Timing is
+ * process-wide and not thread-safe.
+ */
+enum {
+  KVR_KERNEL_PLAN = 0,      /* plan + RoPE table (once per call)          */
+  KVR_KERNEL_NORM = 1,      /* gather / residual sum + RMSNorm            */
+  KVR_KERNEL_QKV = 2,       /* QKV projection GEMM                         */
+  KVR_KERNEL_ROPE = 3,      /* RoPE + K/V write-back + flags               */
+  KVR_KERNEL_ATTN = 4,      /* packed causal attention                     */
+  KVR_KERNEL_ATTN_MERGE = 5,/* split-KV merge                              */
+  KVR_KERNEL_OPROJ = 6,     /* O projection GEMM                           */
+  KVR_KERNEL_GATEUP = 7,    /* gate/up GEMM with SwiGLU epilogue           */
+  KVR_KERNEL_DOWN = 8,      /* down projection GEMM                        */
+  KVR_KERNEL_FINAL = 9,     /* last residual sum into x_out                */
+  KVR_KERNEL_COUNT = 10
+};
+kvr_status kvr_timing_begin(uint32_t mask);
+kvr_status kvr_timing_end(double* total_ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVR_H */

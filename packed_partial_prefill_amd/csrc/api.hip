@@ -1,0 +1,383 @@
+// Host side of libkvr: the extern "C" entry points declared in kvr.h.
+// Validates arguments before touching the device, carves the caller's
+// workspace, and enqueues the per-layer kernel sequence on the caller's
+// stream (no synchronisation, no device allocation).
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "kvr_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+kvr_status fail(kvr_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+kvr_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool dev_ok(const void* p) { return p != nullptr && aligned16(p); }
+
+// ---------------------------------------------------------------- timing
+struct Timing {
+  uint32_t mask = 0;
+  std::vector<hipEvent_t> ev;  // pairs
+  std::vector<int> id;
+  size_t used = 0;
+} g_timing;
+
+struct Launch {
+  int id;
+  hipStream_t stream;
+  bool on;
+  Launch(int kernel_id, hipStream_t s) : id(kernel_id), stream(s), on(false) {
+    if (!(g_timing.mask & (1u << kernel_id))) return;
+    if (g_timing.used * 2 + 2 > g_timing.ev.size()) {
+      hipEvent_t a, b;
+      if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) return;
+      g_timing.ev.push_back(a);
+      g_timing.ev.push_back(b);
+      g_timing.id.push_back(-1);
+    }
+    g_timing.id[g_timing.used] = kernel_id;
+    on = hipEventRecord(g_timing.ev[g_timing.used * 2], stream) == hipSuccess;
+  }
+  void done() {
+    if (!on) return;
+    hipEventRecord(g_timing.ev[g_timing.used * 2 + 1], stream);
+    ++g_timing.used;
+  }
+};
+
+#define KVR_RUN(kid, stream, what, expr)          \
+  do {                                            \
+    Launch _l((kid), (stream));                   \
+    hipError_t _e = (expr);                       \
+    _l.done();                                    \
+    if (_e != hipSuccess) return hip_fail(_e, what); \
+  } while (0)
+
+// ---------------------------------------------------------------- config
+kvr_status check_config(const kvr_config* c, kvr::Shape* sh) {
+  if (!c) return fail(KVR_ERR_INVALID_ARGUMENT, "cfg is NULL");
+  if (c->dtype != KVR_F32 && c->dtype != KVR_BF16)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(c->dtype));
+  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->intermediate <= 0)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "non-positive shape");
+  if (c->head_dim != 64 && c->head_dim != 128)
+    return fail(KVR_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", c->head_dim);
+  if (c->n_q_heads % c->n_kv_heads)
+    return fail(KVR_ERR_UNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
+  if (c->hidden % 64 || c->intermediate % 64)
+    return fail(KVR_ERR_UNSUPPORTED, "hidden and intermediate must be multiples of 64");
+  if (c->hidden > 8192) return fail(KVR_ERR_UNSUPPORTED, "hidden > 8192");
+  if (!std::isfinite(c->alpha) || !std::isfinite(c->beta) || !std::isfinite(c->rms_eps) ||
+      c->rms_eps < 0.f)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "alpha, beta and rms_eps must be finite (eps >= 0)");
+  if (!std::isfinite(c->rope_theta) || c->rope_theta <= 0.0)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "rope_theta must be finite and positive");
+  sh->hidden = c->hidden;
+  sh->hq = c->n_q_heads;
+  sh->hkv = c->n_kv_heads;
+  sh->d = c->head_dim;
+  sh->inter = c->intermediate;
+  sh->group = c->n_q_heads / c->n_kv_heads;
+  return KVR_OK;
+}
+
+size_t esize(kvr_dtype dt) { return dt == KVR_BF16 ? 2 : 4; }
+
+// Workspace layout; offsets are 256-byte aligned from an aligned base.
+struct Layout {
+  size_t tab, n_full, n_total, nbuf, part, q, o, mlp, attn, total;
+  int split_qkv, split_o, split_down;
+};
+
+size_t up256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+Layout layout_for(const kvr_config* c, const kvr::Shape& sh, int B, int n_tokens) {
+  Layout L{};
+  const size_t es = esize(c->dtype);
+  const int nt = kvr::plan_tiles(B, sh.group);
+  L.split_qkv = kvr::gemm_splits_for(c->dtype, B, sh.qkv_cols(), sh.hidden);
+  L.split_o = kvr::gemm_splits_for(c->dtype, B, sh.hidden, sh.hq * sh.d);
+  L.split_down = kvr::gemm_splits_for(c->dtype, B, sh.hidden, sh.inter);
+  size_t part_floats = static_cast<size_t>(L.split_qkv) * B * sh.qkv_cols();
+  part_floats = std::max(part_floats, static_cast<size_t>(L.split_o) * B * sh.hidden);
+  part_floats = std::max(part_floats, static_cast<size_t>(L.split_down) * B * sh.hidden);
+  size_t off = 0;
+  L.tab = off;     off = up256(off + static_cast<size_t>(B) * (sh.d / 2) * sizeof(float2));
+  L.n_full = off;  off = up256(off + static_cast<size_t>(nt) * 4);
+  L.n_total = off; off = up256(off + static_cast<size_t>(nt) * 4);
+  L.nbuf = off;    off = up256(off + static_cast<size_t>(B) * sh.hidden * es);
+  L.part = off;    off = up256(off + part_floats * 4);
+  L.q = off;       off = up256(off + static_cast<size_t>(B) * sh.hq * sh.d * es);
+  L.o = off;       off = up256(off + static_cast<size_t>(B) * sh.hq * sh.d * es);
+  L.mlp = off;     off = up256(off + static_cast<size_t>(B) * sh.inter * es);
+  L.attn = off;    off = up256(off + kvr::attention_workspace_bytes(c->dtype, B, n_tokens, sh));
+  L.total = off;
+  return L;
+}
+
+kvr_status check_weights(const kvr_layer_weights& w, int layer) {
+  const void* req[] = {w.attn_norm, w.wq, w.wk, w.wv, w.wo, w.mlp_norm, w.w_gate, w.w_up, w.w_down};
+  for (const void* p : req)
+    if (!dev_ok(p)) return fail(KVR_ERR_INVALID_ARGUMENT, "layer %d: weight pointer NULL or not 16-byte aligned", layer);
+  const int nb = (w.bq != nullptr) + (w.bk != nullptr) + (w.bv != nullptr);
+  if (nb != 0 && nb != 3)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "layer %d: bq, bk, bv must be all NULL or all set", layer);
+  if (nb == 3 && (!aligned16(w.bq) || !aligned16(w.bk) || !aligned16(w.bv)))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "layer %d: bias pointers not 16-byte aligned", layer);
+  return KVR_OK;
+}
+
+kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weights* w,
+                     const kvr_kv* caches, const kvr_meta* meta, const int32_t* d_T, int B,
+                     const float* x_in, int x_in_rows, float* x_out, void* ws, size_t ws_bytes,
+                     hipStream_t stream) {
+  g_err[0] = '\0';
+  kvr::Shape sh;
+  kvr_status st = check_config(cfg, &sh);
+  if (st != KVR_OK) return st;
+  if (n_layers < 1) return fail(KVR_ERR_INVALID_ARGUMENT, "n_layers must be >= 1");
+  if (!w || !caches) return fail(KVR_ERR_INVALID_ARGUMENT, "weights / caches arrays are NULL");
+  if (!meta) return fail(KVR_ERR_INVALID_ARGUMENT, "meta is NULL");
+  const int N = meta->n_tokens;
+  if (N <= 0) return fail(KVR_ERR_INVALID_ARGUMENT, "meta->n_tokens must be positive");
+  if (B < 0 || B > N) return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d outside [0, N=%d]", B, N);
+  if (x_in_rows != B && x_in_rows != N)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "x_in_rows=%d must be B=%d or N=%d", x_in_rows, B, N);
+  if (B == 0) return KVR_OK;
+  if (!dev_ok(d_T) || !dev_ok(x_in) || !dev_ok(x_out) || !dev_ok(ws) || !dev_ok(meta->flags))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "T, x_in, x_out, ws and flags must be non-NULL and 16-byte aligned");
+  const bool gather = (x_in_rows == N) && !(B == N);
+  if (gather && x_in == x_out)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "x_out may alias x_in only when x_in_rows == B");
+  for (int l = 0; l < n_layers; ++l) {
+    if ((st = check_weights(w[l], l)) != KVR_OK) return st;
+    if (!dev_ok(caches[l].k) || !dev_ok(caches[l].v))
+      return fail(KVR_ERR_INVALID_ARGUMENT, "layer %d: cache pointers NULL or not 16-byte aligned", l);
+  }
+  const Layout L = layout_for(cfg, sh, B, N);
+  uint8_t* base = reinterpret_cast<uint8_t*>(up256(reinterpret_cast<uintptr_t>(ws)));
+  const size_t slack = static_cast<size_t>(base - static_cast<uint8_t*>(ws));
+  if (ws_bytes < L.total + slack)
+    return fail(KVR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total + slack);
+
+  const kvr_dtype dt = cfg->dtype;
+  float2* tab = reinterpret_cast<float2*>(base + L.tab);
+  int32_t* n_full = reinterpret_cast<int32_t*>(base + L.n_full);
+  int32_t* n_total = reinterpret_cast<int32_t*>(base + L.n_total);
+  void* nbuf = base + L.nbuf;
+  float* part = reinterpret_cast<float*>(base + L.part);
+  void* qbuf = base + L.q;
+  void* obuf = base + L.o;
+  void* mlp = base + L.mlp;
+  void* attn_ws = base + L.attn;
+  const int qkv_n = sh.qkv_cols();
+
+  // once per call: plan (Eq. 23-24) and RoPE table for the fixed positions
+  KVR_RUN(KVR_KERNEL_PLAN, stream, "plan",
+          kvr::launch_build_plan(d_T, B, sh.group, n_full, n_total, stream));
+  KVR_RUN(KVR_KERNEL_PLAN, stream, "rope table",
+          kvr::launch_rope_table(d_T, B, sh.d, cfg->rope_theta, tab, stream));
+  // gather the selected rows once; RMSNorm for layer 0
+  KVR_RUN(KVR_KERNEL_NORM, stream, "gather+norm",
+          kvr::launch_gather_norm(dt, x_in, gather ? d_T : nullptr, x_out,
+                                  static_cast<const float*>(w[0].attn_norm), cfg->rms_eps, nbuf, B,
+                                  sh.hidden, stream));
+  for (int l = 0; l < n_layers; ++l) {
+    const kvr_layer_weights& W = w[l];
+    kvr::WeightSegs qkv{{W.wq, W.wk, W.wv},
+                        {0, sh.hq * sh.d, (sh.hq + sh.hkv) * sh.d, qkv_n}, 3};
+    KVR_RUN(KVR_KERNEL_QKV, stream, "qkv gemm",
+            kvr::launch_gemm_partial(dt, nbuf, qkv, B, qkv_n, sh.hidden, L.split_qkv, part, stream));
+    KVR_RUN(KVR_KERNEL_ROPE, stream, "rope+writeback",
+            kvr::launch_rope_writeback(dt, part, L.split_qkv, static_cast<size_t>(B) * qkv_n,
+                                       static_cast<const float*>(W.bq),
+                                       static_cast<const float*>(W.bk),
+                                       static_cast<const float*>(W.bv), tab, d_T, B, sh, qbuf,
+                                       caches[l].k, caches[l].v, meta->flags, stream));
+    KVR_RUN(KVR_KERNEL_ATTN, stream, "attention",
+            kvr::launch_attention(dt, qbuf, caches[l].k, caches[l].v, meta->flags, d_T, B, N, sh,
+                                  cfg->alpha, cfg->beta, n_full, n_total, attn_ws, obuf, stream));
+    if (kvr::attention_needs_merge(dt))
+      KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "attention merge",
+              kvr::launch_attention_merge(dt, B, sh, n_total, attn_ws, obuf, stream));
+    kvr::WeightSegs wo{{W.wo, nullptr, nullptr}, {0, sh.hidden, sh.hidden, sh.hidden}, 1};
+    KVR_RUN(KVR_KERNEL_OPROJ, stream, "o gemm",
+            kvr::launch_gemm_partial(dt, obuf, wo, B, sh.hidden, sh.hq * sh.d, L.split_o, part,
+                                     stream));
+    KVR_RUN(KVR_KERNEL_NORM, stream, "residual+norm",
+            kvr::launch_residual_norm(dt, x_out, part, L.split_o,
+                                      static_cast<size_t>(B) * sh.hidden,
+                                      static_cast<const float*>(W.mlp_norm), cfg->rms_eps, nbuf,
+                                      B, sh.hidden, stream));
+    KVR_RUN(KVR_KERNEL_GATEUP, stream, "gate/up gemm",
+            kvr::launch_gemm_swiglu(dt, nbuf, W.w_gate, W.w_up, B, sh.inter, sh.hidden, mlp,
+                                    stream));
+    kvr::WeightSegs wd{{W.w_down, nullptr, nullptr}, {0, sh.hidden, sh.hidden, sh.hidden}, 1};
+    KVR_RUN(KVR_KERNEL_DOWN, stream, "down gemm",
+            kvr::launch_gemm_partial(dt, mlp, wd, B, sh.hidden, sh.inter, L.split_down, part,
+                                     stream));
+    const bool last = (l + 1 == n_layers);
+    KVR_RUN(last ? KVR_KERNEL_FINAL : KVR_KERNEL_NORM, stream, "residual+norm",
+            kvr::launch_residual_norm(
+                dt, x_out, part, L.split_down, static_cast<size_t>(B) * sh.hidden,
+                last ? nullptr : static_cast<const float*>(w[l + 1].attn_norm), cfg->rms_eps,
+                nbuf, B, sh.hidden, stream));
+  }
+  return KVR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvr_status kvr_build_repair_set(const int32_t* d_s, const int32_t* d_e, int32_t m,
+                                int32_t n_tokens, int32_t tau, uint32_t mode,
+                                const kvr_meta* meta, const kvr_repair_set* out,
+                                int32_t* h_counts, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (m < 1) return fail(KVR_ERR_BAD_BLOCKS, "m must be >= 1");
+  if (n_tokens < 1) return fail(KVR_ERR_INVALID_ARGUMENT, "n_tokens must be >= 1");
+  if (tau < 0) return fail(KVR_ERR_INVALID_ARGUMENT, "tau must be >= 0");
+  if (mode & ~static_cast<uint32_t>(KVR_SEAM_ASYMMETRIC | KVR_INIT_META))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "unknown mode bits 0x%x", mode);
+  if (!dev_ok(d_s) || !dev_ok(d_e)) return fail(KVR_ERR_INVALID_ARGUMENT, "d_s / d_e NULL or misaligned");
+  if (!out || !dev_ok(out->T) || !dev_ok(out->run_start) || !dev_ok(out->run_len) ||
+      !dev_ok(out->counts) || out->cap < 0)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "repair-set outputs NULL, misaligned or cap < 0");
+  const bool init = (mode & KVR_INIT_META) != 0;
+  if (init) {
+    if (!meta || !dev_ok(meta->flags) || meta->n_tokens != n_tokens ||
+        (meta->block_id && !aligned16(meta->block_id)))
+      return fail(KVR_ERR_INVALID_ARGUMENT, "KVR_INIT_META needs meta with flags and n_tokens == N");
+  }
+  hipError_t e = kvr::launch_build_repair_set(d_s, d_e, m, n_tokens, tau,
+                                              (mode & KVR_SEAM_ASYMMETRIC) != 0, out->T,
+                                              out->run_start, out->run_len, out->counts, out->cap,
+                                              stream);
+  if (e != hipSuccess) return hip_fail(e, "build repair set");
+  if (init) {
+    e = kvr::launch_init_meta(d_s, d_e, m, n_tokens, out->counts, meta->flags, meta->block_id,
+                              stream);
+    if (e != hipSuccess) return hip_fail(e, "init meta");
+  }
+  if (!h_counts) return KVR_OK;
+  e = hipMemcpyAsync(h_counts, out->counts, 3 * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy counts");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "synchronize");
+  if (h_counts[2] == KVR_ERR_BAD_BLOCKS) return fail(KVR_ERR_BAD_BLOCKS, "blocks do not tile [0, N)");
+  if (h_counts[2] == KVR_ERR_CAPACITY)
+    return fail(KVR_ERR_CAPACITY, "|T| = %d exceeds cap %d", h_counts[0], out->cap);
+  return KVR_OK;
+}
+
+kvr_status kvr_check_support(const int32_t* d_T, int32_t B, int32_t n_tokens,
+                             int32_t first_selectable, int32_t* d_result, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (B < 0 || n_tokens < 0 || B > n_tokens)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d, n_tokens=%d", B, n_tokens);
+  if (!dev_ok(d_result) || (B > 0 && !dev_ok(d_T)))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "d_T / d_result NULL or misaligned");
+  hipError_t e = kvr::launch_check_support(d_T, B, n_tokens, first_selectable, d_result, stream);
+  if (e != hipSuccess) return hip_fail(e, "check support");
+  int32_t h = 0;
+  e = hipMemcpyAsync(&h, d_result, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy result");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "synchronize");
+  if (h != KVR_OK)
+    return fail(KVR_ERR_BAD_SUPPORT, "support not strictly increasing or outside [%d, %d)",
+                first_selectable, n_tokens);
+  return KVR_OK;
+}
+
+kvr_status kvr_build_plan(const int32_t* d_T, int32_t B, int32_t group, int32_t* d_n_full,
+                          int32_t* d_n_total, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (B < 0 || group < 1) return fail(KVR_ERR_INVALID_ARGUMENT, "B < 0 or group < 1");
+  if (B == 0) return KVR_OK;
+  if (!dev_ok(d_T) || !dev_ok(d_n_full) || !dev_ok(d_n_total))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "pointers NULL or misaligned");
+  hipError_t e = kvr::launch_build_plan(d_T, B, group, d_n_full, d_n_total, stream);
+  return e == hipSuccess ? KVR_OK : hip_fail(e, "build plan");
+}
+
+size_t kvr_workspace_bytes(const kvr_config* cfg, int32_t B, int32_t n_tokens) {
+  kvr::Shape sh;
+  if (check_config(cfg, &sh) != KVR_OK || B < 0 || n_tokens <= 0 || B > n_tokens) return 0;
+  return layout_for(cfg, sh, B, n_tokens).total + 256;
+}
+
+kvr_status kvr_layer_repair(const kvr_config* cfg, const kvr_layer_weights* w, kvr_kv cache,
+                            const kvr_meta* meta, const int32_t* d_T, int32_t B,
+                            const float* x_in, int32_t x_in_rows, float* x_out, void* ws,
+                            size_t ws_bytes, hipStream_t stream) {
+  return run_stack(cfg, 1, w, &cache, meta, d_T, B, x_in, x_in_rows, x_out, ws, ws_bytes, stream);
+}
+
+kvr_status kvr_stack_repair(const kvr_config* cfg, int32_t n_layers, const kvr_layer_weights* w,
+                            const kvr_kv* caches, const kvr_meta* meta, const int32_t* d_T,
+                            int32_t B, const float* x_in, int32_t x_in_rows, float* x_out,
+                            void* ws, size_t ws_bytes, hipStream_t stream) {
+  return run_stack(cfg, n_layers, w, caches, meta, d_T, B, x_in, x_in_rows, x_out, ws, ws_bytes,
+                   stream);
+}
+
+const char* kvr_status_string(kvr_status s) {
+  switch (s) {
+    case KVR_OK: return "KVR_OK";
+    case KVR_ERR_INVALID_ARGUMENT: return "KVR_ERR_INVALID_ARGUMENT";
+    case KVR_ERR_UNSUPPORTED: return "KVR_ERR_UNSUPPORTED";
+    case KVR_ERR_BAD_BLOCKS: return "KVR_ERR_BAD_BLOCKS";
+    case KVR_ERR_BAD_SUPPORT: return "KVR_ERR_BAD_SUPPORT";
+    case KVR_ERR_CAPACITY: return "KVR_ERR_CAPACITY";
+    case KVR_ERR_WORKSPACE: return "KVR_ERR_WORKSPACE";
+    case KVR_ERR_HIP: return "KVR_ERR_HIP";
+  }
+  return "KVR_UNKNOWN_STATUS";
+}
+
+const char* kvr_last_error(void) { return g_err; }
+
+kvr_status kvr_timing_begin(uint32_t mask) {
+  g_timing.mask = mask & ((1u << KVR_KERNEL_COUNT) - 1u);
+  g_timing.used = 0;
+  return KVR_OK;
+}
+
+kvr_status kvr_timing_end(double* total_ms, int32_t* launches) {
+  g_err[0] = '\0';
+  if (total_ms) for (int i = 0; i < KVR_KERNEL_COUNT; ++i) total_ms[i] = 0.0;
+  if (launches) for (int i = 0; i < KVR_KERNEL_COUNT; ++i) launches[i] = 0;
+  kvr_status st = KVR_OK;
+  for (size_t i = 0; i < g_timing.used; ++i) {
+    hipEvent_t a = g_timing.ev[2 * i], b = g_timing.ev[2 * i + 1];
+    hipError_t e = hipEventSynchronize(b);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, a, b);
+    if (e != hipSuccess) { st = hip_fail(e, "timing events"); break; }
+    const int id = g_timing.id[i];
+    if (total_ms) total_ms[id] += ms;
+    if (launches) launches[id] += 1;
+  }
+  g_timing.mask = 0;
+  g_timing.used = 0;
+  return st;
+}
+
+}  // extern "C"

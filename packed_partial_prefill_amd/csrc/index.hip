@@ -1,0 +1,246 @@
+// Integer kernels of the repair: the seam set T_tau and its runs, load-time
+// metadata, support validation, the per-query-tile attention plan and the
+// per-row RoPE table.
+//
+// Seam windows and the asymmetric true-prefix rule: cross-attention reuse
+// specification page, section 6.3.  Runs are the execution intervals of
+// "Budgeted KV-Cache Repair", section 3.2.  Plan: same page, section 13.2,
+// Eq. 23-24.
+#include "kvr_internal.h"
+
+namespace kvr {
+
+namespace {
+
+constexpr int kBuildThreads = 1024;
+
+// Exclusive prefix sum over a 1024-thread workgroup; *total gets the sum.
+__device__ int block_exclusive_scan(int v, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wid] = x;
+  __syncthreads();
+  int pre = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int w = wsum[i];
+    pre += (i < wid) ? w : 0;
+    tot += w;
+  }
+  __syncthreads();
+  *total = tot;
+  return pre + x - v;
+}
+
+// Positions of block i that belong to T_tau: at most two half-open ranges
+// [a0, a1) (leading window, merged with the trailing one when they touch)
+// and [b0, b1) (trailing window).
+struct BlockRanges {
+  int a0, a1, b0, b1;
+  __device__ int count() const { return (a1 - a0) + (b1 - b0); }
+};
+
+__device__ BlockRanges block_ranges(int i, int m, int si, int ei, int tau, bool asym) {
+  const bool lead = i >= 1;
+  const bool trail = (i < m - 1 && !(asym && i == 0)) || (asym && m >= 2 && i == m - 1);
+  const int la = si, lb = lead ? min(ei, si + tau) : si;
+  const int ta = trail ? max(si, ei - tau) : ei, tb = ei;
+  BlockRanges r;
+  if (lb >= ta) {  // windows overlap or touch: one range
+    r.a0 = la; r.a1 = tb; r.b0 = tb; r.b1 = tb;
+  } else {
+    r.a0 = la; r.a1 = lb; r.b0 = ta; r.b1 = tb;
+  }
+  return r;
+}
+
+__global__ __launch_bounds__(kBuildThreads) void k_build_repair_set(
+    const int32_t* __restrict__ s, const int32_t* __restrict__ e, int m, int n_tokens, int tau,
+    int asym, int32_t* __restrict__ T, int32_t* __restrict__ run_start,
+    int32_t* __restrict__ run_len, int32_t* __restrict__ counts, int cap) {
+  __shared__ int wsum[16];
+  __shared__ int s_bad;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+
+  // 1. the blocks must tile [0, N): s_1 = 0, e_i = s_{i+1}, e_m = N, non-empty
+  for (int i = tid; i < m; i += blockDim.x) {
+    const int si = s[i], ei = e[i];
+    const bool bad = !(si < ei) || (i == 0 && si != 0) || (i == m - 1 && ei != n_tokens) ||
+                     (i + 1 < m && ei != s[i + 1]);
+    if (bad) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) { counts[0] = 0; counts[1] = 0; counts[2] = KVR_ERR_BAD_BLOCKS; }
+    return;
+  }
+
+  // 2. |T| = sum of per-block counts; check capacity before writing
+  int total = 0;
+  for (int base = 0; base < m; base += blockDim.x) {
+    const int i = base + tid;
+    const int c = i < m ? block_ranges(i, m, s[i], e[i], tau, asym != 0).count() : 0;
+    int chunk;
+    block_exclusive_scan(c, wsum, &chunk);
+    total += chunk;
+  }
+  if (total > cap) {
+    if (tid == 0) { counts[0] = total; counts[1] = 0; counts[2] = KVR_ERR_CAPACITY; }
+    return;
+  }
+
+  // 3. fill T: block i writes its ranges at its exclusive offset
+  int off0 = 0;
+  for (int base = 0; base < m; base += blockDim.x) {
+    const int i = base + tid;
+    BlockRanges r{0, 0, 0, 0};
+    if (i < m) r = block_ranges(i, m, s[i], e[i], tau, asym != 0);
+    int chunk;
+    int off = off0 + block_exclusive_scan(i < m ? r.count() : 0, wsum, &chunk);
+    for (int t = r.a0; t < r.a1; ++t) T[off++] = t;
+    for (int t = r.b0; t < r.b1; ++t) T[off++] = t;
+    off0 += chunk;
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // 4. maximal runs: T[k] opens a run unless T[k] == T[k-1] + 1.  run_len
+  //    first holds the opening index, then the length.
+  int nruns = 0;
+  for (int base = 0; base < total; base += blockDim.x) {
+    const int k = base + tid;
+    const int open = (k < total) && (k == 0 || T[k] != T[k - 1] + 1);
+    int chunk;
+    const int id = nruns + block_exclusive_scan(open, wsum, &chunk);
+    if (open) { run_start[id] = T[k]; run_len[id] = k; }
+    nruns += chunk;
+  }
+  __threadfence_block();
+  __syncthreads();
+  for (int base = 0; base < nruns; base += blockDim.x) {
+    const int j = base + tid;
+    int len = 0;
+    if (j < nruns) len = ((j + 1 < nruns) ? run_len[j + 1] : total) - run_len[j];
+    __syncthreads();
+    if (j < nruns) run_len[j] = len;
+    __threadfence_block();
+    __syncthreads();
+  }
+  if (tid == 0) { counts[0] = total; counts[1] = nruns; counts[2] = KVR_OK; }
+}
+
+// Load-time metadata (6.2): block 1 global, later blocks local; the first
+// token of every block after the first is a spurious sink.  Skipped when the
+// build reported bad blocks.
+__global__ void k_init_meta(const int32_t* __restrict__ s, const int32_t* __restrict__ e, int m,
+                            int n_tokens, const int32_t* __restrict__ counts,
+                            uint8_t* __restrict__ flags, int32_t* __restrict__ block_id) {
+  if (counts[2] == KVR_ERR_BAD_BLOCKS) return;
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_tokens) return;
+  int lo = 0, hi = m - 1;  // largest i with s[i] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (s[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  uint8_t f = 0;
+  if (t >= e[0]) f |= KVR_FLAG_LOCAL;
+  if (lo >= 1 && t == s[lo]) f |= KVR_FLAG_SINK;
+  flags[t] = f;
+  if (block_id) block_id[t] = lo;
+}
+
+__global__ __launch_bounds__(kBuildThreads) void k_check_support(const int32_t* __restrict__ T,
+                                                                 int B, int n_tokens, int first,
+                                                                 int32_t* __restrict__ result) {
+  __shared__ int s_bad;
+  if (threadIdx.x == 0) s_bad = 0;
+  __syncthreads();
+  for (int k = threadIdx.x; k < B; k += blockDim.x) {
+    const int t = T[k];
+    if (t < first || t >= n_tokens || (k > 0 && T[k - 1] >= t)) atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) result[0] = s_bad ? KVR_ERR_BAD_SUPPORT : KVR_OK;
+}
+
+__global__ void k_build_plan(const int32_t* __restrict__ T, int B, int group, int n_tiles,
+                             int32_t* __restrict__ n_full, int32_t* __restrict__ n_total) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= n_tiles) return;
+  const int P = B * group;
+  const int p0 = t * KVR_ATTN_QROWS;
+  const int p1 = min(P, p0 + KVR_ATTN_QROWS) - 1;
+  const int u_min = T[p0 / group], u_max = T[p1 / group];
+  n_full[t] = (u_min + 1) / KVR_ATTN_KV_TILE;
+  n_total[t] = (u_max + KVR_ATTN_KV_TILE) / KVR_ATTN_KV_TILE;
+}
+
+// cos / sin of g * theta^(-2i/d) for every packed row and frequency, built in
+// float64 once per call and stored as float32 pairs [B][d/2].
+__global__ void k_rope_table(const int32_t* __restrict__ T, int B, int half, double theta,
+                             float2* __restrict__ tab) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * half) return;
+  const int r = idx / half, i = idx - r * half;
+  const double inv = pow(theta, -(2.0 * i) / (2.0 * half));
+  const double ang = static_cast<double>(T[r]) * inv;
+  double sn, cs;
+  sincos(ang, &sn, &cs);
+  tab[idx] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+}
+
+}  // namespace
+
+hipError_t launch_build_repair_set(const int32_t* s, const int32_t* e, int m, int n_tokens,
+                                   int tau, bool asym, int32_t* T, int32_t* run_start,
+                                   int32_t* run_len, int32_t* counts, int cap,
+                                   hipStream_t stream) {
+  hipLaunchKernelGGL(k_build_repair_set, dim3(1), dim3(kBuildThreads), 0, stream, s, e, m,
+                     n_tokens, tau, asym ? 1 : 0, T, run_start, run_len, counts, cap);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_meta(const int32_t* s, const int32_t* e, int m, int n_tokens,
+                            const int32_t* counts, uint8_t* flags, int32_t* block_id,
+                            hipStream_t stream) {
+  if (n_tokens <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_init_meta, dim3((n_tokens + 255) / 256), dim3(256), 0, stream, s, e, m,
+                     n_tokens, counts, flags, block_id);
+  return hipGetLastError();
+}
+
+hipError_t launch_check_support(const int32_t* T, int B, int n_tokens, int first,
+                                int32_t* result, hipStream_t stream) {
+  hipLaunchKernelGGL(k_check_support, dim3(1), dim3(kBuildThreads), 0, stream, T, B, n_tokens,
+                     first, result);
+  return hipGetLastError();
+}
+
+int plan_tiles(int B, int group) { return (B * group + KVR_ATTN_QROWS - 1) / KVR_ATTN_QROWS; }
+
+hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full,
+                             int32_t* n_total, hipStream_t stream) {
+  const int nt = plan_tiles(B, group);
+  if (nt == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_build_plan, dim3((nt + 255) / 256), dim3(256), 0, stream, T, B, group, nt,
+                     n_full, n_total);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(const int32_t* T, int B, int head_dim, double theta, float2* tab,
+                             hipStream_t stream) {
+  const int n = B * (head_dim / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rope_table, dim3((n + 255) / 256), dim3(256), 0, stream, T, B,
+                     head_dim / 2, theta, tab);
+  return hipGetLastError();
+}
+
+}  // namespace kvr

@@ -1,0 +1,79 @@
+// Internal launch interface of libkvr (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kvr.h"
+
+namespace kvr {
+
+// Model shape of one call, validated by the host layer.
+struct Shape {
+  int hidden, hq, hkv, d, inter, group;
+  __host__ __device__ int qkv_cols() const { return (hq + 2 * hkv) * d; }
+};
+
+// ---- index.hip --------------------------------------------------------------
+hipError_t launch_build_repair_set(const int32_t* s, const int32_t* e, int m, int n_tokens,
+                                   int tau, bool asym, int32_t* T, int32_t* run_start,
+                                   int32_t* run_len, int32_t* counts, int cap, hipStream_t stream);
+hipError_t launch_init_meta(const int32_t* s, const int32_t* e, int m, int n_tokens,
+                            const int32_t* counts, uint8_t* flags, int32_t* block_id,
+                            hipStream_t stream);
+hipError_t launch_check_support(const int32_t* T, int B, int n_tokens, int first,
+                                int32_t* result, hipStream_t stream);
+int plan_tiles(int B, int group);
+hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full,
+                             int32_t* n_total, hipStream_t stream);
+hipError_t launch_rope_table(const int32_t* T, int B, int head_dim, double theta, float2* tab,
+                             hipStream_t stream);
+
+// ---- norm.hip ---------------------------------------------------------------
+// x_res[r] = x_in[gather ? T[r] : r]; n_out[r] = RMSNorm(x_res[r]) * gamma.
+hipError_t launch_gather_norm(kvr_dtype dt, const float* x_in, const int32_t* gather_T,
+                              float* x_res, const float* gamma, float eps, void* n_out, int B,
+                              int hidden, hipStream_t stream);
+// x_res[r] += sum_s part[s][r]; if gamma: n_out[r] = RMSNorm(x_res[r]) * gamma.
+hipError_t launch_residual_norm(kvr_dtype dt, float* x_res, const float* part, int splits,
+                                size_t split_stride, const float* gamma, float eps, void* n_out,
+                                int B, int hidden, hipStream_t stream);
+
+// ---- gemm.hip ---------------------------------------------------------------
+// Weight matrix given as up to three row segments (e.g. Wq | Wk | Wv):
+// output column n belongs to segment j with n_begin[j] <= n < n_begin[j+1].
+struct WeightSegs {
+  const void* w[3];
+  int n_begin[4];
+  int nseg;
+};
+// part[s][M][N] (float32) = A[M, K-slice s] * W[N, K-slice s]^T for
+// s < splits (K split evenly in multiples of 64).
+hipError_t launch_gemm_partial(kvr_dtype dt, const void* A, const WeightSegs& W, int M, int N,
+                               int K, int splits, float* part, hipStream_t stream);
+// out[M][N] = SiLU(A Wg^T) * (A Wu^T), stored in dtype dt.
+hipError_t launch_gemm_swiglu(kvr_dtype dt, const void* A, const void* Wg, const void* Wu, int M,
+                              int N, int K, void* out, hipStream_t stream);
+int gemm_splits_for(kvr_dtype dt, int M, int N, int K);
+
+// ---- rope.hip -----------------------------------------------------------------
+hipError_t launch_rope_writeback(kvr_dtype dt, const float* qkv_part, int splits,
+                                 size_t split_stride, const float* bq, const float* bk,
+                                 const float* bv, const float2* tab, const int32_t* T, int B,
+                                 const Shape& sh, void* q_out, void* k_cache, void* v_cache,
+                                 uint8_t* flags, hipStream_t stream);
+
+// ---- attention.hip ----------------------------------------------------------
+size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh);
+hipError_t launch_attention(kvr_dtype dt, const void* q, const void* k_cache,
+                            const void* v_cache, const uint8_t* flags, const int32_t* T, int B,
+                            int n_tokens, const Shape& sh, float alpha, float beta,
+                            const int32_t* plan_n_full, const int32_t* plan_n_total, void* ws,
+                            void* o_out, hipStream_t stream);
+bool attention_needs_merge(kvr_dtype dt);
+hipError_t launch_attention_merge(kvr_dtype dt, int B, const Shape& sh,
+                                  const int32_t* plan_n_total, void* ws, void* o_out,
+                                  hipStream_t stream);
+
+}  // namespace kvr

@@ -1,0 +1,137 @@
+"""The C-ABI library loads, exports every entry point include/kvr.h declares,
+and rejects bad arguments on the host before any device work (these calls
+pass fake, aligned addresses that the library must never dereference)."""
+import ctypes as C
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvr.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvr_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
+              "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
+              "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    import packed_partial_prefill_amd as kvr
+    out = subprocess.run(["nm", "-D", "--defined-only", kvr.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    missing = [n for n in _declared() if n not in exported]
+    assert not missing, missing
+    for n in _declared():
+        getattr(kvr.lib(), n)
+
+
+@pytest.fixture(scope="module")
+def kvr():
+    import packed_partial_prefill_amd as m
+    return m
+
+
+FAKE = 1 << 20   # aligned, never dereferenced: validation fails first
+
+
+def _cfg(kvr, **kw):
+    c = dict(hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64, intermediate=512,
+             rms_eps=1e-6, rope_theta=1e6, alpha=-1.0, beta=-2.0, dtype=kvr.KVR_F32)
+    c.update(kw)
+    return kvr.kvr_config(**c)
+
+
+def _w(kvr, **over):
+    vals = {n: FAKE for n, _ in kvr.kvr_layer_weights._fields_}
+    vals.update(bq=None, bk=None, bv=None)
+    vals.update(over)
+    return kvr.kvr_layer_weights(**vals)
+
+
+def _layer(kvr, cfg=None, w=None, B=4, x_rows=4, n_tokens=512, ws_bytes=1 << 40, T=FAKE,
+           x_in=FAKE, x_out=FAKE + 4096, flags=FAKE):
+    lib = kvr.lib()
+    cfg = cfg or _cfg(kvr)
+    w = w or _w(kvr)
+    meta = kvr.kvr_meta(flags, None, n_tokens)
+    return lib.kvr_layer_repair(C.byref(cfg), C.byref(w), kvr.kvr_kv(FAKE, FAKE), C.byref(meta),
+                                T, B, x_in, x_rows, x_out, FAKE, ws_bytes, None)
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=96), -2), (dict(n_q_heads=5), -2), (dict(hidden=200), -2),
+    (dict(intermediate=500), -2), (dict(alpha=float("nan")), -1), (dict(beta=float("inf")), -1),
+    (dict(rms_eps=float("nan")), -1), (dict(dtype=7), -1), (dict(rope_theta=0.0), -1)])
+def test_layer_repair_rejects_bad_config(kvr, over, status):
+    assert _layer(kvr, cfg=_cfg(kvr, **over)) == status
+    assert kvr.kvr_last_error() != ""
+
+
+def test_layer_repair_rejects_bad_arguments(kvr):
+    assert _layer(kvr, B=-1) == -1
+    assert _layer(kvr, B=600) == -1                        # B > N
+    assert _layer(kvr, x_rows=7) == -1                     # neither B nor N
+    assert _layer(kvr, T=None) == -1
+    assert _layer(kvr, T=FAKE + 4) == -1                   # misaligned
+    assert _layer(kvr, x_in=FAKE, x_out=FAKE, x_rows=512) == -1   # gather into x_in itself
+    assert _layer(kvr, w=_w(kvr, wq=None)) == -1
+    assert _layer(kvr, w=_w(kvr, bq=FAKE)) == -1           # partial biases
+    assert _layer(kvr, ws_bytes=1024) == -6
+    assert _layer(kvr, B=0, x_rows=0) == 0                 # no-op success
+    assert _layer(kvr, B=0, x_rows=512) == 0
+
+
+def test_workspace_bytes(kvr):
+    lib = kvr.lib()
+    c = _cfg(kvr)
+    a = lib.kvr_workspace_bytes(C.byref(c), 24, 512)
+    b = lib.kvr_workspace_bytes(C.byref(c), 48, 512)
+    assert 0 < a < b
+    assert lib.kvr_workspace_bytes(C.byref(_cfg(kvr, head_dim=80)), 24, 512) == 0
+    assert lib.kvr_workspace_bytes(C.byref(c), 600, 512) == 0
+
+
+def test_build_repair_set_host_validation(kvr):
+    lib = kvr.lib()
+    out = kvr.kvr_repair_set(FAKE, FAKE, FAKE, FAKE, 16)
+    f = lambda m=2, n=8, tau=1, mode=1, meta=None, s=FAKE: lib.kvr_build_repair_set(
+        s, FAKE, m, n, tau, mode, meta, C.byref(out), None, None)
+    assert f(m=0) == -3
+    assert f(tau=-1) == -1
+    assert f(mode=8) == -1
+    assert f(s=None) == -1
+    assert f(mode=3) == -1                                 # INIT_META without meta
+    bad_meta = kvr.kvr_meta(FAKE, None, 9)
+    assert f(mode=3, meta=C.byref(bad_meta)) == -1         # meta for another N
+
+
+def test_check_support_and_plan_host_validation(kvr):
+    lib = kvr.lib()
+    assert lib.kvr_check_support(FAKE, 5, 4, 0, FAKE, None) == -1
+    assert lib.kvr_check_support(FAKE, 1, 4, 0, None, None) == -1
+    assert lib.kvr_build_plan(FAKE, 4, 0, FAKE, FAKE, None) == -1
+    assert lib.kvr_build_plan(FAKE, 0, 7, FAKE, FAKE, None) == 0
+
+
+def test_status_strings(kvr):
+    for st, name in kvr.STATUS_NAMES.items():
+        assert kvr.kvr_status_string(st) == name
+
+
+def test_python_binding_has_the_c_names(kvr):
+    for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
+              "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
+              "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
+        assert callable(getattr(kvr, n))

@@ -1,0 +1,119 @@
+"""GPU parity of one repaired layer (kvr_layer_repair) against the oracle on
+the same seeded inputs: packed outputs and refreshed K/V rows within the
+stated tolerance, flags and every untouched cache row bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.gpu_harness import (assert_close, build_seams_gpu, cfg_of, cpu, dev_cache,
+                               dev_weights, kvr, log, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_layer_case(w: wl.Workload, T_np=None, x_packed=False, stream=None, check_rows=None,
+                   cfg_over=None):
+    """Runs one layer on the GPU and the oracle; returns the max errors."""
+    m = kvr()
+    cfg = cfg_of(w, **(cfg_over or {}))
+    log(f"[layer] {w.name} dtype={w.dtype} support={w.support} "
+        f"B={'seams' if T_np is None else len(T_np)} packed_input={x_packed}")
+    if T_np is None and w.support == "seams":
+        dT, _, h, flags, _ = build_seams_gpu(w)
+    else:
+        T_np = wl.explicit_support(w) if T_np is None else np.asarray(T_np, np.int32)
+        dT = torch.from_numpy(T_np.astype(np.int32)).cuda()
+        flags = torch.from_numpy(wl.initial_flags(w)).cuda()
+    T = dT.cpu().numpy().astype(np.int64)
+    B = len(T)
+    flags0 = wl.initial_flags(w)
+    assert np.array_equal(flags.cpu().numpy(), flags0)
+    wnp = wl.layer_weights(w, 0)
+    K0, V0 = wl.kv_cache(w, 0)
+    X = wl.hidden_states(w)
+    dw = dev_weights(w, wnp)
+    kc, vc = dev_cache(w, K0, V0)
+    kc0, vc0 = kc.clone(), vc.clone()
+    x_in = torch.from_numpy(X[T] if x_packed else X).cuda()
+    x_out = torch.empty((B, w.hidden), dtype=torch.float32, device="cuda")
+    ws = workspace(cfg, B, w.n_tokens)
+    m.kvr_layer_repair(cfg, dw, kc, vc, flags, dT, x_in, x_out, ws, stream=stream)
+    torch.cuda.synchronize()
+
+    c_or = cfg_of(w, **(cfg_over or {}))
+    K, V = K0.astype(np.float64), V0.astype(np.float64)
+    f = flags0.copy()
+    rows = T if check_rows is None else T[:check_rows]
+    y = oracle.stack_repair(c_or, [(wnp, K, V)], f, rows, X)
+    n = len(rows)
+    errs = {}
+    errs["y"] = assert_close(w, cpu(x_out[:n]), y, "packed output")
+    errs["k"] = assert_close(w, cpu(kc[torch.from_numpy(rows).cuda()]), K[rows], "K rows")
+    errs["v"] = assert_close(w, cpu(vc[torch.from_numpy(rows).cuda()]), V[rows], "V rows")
+    # untouched rows bit-identical; flags bit-exact (cleared at T only)
+    keep = torch.ones(w.n_tokens, dtype=torch.bool, device="cuda")
+    keep[dT.long()] = False
+    assert torch.equal(kc[keep], kc0[keep]) and torch.equal(vc[keep], vc0[keep])
+    f_ref = flags0.copy()
+    f_ref[T] &= np.uint8(0xFC)
+    assert np.array_equal(flags.cpu().numpy(), f_ref)
+    return errs
+
+
+def test_tiny_f32_seams():
+    run_layer_case(wl.TINY)
+
+
+def test_tiny_f32_packed_input_and_side_stream():
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        run_layer_case(wl.TINY.with_(support="explicit"), T_np=np.arange(130, 167, dtype=np.int32),
+                       x_packed=True, stream=s)
+
+
+def test_tiny_f32_with_qkv_bias():
+    run_layer_case(wl.TINY.with_(qkv_bias=True))
+
+
+def test_tiny_f32_unbiased_alpha_beta_zero():
+    run_layer_case(wl.TINY.with_(alpha=0.0, beta=0.0))
+
+
+def test_tiny_f32_isolated_tokens_exercise_sinks():
+    # isolated positions landing on block-leading sinks: beta is live here
+    T = np.array([128, 129, 200, 256, 300, 384, 385, 511], dtype=np.int32)
+    run_layer_case(wl.TINY.with_(support="explicit"), T_np=T)
+
+
+def test_tiny_f32_edges_single_row_first_position_and_all_rows():
+    run_layer_case(wl.TINY.with_(support="explicit"), T_np=np.array([0], np.int32))
+    run_layer_case(wl.TINY.with_(support="explicit"), T_np=np.array([511], np.int32))
+    run_layer_case(wl.TINY.with_(support="explicit"), T_np=np.arange(512, dtype=np.int32))
+
+
+def test_tiny_bf16_head_dim_128_group_6():
+    w = wl.Workload("tiny-bf16-g6", 101, hidden=384, n_q_heads=6, n_kv_heads=1, head_dim=128,
+                    intermediate=640, n_layers=1, n_tokens=700, block_size=100, dtype="bf16",
+                    alpha=-1.0, beta=-2.0, tau=5)
+    run_layer_case(w)
+
+
+def test_qwen15_layer_seams():
+    run_layer_case(wl.QWEN15_LAYER)
+
+
+@pytest.mark.timeout(600)
+def test_qwen7_layer_16k_seams():
+    run_layer_case(wl.QWEN7_LAYER_SEAMS)
+
+
+@pytest.mark.timeout(600)
+def test_qwen7_layer_16k_contiguous():
+    run_layer_case(wl.QWEN7_LAYER_CONTIG)
+
+
+@pytest.mark.timeout(600)
+def test_qwen7_layer_16k_matched():
+    run_layer_case(wl.QWEN7_LAYER_MATCHED, check_rows=128)

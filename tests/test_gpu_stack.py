@@ -1,0 +1,151 @@
+"""GPU parity of the layer stack (kvr_stack_repair).
+
+At full size the oracle cannot run every row through 28 layers in seconds,
+so the checks are (a) exact oracle parity on the first k packed rows (a
+repair's first k rows depend only on keys at or before their positions, so
+the oracle's repair of T[:k] is exactly their value; pinned on the CPU by
+test_causal_prefix_of_support_is_self_contained), and (b) properties that
+hold at any size: untouched rows bit-identical, flags exact, finite outputs,
+and agreement of two schedules of the same computation.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests.gpu_harness import (assert_close, build_seams_gpu, cfg_of, cpu, dev_cache,
+                               dev_weights, kvr, log, workspace)
+
+pytestmark = pytest.mark.gpu
+
+
+def _upload_layers(w, oracle_rows_upto=None):
+    """Generate every layer once; returns device weights/caches, and host
+    float64 copies (optionally truncated to the rows the oracle needs)."""
+    dws, dcs, host = [], [], []
+    for li in range(w.n_layers):
+        wnp = wl.layer_weights(w, li)
+        K0, V0 = wl.kv_cache(w, li)
+        dws.append(dev_weights(w, wnp))
+        dcs.append(dev_cache(w, K0, V0))
+        n = w.n_tokens if oracle_rows_upto is None else oracle_rows_upto
+        host.append((wnp, K0[:n].astype(np.float64), V0[:n].astype(np.float64)))
+    return dws, dcs, host
+
+
+def test_small_stack_seams_bf16():
+    w = wl.Workload("small-stack-bf16", 102, hidden=256, n_q_heads=8, n_kv_heads=2, head_dim=64,
+                    intermediate=512, n_layers=4, n_tokens=1024, block_size=128, dtype="bf16",
+                    alpha=-1.0, beta=-2.0, tau=7)
+    log(f"[stack] {w.name}")
+    m = kvr()
+    dT, _, h, flags, _ = build_seams_gpu(w)
+    T = dT.cpu().numpy().astype(np.int64)
+    dws, dcs, host = _upload_layers(w)
+    X = wl.hidden_states(w)
+    x_out = torch.empty((len(T), w.hidden), dtype=torch.float32, device="cuda")
+    cfg = cfg_of(w)
+    m.kvr_stack_repair(cfg, dws, dcs, flags, dT, torch.from_numpy(X).cuda(), x_out,
+                       workspace(cfg, len(T), w.n_tokens))
+    torch.cuda.synchronize()
+    f = wl.initial_flags(w)
+    y = oracle.stack_repair(cfg, host, f, T, X)
+    assert_close(w, cpu(x_out), y, "stack output")
+    for li, ((_, K, V), (kc, vc)) in enumerate(zip(host, dcs)):
+        assert_close(w, cpu(kc[dT.long()]), K[T], f"layer {li} K rows")
+        assert_close(w, cpu(vc[dT.long()]), V[T], f"layer {li} V rows")
+    assert np.array_equal(flags.cpu().numpy(), f)
+
+
+@pytest.mark.timeout(900)
+def test_qwen7_stack28_32k_isolated_sampled():
+    w = wl.QWEN7_STACK_ISOLATED
+    m = kvr()
+    T = wl.isolated_support(w)
+    k = 8
+    log(f"[stack] {w.name}: B={len(T)} layers={w.n_layers}; oracle on first {k} rows")
+    dT = torch.from_numpy(T).cuda()
+    res = torch.empty(4, dtype=torch.int32, device="cuda")
+    m.kvr_check_support(dT, w.n_tokens, w.block_size, res)
+    dws, dcs, host = _upload_layers(w, oracle_rows_upto=int(T[k - 1]) + 1)
+    log("  inputs on device")
+    X = wl.hidden_states(w)
+    flags = torch.from_numpy(wl.initial_flags(w)).cuda()
+    keep = torch.ones(w.n_tokens, dtype=torch.bool, device="cuda")
+    keep[dT.long()] = False
+    k_keep0 = [kc[keep].clone() for kc, _ in dcs[:2]]
+    x_out = torch.empty((len(T), w.hidden), dtype=torch.float32, device="cuda")
+    cfg = cfg_of(w)
+    m.kvr_stack_repair(cfg, dws, dcs, flags, dT, torch.from_numpy(X).cuda(), x_out,
+                       workspace(cfg, len(T), w.n_tokens))
+    torch.cuda.synchronize()
+    log("  gpu stack done")
+    out = cpu(x_out)
+    assert np.all(np.isfinite(out))
+    for li in range(2):
+        assert torch.equal(dcs[li][0][keep], k_keep0[li])
+    f_ref = wl.initial_flags(w)
+    f_ref[T] &= np.uint8(0xFC)
+    assert np.array_equal(flags.cpu().numpy(), f_ref)
+    f = wl.initial_flags(w)[: int(T[k - 1]) + 1].copy()
+    y = oracle.stack_repair(cfg, host, f, T[:k], X)
+    assert_close(w, out[:k], y, f"stack output rows 0..{k - 1}")
+    for li in (0, w.n_layers - 1):
+        _, K, V = host[li]
+        assert_close(w, cpu(dcs[li][0][dT[:k].long()]), K[T[:k]], f"layer {li} K rows")
+        assert_close(w, cpu(dcs[li][1][dT[:k].long()]), V[T[:k]], f"layer {li} V rows")
+
+
+@pytest.mark.timeout(900)
+def test_qwen15_stack28_16k_degenerate():
+    """Degeneration (tau >= |B|/2): T covers B_2..B_m, no local key and no
+    sink survives write-back, so the repair equals a full causal prefill.
+    B_1's cache is itself produced by a repair over B_1 (a prefix sees only
+    itself).  Checks: oracle parity on B_1 and the first k rows of T; and at
+    full size, the two-phase result equals one repair over all N positions."""
+    w = wl.QWEN15_STACK_DEGENERATE
+    m = kvr()
+    k = 32
+    dT, _, h, flags, _ = build_seams_gpu(w)
+    T = dT.cpu().numpy().astype(np.int64)
+    assert T[0] == w.block_size and len(T) == w.n_tokens - w.block_size
+    log(f"[stack] {w.name}: B={len(T)} layers={w.n_layers}; oracle on B_1 + first {k} rows")
+    upto = w.block_size + k
+    dws, dcs, host = _upload_layers(w, oracle_rows_upto=upto)
+    fresh = [(kc.clone(), vc.clone()) for kc, vc in dcs]
+    X = wl.hidden_states(w)
+    dX = torch.from_numpy(X).cuda()
+    cfg = cfg_of(w)
+    TA = torch.arange(w.block_size, dtype=torch.int32, device="cuda")
+    xa = torch.empty((w.block_size, w.hidden), dtype=torch.float32, device="cuda")
+    m.kvr_stack_repair(cfg, dws, dcs, flags, TA, dX, xa, workspace(cfg, w.block_size, w.n_tokens))
+    xb = torch.empty((len(T), w.hidden), dtype=torch.float32, device="cuda")
+    m.kvr_stack_repair(cfg, dws, dcs, flags, dT, dX, xb, workspace(cfg, len(T), w.n_tokens))
+    torch.cuda.synchronize()
+    log("  gpu two-phase done")
+    assert np.all(flags.cpu().numpy() == 0)
+
+    # (a) oracle on B_1 then on the first k rows of T
+    f = wl.initial_flags(w)[:upto].copy()
+    ya = oracle.stack_repair(cfg, host, f, np.arange(w.block_size), X)
+    yb = oracle.stack_repair(cfg, host, f, T[:k], X)
+    assert_close(w, cpu(xa), ya, "B_1 output")
+    assert_close(w, cpu(xb[:k]), yb, f"T output rows 0..{k - 1}")
+    for li in (0, w.n_layers - 1):
+        _, K, V = host[li]
+        assert_close(w, cpu(dcs[li][0][:upto]), K[:upto], f"layer {li} K rows 0..{upto - 1}")
+        assert_close(w, cpu(dcs[li][1][:upto]), V[:upto], f"layer {li} V rows 0..{upto - 1}")
+
+    # (b) full size: one repair over [0, N) with alpha = beta = 0 is the same
+    # full prefill; compare every row of the two-phase result against it
+    flags2 = torch.from_numpy(wl.initial_flags(w)).cuda()
+    T_all = torch.arange(w.n_tokens, dtype=torch.int32, device="cuda")
+    x_all = torch.empty((w.n_tokens, w.hidden), dtype=torch.float32, device="cuda")
+    m.kvr_stack_repair(cfg, dws, fresh, flags2, T_all, dX, x_all, workspace(cfg, w.n_tokens, w.n_tokens))
+    torch.cuda.synchronize()
+    log("  gpu single-call prefill done")
+    assert_close(w, cpu(xb), cpu(x_all[w.block_size:]), "two-phase vs one-call, all rows")
+    for li in (0, 13, w.n_layers - 1):
+        assert_close(w, cpu(dcs[li][0]), cpu(fresh[li][0]), f"layer {li} K, all rows")
+        assert_close(w, cpu(dcs[li][1]), cpu(fresh[li][1]), f"layer {li} V, all rows")

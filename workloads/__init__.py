@@ -28,7 +28,7 @@ from __future__ import annotations
 
 import math
 import threading
-from dataclasses import dataclass, field, replace
+from dataclasses import dataclass, replace
 from typing import Dict, Optional, Tuple
 
 import numpy as np
@@ -148,9 +148,11 @@ def bf16_from_bits(bits: np.ndarray) -> np.ndarray:
 # ----------------------------------------------------------------------------
 # Chunked, thread-parallel standard normals
 # ----------------------------------------------------------------------------
-def _normal_chunks(key: Tuple[int, ...], n: int, out: np.ndarray, threads: int) -> None:
+def _normal_chunks(key: Tuple[int, ...], n: int, out: np.ndarray, threads: int,
+                   scale: float = 1.0, offset: float = 0.0, bf16: bool = False) -> None:
+    """Fill ``out`` with N(offset, scale^2) draws chunk by chunk (optionally
+    bf16-rounded); chunks are spread over threads, numpy releases the GIL."""
     nchunks = (n + CHUNK - 1) // CHUNK
-
     nthreads = max(1, min(threads, nchunks))
 
     def work(c0: int) -> None:
@@ -158,7 +160,12 @@ def _normal_chunks(key: Tuple[int, ...], n: int, out: np.ndarray, threads: int) 
             lo = c * CHUNK
             hi = min(n, lo + CHUNK)
             g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key) + [c])))
-            out[lo:hi] = g.standard_normal(hi - lo, dtype=np.float32)
+            x = g.standard_normal(hi - lo, dtype=np.float32)
+            if scale != 1.0:
+                x *= np.float32(scale)
+            if offset != 0.0:
+                x += np.float32(offset)
+            out[lo:hi] = bf16_round(x) if bf16 else x
 
     if nthreads == 1:
         work(0)
@@ -185,13 +192,8 @@ def normal(w: Workload, layer: int, tensor: int, shape, scale: float = 1.0,
     n = int(np.prod(shape))
     out = np.empty(n, dtype=np.float32)
     _normal_chunks((SEED_ROOT, w.cfg_id, layer, tensor), n, out,
-                   threads if threads is not None else default_threads())
-    if scale != 1.0:
-        out *= np.float32(scale)
-    if offset != 0.0:
-        out += np.float32(offset)
-    if w.dtype == "bf16":
-        out = bf16_round(out)
+                   threads if threads is not None else default_threads(), scale, offset,
+                   w.dtype == "bf16")
     return out.reshape(shape)
 
 
