@@ -207,14 +207,15 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
             kvr::launch_rope_writeback(dt, part, L.split_qkv, static_cast<size_t>(B) * qkv_n,
                                        static_cast<const float*>(W.bq),
                                        static_cast<const float*>(W.bk),
-                                       static_cast<const float*>(W.bv), tab, d_T, B, sh, qbuf,
+                                       static_cast<const float*>(W.bv), tab, d_T, B, sh,
+                                       kvr::attention_q_scale(dt, sh.d), qbuf,
                                        caches[l].k, caches[l].v, meta->flags, stream));
     KVR_RUN(KVR_KERNEL_ATTN, stream, "attention",
             kvr::launch_attention(dt, qbuf, caches[l].k, caches[l].v, meta->flags, d_T, B, N, sh,
                                   cfg->alpha, cfg->beta, n_full, n_total, attn_ws, obuf, stream));
     if (kvr::attention_needs_merge(dt))
       KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "attention merge",
-              kvr::launch_attention_merge(dt, B, sh, n_total, attn_ws, obuf, stream));
+              kvr::launch_attention_merge(dt, B, N, sh, n_total, attn_ws, obuf, stream));
     kvr::WeightSegs wo{{W.wo, nullptr, nullptr}, {0, sh.hidden, sh.hidden, sh.hidden}, 1};
     KVR_RUN(KVR_KERNEL_OPROJ, stream, "o gemm",
             kvr::launch_gemm_partial(dt, obuf, wo, B, sh.hidden, sh.hq * sh.d, L.split_o, part,

@@ -5,9 +5,10 @@
 // Eq. 22) with logits <q, k_j>/sqrt(d) + alpha*[local_j] + beta*[sink_j]
 // (cross-attention reuse page, 6.4) and an online softmax.
 //
-// This file holds the VALU kernel used for float32 storage: one wave per
-// (row, head); each 64-key step scores one key per lane, then accumulates
-// P*V with every lane owning d/64 output columns.
+// bf16 storage runs on the MFMA kernel below (split-KV plus a merge kernel);
+// float32 storage runs on a VALU kernel: one wave per (row, head), each
+// 64-key step scores one key per lane, then accumulates P*V with every lane
+// owning d/64 output columns.
 #include "common.h"
 #include "kvr_internal.h"
 
@@ -67,36 +68,388 @@ __global__ __launch_bounds__(64) void k_attn_rowwise(const T* __restrict__ q,
   for (int c = 0; c < per; ++c) Elem<T>::store(orow, lane * per + c, acc[c] * inv);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel (gfx950 v_mfma_f32_32x32x16_bf16), float32 softmax.
+//
+// A workgroup owns KVR_ATTN_QROWS = 128 (packed row, query head) pairs of one
+// KV head group and a range of 64-key tiles (split-KV); 4 waves x 32 pairs.
+// Every key tile is staged once in LDS for all 128 pairs: K in its natural
+// [key][d] layout (16-byte chunks XOR-swizzled by key & 7), V transposed to
+// [d][key] (rows padded to 136 bytes), plus one float bias per key.
+// Scores are formed transposed, S^T = K Q^T, so each lane owns one query
+// column and 16 of the tile's keys: the softmax reduction is in-lane plus one
+// exchange with lane ^ 32.  O^T += V^T P^T then takes the lane's own P values
+// as the B operand; both operands list the keys of one 16-key step in the
+// same permuted order (4h..4h+3, 8+4h..8+4h+3 for lane half h).
+// Tiles below the plan's n_full (Eq. 23) are visible to every pair and skip
+// the causal test.  Q arrives pre-scaled by log2(e)/sqrt(d), so the softmax
+// runs in base 2 with the bias pre-multiplied by log2(e).
+// ---------------------------------------------------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+constexpr int kQRows = KVR_ATTN_QROWS;     // 128 pairs per workgroup
+constexpr int kKvTile = KVR_ATTN_KV_TILE;  // 64 keys per tile
+constexpr int kAttnThreads = 256;
+constexpr int kVtStride = 2 * kKvTile + 8;  // bytes per transposed V row (136)
+
+template <int D>
+struct AttnLds {
+  static constexpr int kBytes = kKvTile * D * 2;   // K tile
+  static constexpr int vBytes = D * kVtStride;     // V^T tile
+  static constexpr int bBytes = kKvTile * 4;       // bias
+  static constexpr int stage = kBytes + vBytes + bBytes;
+  static constexpr int total = 2 * stage;
+};
+
+template <int D>
+__device__ __forceinline__ int kswz(int key, int chunk) {
+  return key * (D * 2) + ((chunk ^ (key & 7)) << 4);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int D>
+__global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    const uint8_t* __restrict__ flags, const int32_t* __restrict__ Tpos,
+    const int32_t* __restrict__ n_full, const int32_t* __restrict__ n_total, int B, int n_tokens,
+    int Hq, int Hkv, int G, float bias_local, float bias_sink, int split_tiles, int n_splits,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  using L = AttnLds<D>;
+  constexpr int KCH = D / 8;   // 16-byte chunks per key row
+  const int qt = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
+  const int tot = n_total[qt];
+  const int c0 = sp * split_tiles;
+  if (c0 >= tot) return;
+  const int c1 = min(tot, c0 + split_tiles);
+  const int nf = n_full[qt];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int P = B * G;
+
+  // the query column this lane owns
+  const int p = qt * kQRows + wave * 32 + (lane & 31);
+  const int pc = min(p, P - 1);
+  const int r = pc / G;
+  const int h = g * G + (pc - r * G);
+  const int u = Tpos[r];
+  bf16x8_t qf[D / 16];
+  {
+    const bf16_t* qrow = q + (static_cast<size_t>(r) * Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
+  }
+
+  const size_t kv_row = static_cast<size_t>(Hkv) * D;   // elements between positions
+  const bf16_t* kg = kc + static_cast<size_t>(g) * D;
+  const bf16_t* vg = vc + static_cast<size_t>(g) * D;
+
+  // staging registers
+  constexpr int KLOADS = kKvTile * KCH / kAttnThreads;        // 4 (D=128) or 2 (D=64)
+  constexpr int VITEMS = (kKvTile / 4) * KCH;                 // 256 or 128
+  u32x4_t rk[KLOADS], rv[4];
+  uint8_t rf = 0;
+  auto gload = [&](int c) {
+    const int kv0 = c * kKvTile;
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int v = tid + i * kAttnThreads;
+      const int key = min(kv0 + v / KCH, n_tokens - 1);
+      rk[i] = *reinterpret_cast<const u32x4_t*>(kg + key * kv_row + (v % KCH) * 8);
+    }
+    if (tid < VITEMS) {
+      const int kgp = tid % (kKvTile / 4), ch = tid / (kKvTile / 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = min(kv0 + kgp * 4 + j, n_tokens - 1);
+        rv[j] = *reinterpret_cast<const u32x4_t*>(vg + key * kv_row + ch * 8);
+      }
+    }
+    if (tid < kKvTile) rf = flags[min(kv0 + tid, n_tokens - 1)];
+  };
+  auto lstore = [&](int buf) {
+    uint8_t* kb = lds + buf * L::stage;
+    uint8_t* vb = kb + L::kBytes;
+    float* bb = reinterpret_cast<float*>(vb + L::vBytes);
+#pragma unroll
+    for (int i = 0; i < KLOADS; ++i) {
+      const int v = tid + i * kAttnThreads;
+      *reinterpret_cast<u32x4_t*>(kb + kswz<D>(v / KCH, v % KCH)) = rk[i];
+    }
+    if (tid < VITEMS) {
+      const int kgp = tid % (kKvTile / 4), ch = tid / (kKvTile / 4);
+      // rv[j] holds d = ch*8 .. +7 of key 4*kgp + j; emit, per d, keys 4*kgp .. +3
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint32_t a0 = rv[0][w], a1 = rv[1][w], a2 = rv[2][w], a3 = rv[3][w];
+        u32x2_t lo, hi;   // d = ch*8 + 2w (low halves) and + 2w + 1 (high halves)
+        lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+        lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
+        hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
+        hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
+        const int d0 = ch * 8 + 2 * w;
+        *reinterpret_cast<u32x2_t*>(vb + d0 * kVtStride + kgp * 8) = lo;
+        *reinterpret_cast<u32x2_t*>(vb + (d0 + 1) * kVtStride + kgp * 8) = hi;
+      }
+    }
+    if (tid < kKvTile)
+      bb[tid] = ((rf & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((rf & KVR_FLAG_SINK) ? bias_sink : 0.f);
+  };
+
+  f32x16_t o[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
+  float m = -INFINITY, l = 0.f;
+
+  gload(c0);
+  lstore(0);
+  __syncthreads();
+  int cur = 0;
+  for (int c = c0; c < c1; ++c) {
+    const bool more = c + 1 < c1;
+    if (more) gload(c + 1);
+    const uint8_t* kb = lds + cur * L::stage;
+    const uint8_t* vb = kb + L::kBytes;
+    const float* bb = reinterpret_cast<const float*>(vb + L::vBytes);
+
+    // S^T = K Q^T for the two 32-key halves of the tile
+    f32x16_t s[2];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+      for (int t = 0; t < 16; ++t) s[sb][t] = 0.f;
+      const int key = sb * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb + kswz<D>(key, ks * 2 + half));
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[sb], 0, 0, 0);
+      }
+    }
+    // bias, causal test on partially visible tiles, running max
+    const bool partial = c >= nf;
+    const int kv0 = c * kKvTile;
+    float mt = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const int kl = sb * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
+        float x = s[sb][t] + bb[kl];
+        if (partial && kv0 + kl > u) x = -INFINITY;
+        s[sb][t] = x;
+        mt = fmaxf(mt, x);
+      }
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m, mt);
+    const float mu = (mn == -INFINITY) ? 0.f : mn;
+    const float corr = fast_exp2(m - mu);
+    float ls = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float e = fast_exp2(s[sb][t] - mu);
+        s[sb][t] = e;
+        ls += e;
+      }
+    l = l * corr + ls;
+    m = mn;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) o[db][t] *= corr;
+
+    // O^T += V^T P^T, four 16-key steps
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[sb][hs * 8 + i]);
+        const int kcol = (sb * 32 + hs * 16 + 4 * half) * 2;   // byte offset of key group
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const uint8_t* vr = vb + (db * 32 + (lane & 31)) * kVtStride + kcol;
+          const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(vr);
+          const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(vr + 16);
+          u32x4_t av;
+          av[0] = x0[0]; av[1] = x0[1]; av[2] = x1[0]; av[3] = x1[1];
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb,
+                                                          o[db], 0, 0, 0);
+        }
+      }
+
+    if (more) lstore(cur ^ 1);
+    __syncthreads();
+    cur ^= 1;
+  }
+
+  // partial results: O^T columns (unnormalised), running max and sum
+  const size_t slot = (static_cast<size_t>(qt) * Hkv + g) * n_splits + sp;
+  const int ql = wave * 32 + (lane & 31);
+  float* po = part_o + slot * D * kQRows;
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int d = db * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
+      po[d * kQRows + ql] = o[db][t];
+    }
+  l += __shfl_xor(l, 32, 64);
+  if (half == 0) {
+    float* pm = part_ml + slot * 2 * kQRows;
+    pm[ql] = m;
+    pm[kQRows + ql] = l;
+  }
+}
+
+// Merge the split-KV partials of one (query tile, KV group): weights
+// 2^(m_s - max m), normalised by the weighted sums; the result is transposed
+// through LDS so that each output row (one pair) is written contiguously.
+template <int D>
+__global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ n_total, int B, int Hq, int Hkv, int G, int split_tiles,
+    int n_splits, bf16_t* __restrict__ o) {
+  __shared__ __attribute__((aligned(16))) bf16_t tile[kQRows][D + 8];
+  __shared__ float wsc[kQRows];
+  const int qt = blockIdx.x, g = blockIdx.y;
+  const int ns = (n_total[qt] + split_tiles - 1) / split_tiles;
+  const size_t slot0 = (static_cast<size_t>(qt) * Hkv + g) * n_splits;
+  const int tid = threadIdx.x;
+  const int ql = tid & (kQRows - 1), part = tid >> 7;   // two threads per pair
+  // per-pair split weights (recomputed by both threads of the pair)
+  float mmax = -INFINITY;
+  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, part_ml[(slot0 + s) * 2 * kQRows + ql]);
+  float denom = 0.f;
+  for (int s = 0; s < ns; ++s) {
+    const float* pm = part_ml + (slot0 + s) * 2 * kQRows;
+    denom += fast_exp2(pm[ql] - mmax) * pm[kQRows + ql];
+  }
+  const float inv = 1.f / denom;
+  for (int d = part; d < D; d += 2) {
+    float acc = 0.f;
+    for (int s = 0; s < ns; ++s) {
+      const float wgt = fast_exp2(part_ml[(slot0 + s) * 2 * kQRows + ql] - mmax);
+      acc += wgt * part_o[(slot0 + s) * D * kQRows + d * kQRows + ql];
+    }
+    tile[ql][d] = f32_to_bf16(acc * inv);
+  }
+  (void)wsc;
+  __syncthreads();
+  // write rows: 16-byte chunks
+  const int P = B * G;
+  constexpr int CH = D / 8;
+  for (int v = tid; v < kQRows * CH; v += kAttnThreads) {
+    const int row = v / CH, ch = v % CH;
+    const int p = qt * kQRows + row;
+    if (p >= P) continue;
+    const int r = p / G, h = g * G + (p - r * G);
+    *reinterpret_cast<u32x4_t*>(o + (static_cast<size_t>(r) * Hq + h) * D + ch * 8) =
+        *reinterpret_cast<const u32x4_t*>(&tile[row][ch * 8]);
+  }
+}
+
+int attn_split_tiles(int n_tokens) {
+  (void)n_tokens;
+  return 32;
+}
+
 }  // namespace
 
-size_t attention_workspace_bytes(kvr_dtype, int, int, const Shape&) { return 0; }
+size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh) {
+  if (dt != KVR_BF16) return 0;
+  const int nt = plan_tiles(B, sh.group);
+  const int st = attn_split_tiles(n_tokens);
+  const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
+  return static_cast<size_t>(nt) * sh.hkv * ns * (sh.d + 2) * kQRows * sizeof(float);
+}
+
+namespace {
+template <int D>
+hipError_t launch_mfma(const void* q, const void* k_cache, const void* v_cache,
+                       const uint8_t* flags, const int32_t* T, int B, int n_tokens,
+                       const Shape& sh, float alpha, float beta, const int32_t* n_full,
+                       const int32_t* n_total, void* ws, hipStream_t stream) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_mfma<D>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       AttnLds<D>::total);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int nt = plan_tiles(B, sh.group);
+  const int st = attn_split_tiles(n_tokens);
+  const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
+  const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + slots * sh.d * kQRows;
+  const float log2e = 1.4426950408889634f;
+  dim3 grid(nt, sh.hkv, ns);
+  hipLaunchKernelGGL(k_attn_mfma<D>, grid, dim3(kAttnThreads), AttnLds<D>::total, stream,
+                     static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
+                     static_cast<const bf16_t*>(v_cache), flags, T, n_full, n_total, B, n_tokens,
+                     sh.hq, sh.hkv, sh.group, alpha * log2e, beta * log2e, st, ns, part_o,
+                     part_ml);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_total, void* ws,
+                        void* o_out, hipStream_t stream) {
+  const int nt = plan_tiles(B, sh.group);
+  const int st = attn_split_tiles(n_tokens);
+  const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
+  const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
+  const float* part_o = static_cast<const float*>(ws);
+  const float* part_ml = part_o + slots * sh.d * kQRows;
+  hipLaunchKernelGGL(k_attn_merge<D>, dim3(nt, sh.hkv), dim3(kAttnThreads), 0, stream, part_o,
+                     part_ml, n_total, B, sh.hq, sh.hkv, sh.group, st, ns,
+                     static_cast<bf16_t*>(o_out));
+  return hipGetLastError();
+}
+}  // namespace
+
+// Scale folded into Q by the RoPE kernel for the MFMA path.
+float attention_q_scale(kvr_dtype dt, int head_dim) {
+  return dt == KVR_BF16 ? 1.4426950408889634f / sqrtf(static_cast<float>(head_dim)) : 1.f;
+}
 
 hipError_t launch_attention(kvr_dtype dt, const void* q, const void* k_cache,
                             const void* v_cache, const uint8_t* flags, const int32_t* T, int B,
                             int n_tokens, const Shape& sh, float alpha, float beta,
                             const int32_t* plan_n_full, const int32_t* plan_n_total, void* ws,
                             void* o_out, hipStream_t stream) {
-  (void)n_tokens; (void)plan_n_full; (void)plan_n_total; (void)ws;
   if (B == 0) return hipSuccess;
-  dim3 grid(B * sh.hq);
-  if (dt == KVR_BF16)
-    hipLaunchKernelGGL(k_attn_rowwise<bf16_t>, grid, dim3(64), 0, stream,
-                       static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
-                       static_cast<const bf16_t*>(v_cache), flags, T, sh, alpha, beta,
-                       static_cast<bf16_t*>(o_out));
-  else
-    hipLaunchKernelGGL(k_attn_rowwise<float>, grid, dim3(64), 0, stream,
-                       static_cast<const float*>(q), static_cast<const float*>(k_cache),
-                       static_cast<const float*>(v_cache), flags, T, sh, alpha, beta,
-                       static_cast<float*>(o_out));
+  if (dt == KVR_BF16) {
+    if (sh.d == 128)
+      return launch_mfma<128>(q, k_cache, v_cache, flags, T, B, n_tokens, sh, alpha, beta,
+                              plan_n_full, plan_n_total, ws, stream);
+    return launch_mfma<64>(q, k_cache, v_cache, flags, T, B, n_tokens, sh, alpha, beta,
+                           plan_n_full, plan_n_total, ws, stream);
+  }
+  hipLaunchKernelGGL(k_attn_rowwise<float>, dim3(B * sh.hq), dim3(64), 0, stream,
+                     static_cast<const float*>(q), static_cast<const float*>(k_cache),
+                     static_cast<const float*>(v_cache), flags, T, sh, alpha, beta,
+                     static_cast<float*>(o_out));
   return hipGetLastError();
 }
 
-bool attention_needs_merge(kvr_dtype) { return false; }
+bool attention_needs_merge(kvr_dtype dt) { return dt == KVR_BF16; }
 
-hipError_t launch_attention_merge(kvr_dtype, int, const Shape&, const int32_t*, void*, void*,
-                                  hipStream_t) {
-  return hipSuccess;
+hipError_t launch_attention_merge(kvr_dtype dt, int B, int n_tokens, const Shape& sh,
+                                  const int32_t* plan_n_total, void* ws, void* o_out,
+                                  hipStream_t stream) {
+  if (B == 0 || dt != KVR_BF16) return hipSuccess;
+  if (sh.d == 128) return launch_merge<128>(B, n_tokens, sh, plan_n_total, ws, o_out, stream);
+  return launch_merge<64>(B, n_tokens, sh, plan_n_total, ws, o_out, stream);
 }
 
 }  // namespace kvr

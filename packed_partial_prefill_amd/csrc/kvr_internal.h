@@ -61,8 +61,8 @@ int gemm_splits_for(kvr_dtype dt, int M, int N, int K);
 hipError_t launch_rope_writeback(kvr_dtype dt, const float* qkv_part, int splits,
                                  size_t split_stride, const float* bq, const float* bk,
                                  const float* bv, const float2* tab, const int32_t* T, int B,
-                                 const Shape& sh, void* q_out, void* k_cache, void* v_cache,
-                                 uint8_t* flags, hipStream_t stream);
+                                 const Shape& sh, float q_scale, void* q_out, void* k_cache,
+                                 void* v_cache, uint8_t* flags, hipStream_t stream);
 
 // ---- attention.hip ----------------------------------------------------------
 size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh);
@@ -72,8 +72,10 @@ hipError_t launch_attention(kvr_dtype dt, const void* q, const void* k_cache,
                             const int32_t* plan_n_full, const int32_t* plan_n_total, void* ws,
                             void* o_out, hipStream_t stream);
 bool attention_needs_merge(kvr_dtype dt);
-hipError_t launch_attention_merge(kvr_dtype dt, int B, const Shape& sh,
+hipError_t launch_attention_merge(kvr_dtype dt, int B, int n_tokens, const Shape& sh,
                                   const int32_t* plan_n_total, void* ws, void* o_out,
                                   hipStream_t stream);
+// Factor the RoPE kernel folds into the stored queries for this path.
+float attention_q_scale(kvr_dtype dt, int head_dim);
 
 }  // namespace kvr

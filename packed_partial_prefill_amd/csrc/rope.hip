@@ -3,7 +3,8 @@
 // For row r at position u = T[r]: the QKV projection's split-K partials are
 // summed (plus optional biases), q and k are rotated at u (rotate-half
 // pairing (i, i+d/2), angle u * theta^(-2i/d), from the per-call float64
-// table), q is stored for attention, and the fresh k, v overwrite cache row
+// table), q is stored for attention (times the attention kernel's score
+// factor, folded in here), and the fresh k, v overwrite cache row
 // u before attention runs ("Budgeted KV-Cache Repair", section 13.2, Eq. 21);
 // the position's metadata becomes global with the sink bit cleared
 // (cross-attention reuse page, 6.4: write-back sets type <- global).
@@ -20,7 +21,8 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_rope_writeback(
     const float* __restrict__ part, int splits, size_t split_stride, const float* __restrict__ bq,
     const float* __restrict__ bk, const float* __restrict__ bv, const float2* __restrict__ tab,
-    const int32_t* __restrict__ Tpos, Shape sh, T* __restrict__ q_out, T* __restrict__ kc,
+    const int32_t* __restrict__ Tpos, Shape sh, float q_scale, T* __restrict__ q_out,
+    T* __restrict__ kc,
     T* __restrict__ vc, uint8_t* __restrict__ flags) {
   const int r = blockIdx.x;
   const int u = Tpos[r];
@@ -40,8 +42,8 @@ __global__ __launch_bounds__(kThreads) void k_rope_writeback(
     if (bq) { a += bq[c0]; b += bq[c0 + half]; }
     const float2 cs = tr[i];
     T* qo = q_out + (static_cast<size_t>(r) * sh.hq + h) * d;
-    Elem<T>::store(qo, i, a * cs.x - b * cs.y);
-    Elem<T>::store(qo, i + half, b * cs.x + a * cs.y);
+    Elem<T>::store(qo, i, (a * cs.x - b * cs.y) * q_scale);
+    Elem<T>::store(qo, i + half, (b * cs.x + a * cs.y) * q_scale);
   }
   // key heads: rotated, written to cache row u
   const int kbase = sh.hq * d;
@@ -70,16 +72,16 @@ __global__ __launch_bounds__(kThreads) void k_rope_writeback(
 hipError_t launch_rope_writeback(kvr_dtype dt, const float* qkv_part, int splits,
                                  size_t split_stride, const float* bq, const float* bk,
                                  const float* bv, const float2* tab, const int32_t* T, int B,
-                                 const Shape& sh, void* q_out, void* k_cache, void* v_cache,
-                                 uint8_t* flags, hipStream_t stream) {
+                                 const Shape& sh, float q_scale, void* q_out, void* k_cache,
+                                 void* v_cache, uint8_t* flags, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   if (dt == KVR_BF16)
     hipLaunchKernelGGL(k_rope_writeback<bf16_t>, dim3(B), dim3(kThreads), 0, stream, qkv_part,
-                       splits, split_stride, bq, bk, bv, tab, T, sh, static_cast<bf16_t*>(q_out),
+                       splits, split_stride, bq, bk, bv, tab, T, sh, q_scale, static_cast<bf16_t*>(q_out),
                        static_cast<bf16_t*>(k_cache), static_cast<bf16_t*>(v_cache), flags);
   else
     hipLaunchKernelGGL(k_rope_writeback<float>, dim3(B), dim3(kThreads), 0, stream, qkv_part,
-                       splits, split_stride, bq, bk, bv, tab, T, sh, static_cast<float*>(q_out),
+                       splits, split_stride, bq, bk, bv, tab, T, sh, q_scale, static_cast<float*>(q_out),
                        static_cast<float*>(k_cache), static_cast<float*>(v_cache), flags);
   return hipGetLastError();
 }
