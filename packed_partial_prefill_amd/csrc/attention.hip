@@ -74,7 +74,7 @@ __global__ __launch_bounds__(64) void k_attn_rowwise(const T* __restrict__ q,
 // A workgroup owns KVR_ATTN_QROWS = 128 (packed row, query head) pairs of one
 // KV head group and a range of 64-key tiles (split-KV); 4 waves x 32 pairs.
 // Every key tile is staged once in LDS for all 128 pairs: K in its natural
-// [key][d] layout (16-byte chunks XOR-swizzled by key & 7), V transposed to
+// [key][d] layout (16-byte chunks XOR-swizzled by key), V transposed to
 // [d][key] (rows padded to 136 bytes), plus one float bias per key.
 // Scores are formed transposed, S^T = K Q^T, so each lane owns one query
 // column and 16 of the tile's keys: the softmax reduction is in-lane plus one
@@ -104,9 +104,14 @@ struct AttnLds {
   static constexpr int total = 2 * stage;
 };
 
+// 16-byte chunk c of key row k sits at c ^ (k & 15) for 256-byte rows
+// (d = 128) and at c ^ ((k & 7) ^ ((k >> 3) & 1)) for 128-byte rows (d = 64):
+// the 32 rows one MFMA operand load reads then spread over distinct 16-byte
+// bank slots per 8-lane (128 B) and per 16-lane (256 B) pass.
 template <int D>
 __device__ __forceinline__ int kswz(int key, int chunk) {
-  return key * (D * 2) + ((chunk ^ (key & 7)) << 4);
+  const int x = (D == 128) ? (key & 15) : ((key & 7) ^ ((key >> 3) & 1));
+  return key * (D * 2) + ((chunk ^ x) << 4);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -230,39 +235,50 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
         s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[sb], 0, 0, 0);
       }
     }
-    // bias, causal test on partially visible tiles, running max
+    // bias (4 consecutive keys per LDS read), causal test on partially
+    // visible tiles, tile maximum
     const bool partial = c >= nf;
     const int kv0 = c * kKvTile;
     float mt = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int kl = sb * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
-        float x = s[sb][t] + bb[kl];
-        if (partial && kv0 + kl > u) x = -INFINITY;
-        s[sb][t] = x;
-        mt = fmaxf(mt, x);
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int kl0 = sb * 32 + 8 * t4 + 4 * half;
+        const float4 b4 = *reinterpret_cast<const float4*>(bb + kl0);
+        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          float x = s[sb][4 * t4 + j] + bv[j];
+          if (partial && kv0 + kl0 + j > u) x = -INFINITY;
+          s[sb][4 * t4 + j] = x;
+          mt = fmaxf(mt, x);
+        }
       }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const float mn = fmaxf(m, mt);
-    const float mu = (mn == -INFINITY) ? 0.f : mn;
-    const float corr = fast_exp2(m - mu);
-    float ls = 0.f;
+    // Lazy rescaling: the reference maximum m only moves when the tile's
+    // maximum exceeds it by more than 8 (log2 units), so probabilities stay
+    // below 2^8 and most tiles skip rescaling the accumulators.
+    const bool bump = mt > m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+      const float mn = bump ? mt : m;
+      const float corr = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
+      l *= corr;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) o[db][t] *= corr;
+      m = mn;
+    }
+    const float mu = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
         const float e = fast_exp2(s[sb][t] - mu);
         s[sb][t] = e;
-        ls += e;
+        l += e;
       }
-    l = l * corr + ls;
-    m = mn;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) o[db][t] *= corr;
 
     // O^T += V^T P^T, four 16-key steps
 #pragma unroll
@@ -309,51 +325,44 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   }
 }
 
-// Merge the split-KV partials of one (query tile, KV group): weights
-// 2^(m_s - max m), normalised by the weighted sums; the result is transposed
-// through LDS so that each output row (one pair) is written contiguously.
+// Merge the split-KV partials: workgroup (query tile, KV group, 16-row slice
+// of d); thread (pair ql, 8 consecutive d).  Split weights 2^(m_s - max m),
+// normalised by the weighted sums; each thread writes one 16-byte chunk of
+// its pair's output row.
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ n_total, int B, int Hq, int Hkv, int G, int split_tiles,
     int n_splits, bf16_t* __restrict__ o) {
-  __shared__ __attribute__((aligned(16))) bf16_t tile[kQRows][D + 8];
-  __shared__ float wsc[kQRows];
   const int qt = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int ql = tid & (kQRows - 1);
+  const int d0 = blockIdx.z * 16 + (tid >> 7) * 8;
+  const int p = qt * kQRows + ql;
+  if (p >= B * G) return;
   const int ns = (n_total[qt] + split_tiles - 1) / split_tiles;
   const size_t slot0 = (static_cast<size_t>(qt) * Hkv + g) * n_splits;
-  const int tid = threadIdx.x;
-  const int ql = tid & (kQRows - 1), part = tid >> 7;   // two threads per pair
-  // per-pair split weights (recomputed by both threads of the pair)
   float mmax = -INFINITY;
   for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, part_ml[(slot0 + s) * 2 * kQRows + ql]);
-  float denom = 0.f;
+  float denom = 0.f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
   for (int s = 0; s < ns; ++s) {
     const float* pm = part_ml + (slot0 + s) * 2 * kQRows;
-    denom += fast_exp2(pm[ql] - mmax) * pm[kQRows + ql];
+    const float w = fast_exp2(pm[ql] - mmax);
+    denom += w * pm[kQRows + ql];
+    const float* po = part_o + (slot0 + s) * D * kQRows + static_cast<size_t>(d0) * kQRows + ql;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += w * po[i * kQRows];
   }
   const float inv = 1.f / denom;
-  for (int d = part; d < D; d += 2) {
-    float acc = 0.f;
-    for (int s = 0; s < ns; ++s) {
-      const float wgt = fast_exp2(part_ml[(slot0 + s) * 2 * kQRows + ql] - mmax);
-      acc += wgt * part_o[(slot0 + s) * D * kQRows + d * kQRows + ql];
-    }
-    tile[ql][d] = f32_to_bf16(acc * inv);
-  }
-  (void)wsc;
-  __syncthreads();
-  // write rows: 16-byte chunks
-  const int P = B * G;
-  constexpr int CH = D / 8;
-  for (int v = tid; v < kQRows * CH; v += kAttnThreads) {
-    const int row = v / CH, ch = v % CH;
-    const int p = qt * kQRows + row;
-    if (p >= P) continue;
-    const int r = p / G, h = g * G + (p - r * G);
-    *reinterpret_cast<u32x4_t*>(o + (static_cast<size_t>(r) * Hq + h) * D + ch * 8) =
-        *reinterpret_cast<const u32x4_t*>(&tile[row][ch * 8]);
-  }
+  u32x4_t outv;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    outv[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i] * inv)) |
+              (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1] * inv)) << 16);
+  const int r = p / G, h = g * G + (p - r * G);
+  *reinterpret_cast<u32x4_t*>(o + (static_cast<size_t>(r) * Hq + h) * D + d0) = outv;
 }
 
 int attn_split_tiles(int n_tokens) {
@@ -410,7 +419,8 @@ hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_t
   const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
   const float* part_o = static_cast<const float*>(ws);
   const float* part_ml = part_o + slots * sh.d * kQRows;
-  hipLaunchKernelGGL(k_attn_merge<D>, dim3(nt, sh.hkv), dim3(kAttnThreads), 0, stream, part_o,
+  hipLaunchKernelGGL(k_attn_merge<D>, dim3(nt, sh.hkv, D / 16), dim3(kAttnThreads), 0, stream,
+                     part_o,
                      part_ml, n_total, B, sh.hq, sh.hkv, sh.group, st, ns,
                      static_cast<bf16_t*>(o_out));
   return hipGetLastError();

@@ -100,163 +100,241 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fma(const T* __restrict__ A, 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel (gfx950 v_mfma_f32_32x32x16_bf16), float32 accumulation.
 //
-// Workgroup tile 256 (M) x 256 (N) x 64 (K), 8 waves; wave w owns rows
-// (w/2)*64 .. +64 and a 128-column slice.  A (activations) and W tiles are
-// staged in LDS, double-buffered, as rows of eight 16-byte chunks whose
-// chunk index is XOR-swizzled with (row & 7) so that the 32 rows read by one
-// MFMA operand load hit distinct banks.  MFMA operand layout (32x32x16):
-// lane l supplies row/column l%32 and k = 8*(l/32) .. +7 of the 16-wide
-// K slice; accumulator t of lane l is D[8*(t/4) + 4*(l/32) + t%4][l%32].
+// Workgroup tile 256 (M) x 256 (N), 8 waves; wave w owns rows (w/2)*64 .. +64
+// and a 128-column slice (2 x 4 blocks of 32x32).  K advances 32 at a time
+// through four LDS stages that are filled straight from global memory by
+// global_load_lds_dwordx4 (no register staging), three stages ahead of the
+// MFMAs.  Each stage holds a 256 x 32 tile of A and of W as 64-byte rows of
+// four 16-byte chunks; chunk c of row r sits at c ^ (((r >> 1) ^ (r >> 3)) & 3),
+// so any 8 consecutive rows read by an MFMA operand load fall in distinct
+// 16-byte slots of 128 bytes and any 16 in distinct slots of 256 bytes (no
+// bank conflicts whether the LDS serves 8 or 16 lanes per pass).
+// The stage buffers are separate LDS objects picked at compile time, which
+// lets the compiler keep the three newer stages in flight while a stage is
+// consumed.  MFMA operand layout (32x32x16): lane l supplies row/column l%32
+// and k = 8*(l/32) .. +7 of the 16-wide K slice; accumulator t of lane l is
+// D[8*(t/4) + 4*(l/32) + t%4][l%32].
+//
+// Workgroups are numbered along M fastest, then N panel, then K split, and
+// block b is mapped so that each XCD (b % 8) takes one contiguous run of that
+// order: the M tiles sharing a weight panel then run together on one XCD and
+// the panel is fetched from HBM into that XCD's L2 once.
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 
-constexpr int MB = 256, NB = 256, KB = 64, MT = 512;
-constexpr int kTileBytes = MB * KB * 2;              // one 256 x 64 bf16 tile
-constexpr int kLdsBytes = 2 * 2 * kTileBytes;        // A and W, double-buffered
+constexpr int MB = 256, NB = 256, KB = 32, kStages = 4;
+constexpr int kTileBytes = MB * KB * 2;   // 16 KB: one 256 x 32 bf16 tile
+constexpr int kXcds = 8;
+
+__shared__ __attribute__((aligned(16))) uint8_t g_a0[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_a1[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_a2[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_a3[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_w0[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_w1[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_w2[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t g_w3[kTileBytes];
+
+template <int S> __device__ __forceinline__ uint8_t* a_stage() {
+  if constexpr (S == 0) return g_a0; else if constexpr (S == 1) return g_a1;
+  else if constexpr (S == 2) return g_a2; else return g_a3;
+}
+template <int S> __device__ __forceinline__ uint8_t* w_stage() {
+  if constexpr (S == 0) return g_w0; else if constexpr (S == 1) return g_w1;
+  else if constexpr (S == 2) return g_w2; else return g_w3;
+}
 
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * (KB * 2) + (((chunk ^ (row & 7))) << 4);
+  return row * (KB * 2) + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+}
+
+#define KVR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define KVR_GLB(p) ((const __attribute__((address_space(1))) void*)(p))
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] and
+// vmcnt[5:4] at bits 15:14, expcnt[6:4] = 7, lgkmcnt[11:8] = 15).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
+
+// Wave arrangement: WM x WN waves, each owning TM x TN blocks of 32 x 32.
+template <int WM, int WN, int TM, int TN>
+struct Cfg {
+  static_assert(WM * TM * 32 == MB && WN * TN * 32 == NB, "256 x 256 workgroup tile");
+  static constexpr int waves = WM * WN;
+  static constexpr int threads = 64 * waves;
+  static constexpr int loads = (MB / 16) / waves;   // 1 KB DMA slices per wave per operand
+};
+
+template <class C>
+struct GemmThread {
+  const bf16_t* asrc[C::loads];   // this lane's global source (A), at the split's first k
+  const bf16_t* wsrc[C::loads];   // ... (W)
+  int dst[C::loads];              // wave-uniform LDS byte offset of each 1 KB slice
+  int arow[4], wrow[4];
+  int khalf;
+};
+
+template <class C, int S>
+__device__ __forceinline__ void issue_stage(const GemmThread<C>& g, int kb) {
+#pragma unroll
+  for (int j = 0; j < C::loads; ++j) {
+    __builtin_amdgcn_global_load_lds(KVR_GLB(g.asrc[j] + kb), KVR_LDS(a_stage<S>() + g.dst[j]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(KVR_GLB(g.wsrc[j] + kb), KVR_LDS(w_stage<S>() + g.dst[j]), 16, 0, 0);
+  }
+}
+
+template <class C, int TM, int TN, int S>
+__device__ __forceinline__ void mma_stage(const GemmThread<C>& g, f32x16_t (&acc)[TM][TN]) {
+  const uint8_t* a = a_stage<S>();
+  const uint8_t* w = w_stage<S>();
+#pragma unroll
+  for (int ks = 0; ks < KB / 16; ++ks) {
+    const int chunk = ks * 2 + g.khalf;
+    bf16x8_t fa[TM], fw[TN];
+#pragma unroll
+    for (int mb = 0; mb < TM; ++mb) fa[mb] = *reinterpret_cast<const bf16x8_t*>(a + swz(g.arow[mb], chunk));
+#pragma unroll
+    for (int nb = 0; nb < TN; ++nb) fw[nb] = *reinterpret_cast<const bf16x8_t*>(w + swz(g.wrow[nb], chunk));
+#pragma unroll
+    for (int mb = 0; mb < TM; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < TN; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fw[nb], acc[mb][nb], 0, 0, 0);
+  }
+}
+
+// One K step on stage S: wait until only the two newer stages are still in
+// flight, barrier, refill the stage consumed one step earlier with the step
+// three ahead (clamped to the last step: a refill past the end is never
+// read), then run the MFMAs.  Every step issues exactly one stage, so the
+// wait count is fixed (2 pending stages of 2 * loads DMA slices per wave).
+template <class C, int TM, int TN, int S>
+__device__ __forceinline__ void k_step(const GemmThread<C>& g, int i, int nsteps,
+                                       f32x16_t (&acc)[TM][TN]) {
+  wait_vmcnt<4 * C::loads>();
+  __builtin_amdgcn_s_barrier();
+  issue_stage<C, (S + 3) % kStages>(g, min(i + 3, nsteps - 1) * KB);
+  mma_stage<C, TM, TN, S>(g, acc);
 }
 
 // MODE 0: part[split][M][N] = A * W^T over this split's K range (W segmented).
 // MODE 1: W.w[0] = W_gate, W.w[1] = W_up; the tile holds 128 gate rows and the
-//         same 128 up rows; out[M][N] = bf16(SiLU(gate) * up), full K.
-template <int MODE>
-__global__ __launch_bounds__(MT, 1) void k_gemm_mfma(const bf16_t* __restrict__ A, WeightSegs W,
-                                                     int M, int N, int K, int k_per_split,
-                                                     float* __restrict__ part,
-                                                     bf16_t* __restrict__ out) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * MB;
-  const int n0 = blockIdx.x * (MODE == 1 ? NB / 2 : NB);
-  const int k0 = blockIdx.z * k_per_split;
-  const int k1 = min(K, k0 + k_per_split);
+//         same 128 up rows; out[M][N] = bf16(SiLU(gate) * up), full K.  A wave's
+//         first TN/2 column blocks are gate columns, the last TN/2 the matching
+//         up columns, so both factors of an output meet in one lane.
+template <int MODE, int WM, int WN, int TM, int TN>
+__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_mfma(
+    const bf16_t* __restrict__ A, WeightSegs W, int M, int N, int K, int k_per_split,
+    int tiles_m, int tiles_n, int splits, float* __restrict__ part, bf16_t* __restrict__ out) {
+  using C = Cfg<WM, WN, TM, TN>;
+  // XCD-aware order: t = ((split * tiles_n) + n) * tiles_m + m
+  const int total = tiles_m * tiles_n * splits;
+  const int b = blockIdx.x, xcd = b % kXcds, q = total / kXcds, rem = total % kXcds;
+  const int t = xcd * q + min(xcd, rem) + b / kXcds;
+  const int tm = t % tiles_m, tn = (t / tiles_m) % tiles_n, split = t / (tiles_m * tiles_n);
 
-  // global source rows of the 4 + 4 chunks this thread stages per K step
-  const u32x4_t* asrc[4];
-  const u32x4_t* wsrc[4];
-  int lofs[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int m0 = tm * MB;
+  const int n0 = tn * (MODE == 1 ? NB / 2 : NB);
+  const int k0 = split * k_per_split;
+  const int k1 = min(K, k0 + k_per_split);
+  const int nsteps = k1 > k0 ? (k1 - k0) / KB : 0;
+
+  GemmThread<C> g;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int v = tid + i * MT;
-    const int row = v >> 3, chunk = v & 7;
-    lofs[i] = swz(row, chunk);
+  for (int j = 0; j < C::loads; ++j) {
+    const int row0 = (wave * C::loads + j) * 16;
+    const int row = row0 + (lane >> 2);                      // tile row this lane fetches
+    const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);   // logical chunk of its slot
+    g.dst[j] = row0 * (KB * 2);
     const int m = min(m0 + row, M - 1);
-    asrc[i] = reinterpret_cast<const u32x4_t*>(A + static_cast<size_t>(m) * K + chunk * 8);
-    const bf16_t* wrow;
+    g.asrc[j] = A + static_cast<size_t>(m) * K + k0 + chunk * 8;
+    const bf16_t* wr;
     if (MODE == 0) {
       const int n = min(n0 + row, N - 1);
-      int j = 0;
-      if (W.nseg > 1 && n >= W.n_begin[1]) j = 1;
-      if (W.nseg > 2 && n >= W.n_begin[2]) j = 2;
-      wrow = static_cast<const bf16_t*>(W.w[j]) + static_cast<size_t>(n - W.n_begin[j]) * K;
+      int sj = 0;
+      if (W.nseg > 1 && n >= W.n_begin[1]) sj = 1;
+      if (W.nseg > 2 && n >= W.n_begin[2]) sj = 2;
+      wr = static_cast<const bf16_t*>(W.w[sj]) + static_cast<size_t>(n - W.n_begin[sj]) * K;
     } else {
       const int n = min(n0 + (row & 127), N - 1);
-      wrow = static_cast<const bf16_t*>(W.w[row >> 7]) + static_cast<size_t>(n) * K;
+      wr = static_cast<const bf16_t*>(W.w[row >> 7]) + static_cast<size_t>(n) * K;
     }
-    wsrc[i] = reinterpret_cast<const u32x4_t*>(wrow + chunk * 8);
+    g.wsrc[j] = wr + k0 + chunk * 8;
   }
-
-  u32x4_t ra[4], rw[4];
-  auto gload = [&](int kb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ra[i] = asrc[i][kb >> 3];
-      rw[i] = wsrc[i][kb >> 3];
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint8_t* a = lds + buf * 2 * kTileBytes;
-    uint8_t* w = a + kTileBytes;
+  for (int mb = 0; mb < TM; ++mb) g.arow[mb] = (wm * TM + mb) * 32 + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<u32x4_t*>(a + lofs[i]) = ra[i];
-      *reinterpret_cast<u32x4_t*>(w + lofs[i]) = rw[i];
-    }
-  };
-
-  // LDS rows this lane reads as MFMA operands
-  int arow[2], wrow_l[4];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) arow[mb] = wm * 64 + mb * 32 + (lane & 31);
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    if (MODE == 0) wrow_l[nb] = wn * 128 + nb * 32 + (lane & 31);
-    else wrow_l[nb] = (nb < 2 ? 0 : 128) + wn * 64 + (nb & 1) * 32 + (lane & 31);
+  for (int nb = 0; nb < TN; ++nb) {
+    if (MODE == 0) g.wrow[nb] = (wn * TN + nb) * 32 + (lane & 31);
+    else g.wrow[nb] = (nb < TN / 2 ? 0 : NB / 2) + (wn * (TN / 2) + nb % (TN / 2)) * 32 + (lane & 31);
   }
-  const int khalf = lane >> 5;
+  g.khalf = lane >> 5;
 
-  f32x16_t acc[2][4];
+  f32x16_t acc[TM][TN];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < TM; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < TN; ++nb)
 #pragma unroll
-      for (int t = 0; t < 16; ++t) acc[mb][nb][t] = 0.f;
+      for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
 
-  if (k0 < k1) {
-    gload(k0);
-    lstore(0);
-  }
-  __syncthreads();
-  int cur = 0;
-  for (int kb = k0; kb < k1; kb += KB) {
-    const bool more = kb + KB < k1;
-    if (more) gload(kb + KB);
-    const uint8_t* a = lds + cur * 2 * kTileBytes;
-    const uint8_t* w = a + kTileBytes;
-#pragma unroll
-    for (int ks = 0; ks < KB / 16; ++ks) {
-      const int chunk = ks * 2 + khalf;
-      bf16x8_t fa[2], fw[4];
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-        fa[mb] = *reinterpret_cast<const bf16x8_t*>(a + swz(arow[mb], chunk));
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        fw[nb] = *reinterpret_cast<const bf16x8_t*>(w + swz(wrow_l[nb], chunk));
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fw[nb], acc[mb][nb], 0, 0, 0);
+  if (nsteps > 0) {
+    issue_stage<C, 0>(g, 0);
+    issue_stage<C, 1>(g, min(1, nsteps - 1) * KB);
+    issue_stage<C, 2>(g, min(2, nsteps - 1) * KB);
+    int i = 0;
+    for (; i + 4 <= nsteps; i += 4) {
+      k_step<C, TM, TN, 0>(g, i, nsteps, acc);
+      k_step<C, TM, TN, 1>(g, i + 1, nsteps, acc);
+      k_step<C, TM, TN, 2>(g, i + 2, nsteps, acc);
+      k_step<C, TM, TN, 3>(g, i + 3, nsteps, acc);
     }
-    if (more) lstore(cur ^ 1);
-    __syncthreads();
-    cur ^= 1;
+    if (i < nsteps) k_step<C, TM, TN, 0>(g, i, nsteps, acc);
+    if (i + 1 < nsteps) k_step<C, TM, TN, 1>(g, i + 1, nsteps, acc);
+    if (i + 2 < nsteps) k_step<C, TM, TN, 2>(g, i + 2, nsteps, acc);
+    wait_vmcnt<0>();
   }
 
   // epilogue
+  const int khalf = g.khalf;
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
+  for (int mb = 0; mb < TM; ++mb) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int m = m0 + wm * 64 + mb * 32 + 8 * (t >> 2) + 4 * khalf + (t & 3);
+    for (int e = 0; e < 16; ++e) {
+      const int m = m0 + (wm * TM + mb) * 32 + 8 * (e >> 2) + 4 * khalf + (e & 3);
       if (m >= M) continue;
       if (MODE == 0) {
-        float* crow = part + (static_cast<size_t>(blockIdx.z) * M + m) * N;
+        float* crow = part + (static_cast<size_t>(split) * M + m) * N;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-          const int n = n0 + wn * 128 + nb * 32 + (lane & 31);
-          if (n < N) crow[n] = acc[mb][nb][t];
+        for (int nb = 0; nb < TN; ++nb) {
+          const int n = n0 + (wn * TN + nb) * 32 + (lane & 31);
+          if (n < N) crow[n] = acc[mb][nb][e];
         }
       } else {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const int n = n0 + wn * 64 + nb * 32 + (lane & 31);
+        for (int nb = 0; nb < TN / 2; ++nb) {
+          const int n = n0 + (wn * (TN / 2) + nb) * 32 + (lane & 31);
           if (n < N) {
-            const float g = acc[mb][nb][t], u = acc[mb][nb + 2][t];
-            out[static_cast<size_t>(m) * N + n] = f32_to_bf16(g / (1.f + expf(-g)) * u);
+            const float gt = acc[mb][nb][e], up = acc[mb][nb + TN / 2][e];
+            out[static_cast<size_t>(m) * N + n] = f32_to_bf16(gt / (1.f + expf(-gt)) * up);
           }
         }
       }
     }
   }
 }
+
+// Wave arrangement used by the library.
+#ifndef KVR_GEMM_WAVES_M
+#define KVR_GEMM_WAVES_M 4
+#endif
+constexpr int kWM = KVR_GEMM_WAVES_M, kWN = 2, kTM = 8 / kWM, kTN = 4;
+constexpr int MT = 64 * kWM * kWN;
 
 }  // namespace
 
@@ -277,31 +355,17 @@ int gemm_splits_for(kvr_dtype dt, int M, int N, int K) {
   return best;
 }
 
-namespace {
-bool g_lds_attr_set = false;
-hipError_t set_lds_attr() {
-  if (g_lds_attr_set) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mfma<0>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (e == hipSuccess)
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mfma<1>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-  if (e == hipSuccess) g_lds_attr_set = true;
-  return e;
-}
-}  // namespace
-
 hipError_t launch_gemm_partial(kvr_dtype dt, const void* A, const WeightSegs& W, int M, int N,
                                int K, int splits, float* part, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const int kps = ((K / splits + 63) / 64) * 64;
   if (dt == KVR_BF16) {
-    hipError_t e = set_lds_attr();
-    if (e != hipSuccess) return e;
-    dim3 grid((N + NB - 1) / NB, (M + MB - 1) / MB, splits);
-    hipLaunchKernelGGL((k_gemm_mfma<0>), grid, dim3(MT), kLdsBytes, stream,
-                       static_cast<const bf16_t*>(A), W, M, N, K, kps, part, nullptr);
+    const int kps = ((K / splits + KB - 1) / KB) * KB;
+    const int tm = (M + MB - 1) / MB, tn = (N + NB - 1) / NB;
+    hipLaunchKernelGGL((k_gemm_mfma<0, kWM, kWN, kTM, kTN>), dim3(tm * tn * splits), dim3(MT), 0, stream,
+                       static_cast<const bf16_t*>(A), W, M, N, K, kps, tm, tn, splits, part,
+                       nullptr);
   } else {
+    const int kps = ((K / splits + 63) / 64) * 64;
     dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile, splits);
     hipLaunchKernelGGL((k_gemm_fma<float, 0>), grid, dim3(kThreads), 0, stream,
                        static_cast<const float*>(A), W, M, N, K, kps, part, nullptr);
@@ -314,11 +378,9 @@ hipError_t launch_gemm_swiglu(kvr_dtype dt, const void* A, const void* Wg, const
   if (M == 0) return hipSuccess;
   WeightSegs W{{Wg, Wu, nullptr}, {0, N, N, N}, 2};
   if (dt == KVR_BF16) {
-    hipError_t e = set_lds_attr();
-    if (e != hipSuccess) return e;
-    dim3 grid((N + NB / 2 - 1) / (NB / 2), (M + MB - 1) / MB, 1);
-    hipLaunchKernelGGL((k_gemm_mfma<1>), grid, dim3(MT), kLdsBytes, stream,
-                       static_cast<const bf16_t*>(A), W, M, N, K, K, nullptr,
+    const int tm = (M + MB - 1) / MB, tn = (N + NB / 2 - 1) / (NB / 2);
+    hipLaunchKernelGGL((k_gemm_mfma<1, kWM, kWN, kTM, kTN>), dim3(tm * tn), dim3(MT), 0, stream,
+                       static_cast<const bf16_t*>(A), W, M, N, K, K, tm, tn, 1, nullptr,
                        static_cast<bf16_t*>(out));
   } else {
     dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile, 1);

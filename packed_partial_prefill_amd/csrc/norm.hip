@@ -1,7 +1,8 @@
 // Row kernels on the packed residual stream: the one-time gather of the
 // selected rows (the compact B-row hidden buffer of "Budgeted KV-Cache
 // Repair", section 13.2), split-K partial sums added to the residual, and
-// RMSNorm producing the next GEMM's operand.
+// RMSNorm producing the next GEMM's operand.  One workgroup per row; every
+// thread owns float4 chunks of the row (hidden is a multiple of 64).
 #include "common.h"
 #include "kvr_internal.h"
 
@@ -10,7 +11,25 @@ namespace kvr {
 namespace {
 
 constexpr int kRowThreads = 256;
-constexpr int kMaxPerThread = 32;  // hidden <= 8192
+constexpr int kMaxChunks = 8;  // float4 chunks per thread: hidden <= 8192
+
+template <typename T>
+__device__ __forceinline__ void store4(T* row, int j4, float4 v);
+template <>
+__device__ __forceinline__ void store4<float>(float* row, int j4, float4 v) {
+  reinterpret_cast<float4*>(row)[j4] = v;
+}
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* row, int j4, float4 v) {
+  uint2 p;
+  p.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+  p.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+  reinterpret_cast<uint2*>(row)[j4] = p;
+}
+
+__device__ __forceinline__ float4 scale4(float4 v, float s, float4 g) {
+  return make_float4(v.x * s * g.x, v.y * s * g.y, v.z * s * g.z, v.w * s * g.w);
+}
 
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_gather_norm(
@@ -18,50 +37,71 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_norm(
     const float* __restrict__ gamma, float eps, T* __restrict__ n_out, int hidden) {
   __shared__ float red[16];
   const int r = blockIdx.x;
+  const int h4 = hidden >> 2;
   const size_t src = gather_T ? static_cast<size_t>(gather_T[r]) : static_cast<size_t>(r);
-  const float* xr = x_in + src * hidden;
-  float v[kMaxPerThread];
+  const float4* xr = reinterpret_cast<const float4*>(x_in + src * hidden);
+  float4 v[kMaxChunks];
   float ss = 0.f;
-  int c = 0;
-  for (int j = threadIdx.x; j < hidden; j += kRowThreads, ++c) {
-    v[c] = xr[j];
-    ss += v[c] * v[c];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int j4 = threadIdx.x + c * kRowThreads;
+    if (j4 < h4) {
+      v[c] = xr[j4];
+      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    }
   }
   const float tot = block_sum(ss, red);  // all reads of x_in precede any write
   const float rs = rsqrtf(tot / hidden + eps);
-  float* xo = x_res + static_cast<size_t>(r) * hidden;
+  float4* xo = reinterpret_cast<float4*>(x_res + static_cast<size_t>(r) * hidden);
   T* no = n_out + static_cast<size_t>(r) * hidden;
-  c = 0;
-  for (int j = threadIdx.x; j < hidden; j += kRowThreads, ++c) {
-    xo[j] = v[c];
-    Elem<T>::store(no, j, v[c] * rs * gamma[j]);
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int j4 = threadIdx.x + c * kRowThreads;
+    if (j4 < h4) {
+      xo[j4] = v[c];
+      store4<T>(no, j4, scale4(v[c], rs, g4[j4]));
+    }
   }
 }
 
+// x_res[r] += sum_s part[s][r]; when gamma is given, n_out[r] = RMSNorm(x_res[r]) * gamma.
 template <typename T>
 __global__ __launch_bounds__(kRowThreads) void k_residual_norm(
     float* __restrict__ x_res, const float* __restrict__ part, int splits, size_t split_stride,
     const float* __restrict__ gamma, float eps, T* __restrict__ n_out, int hidden) {
   __shared__ float red[16];
   const int r = blockIdx.x;
-  float* xr = x_res + static_cast<size_t>(r) * hidden;
-  const float* pr = part + static_cast<size_t>(r) * hidden;
-  float v[kMaxPerThread];
+  const int h4 = hidden >> 2;
+  float4* xr = reinterpret_cast<float4*>(x_res + static_cast<size_t>(r) * hidden);
+  const float4* pr = reinterpret_cast<const float4*>(part + static_cast<size_t>(r) * hidden);
+  const size_t ps4 = split_stride >> 2;
+  float4 v[kMaxChunks];
   float ss = 0.f;
-  int c = 0;
-  for (int j = threadIdx.x; j < hidden; j += kRowThreads, ++c) {
-    float a = 0.f;
-    for (int s = 0; s < splits; ++s) a += pr[s * split_stride + j];
-    v[c] = xr[j] + a;
-    xr[j] = v[c];
-    ss += v[c] * v[c];
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int j4 = threadIdx.x + c * kRowThreads;
+    if (j4 < h4) {
+      float4 a = xr[j4];
+      for (int s = 0; s < splits; ++s) {
+        const float4 p = pr[s * ps4 + j4];
+        a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
+      }
+      v[c] = a;
+      xr[j4] = a;
+      ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+    }
   }
   if (gamma == nullptr) return;
   const float tot = block_sum(ss, red);
   const float rs = rsqrtf(tot / hidden + eps);
   T* no = n_out + static_cast<size_t>(r) * hidden;
-  c = 0;
-  for (int j = threadIdx.x; j < hidden; j += kRowThreads, ++c) Elem<T>::store(no, j, v[c] * rs * gamma[j]);
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c) {
+    const int j4 = threadIdx.x + c * kRowThreads;
+    if (j4 < h4) store4<T>(no, j4, scale4(v[c], rs, g4[j4]));
+  }
 }
 
 }  // namespace

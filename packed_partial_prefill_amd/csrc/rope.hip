@@ -18,51 +18,86 @@ namespace {
 constexpr int kThreads = 256;
 
 template <typename T>
+__device__ __forceinline__ void put4(T* p, float4 v);
+template <>
+__device__ __forceinline__ void put4<float>(float* p, float4 v) {
+  *reinterpret_cast<float4*>(p) = v;
+}
+template <>
+__device__ __forceinline__ void put4<bf16_t>(bf16_t* p, float4 v) {
+  uint2 w;
+  w.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+  w.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+
+// Sum of the split-K partials of 4 consecutive columns starting at c.
+__device__ __forceinline__ float4 cols4(const float* pr, int splits, size_t split_stride, int c) {
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < splits; ++s)
+    a = add4(a, *reinterpret_cast<const float4*>(pr + s * split_stride + c));
+  return a;
+}
+
+// Rotate 4 consecutive pairs (i .. i+3, i+half .. i+half+3) of one head.
+template <typename T>
+__device__ __forceinline__ void rotate4(const float* pr, int splits, size_t split_stride,
+                                        const float* bias, int c0, int half,
+                                        const float2* tr, float scale, T* dst) {
+  float4 a = cols4(pr, splits, split_stride, c0);
+  float4 b = cols4(pr, splits, split_stride, c0 + half);
+  if (bias) {
+    a = add4(a, *reinterpret_cast<const float4*>(bias + c0));
+    b = add4(b, *reinterpret_cast<const float4*>(bias + c0 + half));
+  }
+  const float4 t01 = *reinterpret_cast<const float4*>(tr);       // (cos, sin) of pairs i, i+1
+  const float4 t23 = *reinterpret_cast<const float4*>(tr + 2);   // pairs i+2, i+3
+  const float c[4] = {t01.x, t01.z, t23.x, t23.z}, sn[4] = {t01.y, t01.w, t23.y, t23.w};
+  const float av[4] = {a.x, a.y, a.z, a.w}, bv[4] = {b.x, b.y, b.z, b.w};
+  float lo[4], hi[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    lo[j] = (av[j] * c[j] - bv[j] * sn[j]) * scale;
+    hi[j] = (bv[j] * c[j] + av[j] * sn[j]) * scale;
+  }
+  put4<T>(dst, make_float4(lo[0], lo[1], lo[2], lo[3]));
+  put4<T>(dst + half, make_float4(hi[0], hi[1], hi[2], hi[3]));
+}
+
+template <typename T>
 __global__ __launch_bounds__(kThreads) void k_rope_writeback(
     const float* __restrict__ part, int splits, size_t split_stride, const float* __restrict__ bq,
     const float* __restrict__ bk, const float* __restrict__ bv, const float2* __restrict__ tab,
     const int32_t* __restrict__ Tpos, Shape sh, float q_scale, T* __restrict__ q_out,
-    T* __restrict__ kc,
-    T* __restrict__ vc, uint8_t* __restrict__ flags) {
+    T* __restrict__ kc, T* __restrict__ vc, uint8_t* __restrict__ flags) {
   const int r = blockIdx.x;
   const int u = Tpos[r];
-  const int d = sh.d, half = d >> 1, ncols = sh.qkv_cols();
+  const int d = sh.d, half = d >> 1, q4 = half >> 2, ncols = sh.qkv_cols();
   const float* pr = part + static_cast<size_t>(r) * ncols;
   const float2* tr = tab + static_cast<size_t>(r) * half;
-  auto col = [&](int c) {
-    float a = 0.f;
-    for (int s = 0; s < splits; ++s) a += pr[s * split_stride + c];
-    return a;
-  };
-  // query heads
-  for (int idx = threadIdx.x; idx < sh.hq * half; idx += kThreads) {
-    const int h = idx / half, i = idx - h * half;
-    const int c0 = h * d + i;
-    float a = col(c0), b = col(c0 + half);
-    if (bq) { a += bq[c0]; b += bq[c0 + half]; }
-    const float2 cs = tr[i];
-    T* qo = q_out + (static_cast<size_t>(r) * sh.hq + h) * d;
-    Elem<T>::store(qo, i, (a * cs.x - b * cs.y) * q_scale);
-    Elem<T>::store(qo, i + half, (b * cs.x + a * cs.y) * q_scale);
+  // query heads (times the attention kernel's score factor)
+  for (int idx = threadIdx.x; idx < sh.hq * q4; idx += kThreads) {
+    const int h = idx / q4, i = (idx - h * q4) * 4;
+    rotate4<T>(pr, splits, split_stride, bq, h * d + i, half, tr + i, q_scale,
+               q_out + (static_cast<size_t>(r) * sh.hq + h) * d + i);
   }
   // key heads: rotated, written to cache row u
   const int kbase = sh.hq * d;
-  for (int idx = threadIdx.x; idx < sh.hkv * half; idx += kThreads) {
-    const int g = idx / half, i = idx - g * half;
-    const int c0 = g * d + i;
-    float a = col(kbase + c0), b = col(kbase + c0 + half);
-    if (bk) { a += bk[c0]; b += bk[c0 + half]; }
-    const float2 cs = tr[i];
-    T* ko = kc + (static_cast<size_t>(u) * sh.hkv + g) * d;
-    Elem<T>::store(ko, i, a * cs.x - b * cs.y);
-    Elem<T>::store(ko, i + half, b * cs.x + a * cs.y);
+  for (int idx = threadIdx.x; idx < sh.hkv * q4; idx += kThreads) {
+    const int g = idx / q4, i = (idx - g * q4) * 4;
+    rotate4<T>(pr + kbase, splits, split_stride, bk, g * d + i, half, tr + i, 1.f,
+               kc + (static_cast<size_t>(u) * sh.hkv + g) * d + i);
   }
   // values: copied to cache row u
   const int vbase = (sh.hq + sh.hkv) * d;
-  for (int idx = threadIdx.x; idx < sh.hkv * d; idx += kThreads) {
-    float a = col(vbase + idx);
-    if (bv) a += bv[idx];
-    Elem<T>::store(vc + static_cast<size_t>(u) * sh.hkv * d, idx, a);
+  for (int idx = threadIdx.x; idx < sh.hkv * (d >> 2); idx += kThreads) {
+    float4 a = cols4(pr, splits, split_stride, vbase + idx * 4);
+    if (bv) a = add4(a, *reinterpret_cast<const float4*>(bv + idx * 4));
+    put4<T>(vc + static_cast<size_t>(u) * sh.hkv * d + idx * 4, a);
   }
   if (threadIdx.x == 0) flags[u] = static_cast<uint8_t>(flags[u] & ~(KVR_FLAG_LOCAL | KVR_FLAG_SINK));
 }
