@@ -73,46 +73,60 @@ __global__ __launch_bounds__(64) void k_attn_rowwise(const T* __restrict__ q,
 //
 // A workgroup owns KVR_ATTN_QROWS = 128 (packed row, query head) pairs of one
 // KV head group and a range of 64-key tiles (split-KV); 4 waves x 32 pairs.
-// Every key tile is staged once in LDS for all 128 pairs: K in its natural
-// [key][d] layout (16-byte chunks XOR-swizzled by key), V transposed to
-// [d][key] (rows padded to 136 bytes), plus one float bias per key.
+// Every key tile is staged once in LDS for all 128 pairs, double-buffered,
+// by global_load_lds_dwordx4 (no register staging): K and V both in their
+// natural [key][d] layout with the 16-byte chunks of each key row
+// XOR-swizzled, plus one float bias per key written by 64 threads.
 // Scores are formed transposed, S^T = K Q^T, so each lane owns one query
 // column and 16 of the tile's keys: the softmax reduction is in-lane plus one
-// exchange with lane ^ 32.  O^T += V^T P^T then takes the lane's own P values
-// as the B operand; both operands list the keys of one 16-key step in the
-// same permuted order (4h..4h+3, 8+4h..8+4h+3 for lane half h).
+// exchange with lane ^ 32.  O^T += V^T P^T takes the lane's own P values as
+// the B operand; its A operand (V^T rows) comes from ds_read_b64_tr_b16,
+// which hands each lane 4 keys of one d column out of 16 lanes' row reads.
+// Both operands list the keys of a 16-key step in the same order (4h..4h+3,
+// 8+4h..8+4h+3 for lane half h).
 // Tiles below the plan's n_full (Eq. 23) are visible to every pair and skip
 // the causal test.  Q arrives pre-scaled by log2(e)/sqrt(d), so the softmax
-// runs in base 2 with the bias pre-multiplied by log2(e).
+// runs in base 2 with the bias pre-multiplied by log2(e).  The running max
+// moves lazily (only when a tile exceeds it by more than 8), which keeps
+// probabilities below 2^8 and skips most accumulator rescales.
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
 typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQRows = KVR_ATTN_QROWS;     // 128 pairs per workgroup
 constexpr int kKvTile = KVR_ATTN_KV_TILE;  // 64 keys per tile
 constexpr int kAttnThreads = 256;
-constexpr int kVtStride = 2 * kKvTile + 8;  // bytes per transposed V row (136)
+
+#define KVR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define KVR_GLB(p) ((const __attribute__((address_space(1))) void*)(p))
+
+template <int N> __device__ __forceinline__ void attn_wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
+}
 
 template <int D>
 struct AttnLds {
   static constexpr int kBytes = kKvTile * D * 2;   // K tile
-  static constexpr int vBytes = D * kVtStride;     // V^T tile
+  static constexpr int vBytes = kKvTile * D * 2;   // V tile
   static constexpr int bBytes = kKvTile * 4;       // bias
   static constexpr int stage = kBytes + vBytes + bBytes;
   static constexpr int total = 2 * stage;
+  static constexpr int slices = (kBytes + vBytes) / 1024 / 4;   // 1 KB DMA slices per wave
 };
 
-// 16-byte chunk c of key row k sits at c ^ (k & 15) for 256-byte rows
-// (d = 128) and at c ^ ((k & 7) ^ ((k >> 3) & 1)) for 128-byte rows (d = 64):
-// the 32 rows one MFMA operand load reads then spread over distinct 16-byte
-// bank slots per 8-lane (128 B) and per 16-lane (256 B) pass.
+// Physical 16-byte chunk of logical chunk c in key row k.  K rows: c ^ (k & 15)
+// (d = 128) or c ^ ((k & 7) ^ ((k >> 3) & 1)) (d = 64), so the 32 rows of an
+// MFMA operand read hit distinct bank slots.  V rows: c ^ (2 * (k & 3)), so
+// the 4 rows x 2 chunks a 16-lane transposing read touches are distinct.
 template <int D>
-__device__ __forceinline__ int kswz(int key, int chunk) {
-  const int x = (D == 128) ? (key & 15) : ((key & 7) ^ ((key >> 3) & 1));
-  return key * (D * 2) + ((chunk ^ x) << 4);
+__device__ __forceinline__ int kchunk(int key, int c) {
+  return c ^ ((D == 128) ? (key & 15) : ((key & 7) ^ ((key >> 3) & 1)));
 }
+__device__ __forceinline__ int vchunk(int key, int c) { return c ^ (2 * (key & 3)); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -125,7 +139,8 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
     float* __restrict__ part_o, float* __restrict__ part_ml) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   using L = AttnLds<D>;
-  constexpr int KCH = D / 8;   // 16-byte chunks per key row
+  constexpr int KCH = D / 8;             // 16-byte chunks per key row
+  constexpr int ROWS = 1024 / (D * 2);   // key rows per 1 KB DMA slice
   const int qt = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int tot = n_total[qt];
   const int c0 = sp * split_tiles;
@@ -152,57 +167,48 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   const bf16_t* kg = kc + static_cast<size_t>(g) * D;
   const bf16_t* vg = vc + static_cast<size_t>(g) * D;
 
-  // staging registers
-  constexpr int KLOADS = kKvTile * KCH / kAttnThreads;        // 4 (D=128) or 2 (D=64)
-  constexpr int VITEMS = (kKvTile / 4) * KCH;                 // 256 or 128
-  u32x4_t rk[KLOADS], rv[4];
-  uint8_t rf = 0;
-  auto gload = [&](int c) {
+  // DMA slices of this wave: slice j covers key rows [j*ROWS, (j+1)*ROWS) of
+  // K (j < 64/ROWS) or V.  Lane i lands at byte i*16 of the slice: row
+  // i / KCH, physical chunk i % KCH, so it fetches the matching logical chunk.
+  constexpr int KSL = kKvTile / ROWS;   // slices per operand per tile (16 or 8)
+  int s_row[L::slices], s_col[L::slices], s_dst[L::slices];
+  bool s_isv[L::slices];
+#pragma unroll
+  for (int j = 0; j < L::slices; ++j) {
+    const int sl = wave * L::slices + j;         // 0 .. 2*KSL-1
+    const bool isv = sl >= KSL;
+    const int row = (isv ? sl - KSL : sl) * ROWS + lane / KCH;
+    const int phys = lane % KCH;
+    const int logical = isv ? vchunk(row, phys) : kchunk<D>(row, phys);   // involutions
+    s_isv[j] = isv;
+    s_row[j] = row;
+    s_col[j] = logical * 8;
+    s_dst[j] = (isv ? L::kBytes : 0) + (isv ? sl - KSL : sl) * 1024;
+  }
+  auto issue = [&](int c, int buf) {
     const int kv0 = c * kKvTile;
+    uint8_t* base = lds + buf * L::stage;
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int v = tid + i * kAttnThreads;
-      const int key = min(kv0 + v / KCH, n_tokens - 1);
-      rk[i] = *reinterpret_cast<const u32x4_t*>(kg + key * kv_row + (v % KCH) * 8);
+    for (int j = 0; j < L::slices; ++j) {
+      const int key = min(kv0 + s_row[j], n_tokens - 1);   // clamped rows are masked
+      const bf16_t* src = (s_isv[j] ? vg : kg) + key * kv_row + s_col[j];
+      __builtin_amdgcn_global_load_lds(KVR_GLB(src), KVR_LDS(base + s_dst[j]), 16, 0, 0);
     }
-    if (tid < VITEMS) {
-      const int kgp = tid % (kKvTile / 4), ch = tid / (kKvTile / 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = min(kv0 + kgp * 4 + j, n_tokens - 1);
-        rv[j] = *reinterpret_cast<const u32x4_t*>(vg + key * kv_row + ch * 8);
-      }
-    }
-    if (tid < kKvTile) rf = flags[min(kv0 + tid, n_tokens - 1)];
   };
-  auto lstore = [&](int buf) {
-    uint8_t* kb = lds + buf * L::stage;
-    uint8_t* vb = kb + L::kBytes;
-    float* bb = reinterpret_cast<float*>(vb + L::vBytes);
-#pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int v = tid + i * kAttnThreads;
-      *reinterpret_cast<u32x4_t*>(kb + kswz<D>(v / KCH, v % KCH)) = rk[i];
-    }
-    if (tid < VITEMS) {
-      const int kgp = tid % (kKvTile / 4), ch = tid / (kKvTile / 4);
-      // rv[j] holds d = ch*8 .. +7 of key 4*kgp + j; emit, per d, keys 4*kgp .. +3
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint32_t a0 = rv[0][w], a1 = rv[1][w], a2 = rv[2][w], a3 = rv[3][w];
-        u32x2_t lo, hi;   // d = ch*8 + 2w (low halves) and + 2w + 1 (high halves)
-        lo[0] = __builtin_amdgcn_perm(a1, a0, 0x05040100u);
-        lo[1] = __builtin_amdgcn_perm(a3, a2, 0x05040100u);
-        hi[0] = __builtin_amdgcn_perm(a1, a0, 0x07060302u);
-        hi[1] = __builtin_amdgcn_perm(a3, a2, 0x07060302u);
-        const int d0 = ch * 8 + 2 * w;
-        *reinterpret_cast<u32x2_t*>(vb + d0 * kVtStride + kgp * 8) = lo;
-        *reinterpret_cast<u32x2_t*>(vb + (d0 + 1) * kVtStride + kgp * 8) = hi;
-      }
-    }
-    if (tid < kKvTile)
+  uint8_t rf = 0;
+  auto fload = [&](int c) {
+    if (tid < kKvTile) rf = flags[min(c * kKvTile + tid, n_tokens - 1)];
+  };
+  auto fstore = [&](int buf) {
+    if (tid < kKvTile) {
+      float* bb = reinterpret_cast<float*>(lds + buf * L::stage + L::kBytes + L::vBytes);
       bb[tid] = ((rf & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((rf & KVR_FLAG_SINK) ? bias_sink : 0.f);
+    }
   };
+
+  // transposing-read address pattern of this lane (see header comment)
+  const int tr_key = (lane & 15) >> 2;                          // key within the 4-key group
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // d offset within a 32-row block
 
   f32x16_t o[D / 32];
 #pragma unroll
@@ -211,13 +217,18 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
     for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
   float m = -INFINITY, l = 0.f;
 
-  gload(c0);
-  lstore(0);
+  issue(c0, 0);
+  fload(c0);
+  fstore(0);
+  attn_wait_vmcnt<0>();
   __syncthreads();
   int cur = 0;
   for (int c = c0; c < c1; ++c) {
     const bool more = c + 1 < c1;
-    if (more) gload(c + 1);
+    if (more) {
+      issue(c + 1, cur ^ 1);
+      fload(c + 1);
+    }
     const uint8_t* kb = lds + cur * L::stage;
     const uint8_t* vb = kb + L::kBytes;
     const float* bb = reinterpret_cast<const float*>(vb + L::vBytes);
@@ -231,14 +242,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
       const int key = sb * 32 + (lane & 31);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(kb + kswz<D>(key, ks * 2 + half));
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+            kb + key * (D * 2) + (kchunk<D>(key, ks * 2 + half) << 4));
         s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[sb], 0, 0, 0);
       }
     }
     // bias (4 consecutive keys per LDS read), causal test on partially
     // visible tiles, tile maximum
     const bool partial = c >= nf;
-    const int kv0 = c * kKvTile;
+    const int lim = u - c * kKvTile;   // keys kl > lim lie in the future
     float mt = -INFINITY;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
@@ -250,15 +262,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           float x = s[sb][4 * t4 + j] + bv[j];
-          if (partial && kv0 + kl0 + j > u) x = -INFINITY;
+          if (partial && kl0 + j > lim) x = -INFINITY;
           s[sb][4 * t4 + j] = x;
           mt = fmaxf(mt, x);
         }
       }
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    // Lazy rescaling: the reference maximum m only moves when the tile's
-    // maximum exceeds it by more than 8 (log2 units), so probabilities stay
-    // below 2^8 and most tiles skip rescaling the accumulators.
     const bool bump = mt > m + 8.f;
     if (__builtin_amdgcn_ballot_w64(bump) != 0) {
       const float mn = bump ? mt : m;
@@ -288,20 +297,28 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
         bf16x8_t pb;
 #pragma unroll
         for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[sb][hs * 8 + i]);
-        const int kcol = (sb * 32 + hs * 16 + 4 * half) * 2;   // byte offset of key group
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const uint8_t* vr = vb + (db * 32 + (lane & 31)) * kVtStride + kcol;
-          const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(vr);
-          const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(vr + 16);
-          u32x4_t av;
-          av[0] = x0[0]; av[1] = x0[1]; av[2] = x1[0]; av[3] = x1[1];
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, av), pb,
-                                                          o[db], 0, 0, 0);
+          s16x4_t x[2];
+#pragma unroll
+          for (int ins = 0; ins < 2; ++ins) {
+            const int key = sb * 32 + hs * 16 + 8 * ins + 4 * half + tr_key;
+            const int d = db * 32 + tr_d;
+            const uint8_t* addr = vb + key * (D * 2) + (vchunk(key, d >> 3) << 4) + (d & 7) * 2;
+            x[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4_t*)(addr));
+          }
+          const s16x4_t x0 = x[0], x1 = x[1];
+          const short av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          bf16x8_t a;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(__bf16, av[i]);
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
         }
       }
 
-    if (more) lstore(cur ^ 1);
+    if (more) fstore(cur ^ 1);
+    attn_wait_vmcnt<0>();   // the next tile's DMA has landed (this wave's part)
     __syncthreads();
     cur ^= 1;
   }

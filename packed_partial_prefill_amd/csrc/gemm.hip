@@ -104,7 +104,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fma(const T* __restrict__ A, 
 // and a 128-column slice (2 x 4 blocks of 32x32).  K advances 32 at a time
 // through four LDS stages that are filled straight from global memory by
 // global_load_lds_dwordx4 (no register staging), three stages ahead of the
-// MFMAs.  Each stage holds a 256 x 32 tile of A and of W as 64-byte rows of
+// MFMAs; the barrier that recycles a stage sits in the middle of each step,
+// after the first half of its MFMAs is issued, so the matrix core stays busy
+// while the waves synchronise.  Each stage holds a 256 x 32 tile of A and of W as 64-byte rows of
 // four 16-byte chunks; chunk c of row r sits at c ^ (((r >> 1) ^ (r >> 3)) & 3),
 // so any 8 consecutive rows read by an MFMA operand load fall in distinct
 // 16-byte slots of 128 bytes and any 16 in distinct slots of 256 bytes (no
@@ -187,37 +189,36 @@ __device__ __forceinline__ void issue_stage(const GemmThread<C>& g, int kb) {
 }
 
 template <class C, int TM, int TN, int S>
-__device__ __forceinline__ void mma_stage(const GemmThread<C>& g, f32x16_t (&acc)[TM][TN]) {
+__device__ __forceinline__ void mma_half(const GemmThread<C>& g, int ks, f32x16_t (&acc)[TM][TN]) {
   const uint8_t* a = a_stage<S>();
   const uint8_t* w = w_stage<S>();
+  const int chunk = ks * 2 + g.khalf;
+  bf16x8_t fa[TM], fw[TN];
 #pragma unroll
-  for (int ks = 0; ks < KB / 16; ++ks) {
-    const int chunk = ks * 2 + g.khalf;
-    bf16x8_t fa[TM], fw[TN];
+  for (int mb = 0; mb < TM; ++mb) fa[mb] = *reinterpret_cast<const bf16x8_t*>(a + swz(g.arow[mb], chunk));
 #pragma unroll
-    for (int mb = 0; mb < TM; ++mb) fa[mb] = *reinterpret_cast<const bf16x8_t*>(a + swz(g.arow[mb], chunk));
+  for (int nb = 0; nb < TN; ++nb) fw[nb] = *reinterpret_cast<const bf16x8_t*>(w + swz(g.wrow[nb], chunk));
 #pragma unroll
-    for (int nb = 0; nb < TN; ++nb) fw[nb] = *reinterpret_cast<const bf16x8_t*>(w + swz(g.wrow[nb], chunk));
+  for (int mb = 0; mb < TM; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < TM; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < TN; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fw[nb], acc[mb][nb], 0, 0, 0);
-  }
+    for (int nb = 0; nb < TN; ++nb)
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fw[nb], acc[mb][nb], 0, 0, 0);
 }
 
-// One K step on stage S: wait until only the two newer stages are still in
-// flight, barrier, refill the stage consumed one step earlier with the step
-// three ahead (clamped to the last step: a refill past the end is never
-// read), then run the MFMAs.  Every step issues exactly one stage, so the
-// wait count is fixed (2 pending stages of 2 * loads DMA slices per wave).
+// One K step on stage S (its data was certified by the previous barrier):
+// the first 16-wide half is read and its MFMAs issued; then, with those in
+// flight, wait until the next stage's DMA has landed (one newer stage may
+// stay in flight), barrier (every wave is past the previous stage), refill
+// the previous stage's buffers with the step three ahead (clamped to the last
+// step: a refill past the end is never read), and run the second half.
 template <class C, int TM, int TN, int S>
 __device__ __forceinline__ void k_step(const GemmThread<C>& g, int i, int nsteps,
                                        f32x16_t (&acc)[TM][TN]) {
-  wait_vmcnt<4 * C::loads>();
+  mma_half<C, TM, TN, S>(g, 0, acc);
+  wait_vmcnt<2 * C::loads>();
   __builtin_amdgcn_s_barrier();
   issue_stage<C, (S + 3) % kStages>(g, min(i + 3, nsteps - 1) * KB);
-  mma_stage<C, TM, TN, S>(g, acc);
+  mma_half<C, TM, TN, S>(g, 1, acc);
 }
 
 // MODE 0: part[split][M][N] = A * W^T over this split's K range (W segmented).
@@ -287,6 +288,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_mfma(
     issue_stage<C, 0>(g, 0);
     issue_stage<C, 1>(g, min(1, nsteps - 1) * KB);
     issue_stage<C, 2>(g, min(2, nsteps - 1) * KB);
+    wait_vmcnt<4 * C::loads>();       // stage 0 landed; stages 1 and 2 may be in flight
+    __builtin_amdgcn_s_barrier();
     int i = 0;
     for (; i + 4 <= nsteps; i += 4) {
       k_step<C, TM, TN, 0>(g, i, nsteps, acc);
