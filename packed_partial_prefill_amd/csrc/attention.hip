@@ -76,7 +76,8 @@ __global__ __launch_bounds__(64) void k_attn_rowwise(const T* __restrict__ q,
 // Every key tile is staged once in LDS for all 128 pairs, double-buffered,
 // by global_load_lds_dwordx4 (no register staging): K and V both in their
 // natural [key][d] layout with the 16-byte chunks of each key row
-// XOR-swizzled, plus one float bias per key written by 64 threads.
+// XOR-swizzled, plus one 16-byte score slice per key written by 64 threads
+// (see below).
 // Scores are formed transposed, S^T = K Q^T, so each lane owns one query
 // column and 16 of the tile's keys: the softmax reduction is in-lane plus one
 // exchange with lane ^ 32.  O^T += V^T P^T takes the lane's own P values as
@@ -86,9 +87,9 @@ __global__ __launch_bounds__(64) void k_attn_rowwise(const T* __restrict__ q,
 // 8+4h..8+4h+3 for lane half h).
 // Tiles below the plan's n_full (Eq. 23) are visible to every pair and skip
 // the causal test.  Q arrives pre-scaled by log2(e)/sqrt(d), so the softmax
-// runs in base 2 with the bias pre-multiplied by log2(e).  The running max
-// moves lazily (only when a tile exceeds it by more than 8), which keeps
-// probabilities below 2^8 and skips most accumulator rescales.
+// runs in base 2 with the bias pre-multiplied by log2(e); bias and running
+// maximum enter through the score MFMA, leaving max, exp2, sum and the bf16
+// pack as the per-score VALU work.
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
@@ -112,7 +113,7 @@ template <int D>
 struct AttnLds {
   static constexpr int kBytes = kKvTile * D * 2;   // K tile
   static constexpr int vBytes = kKvTile * D * 2;   // V tile
-  static constexpr int bBytes = kKvTile * 4;       // bias
+  static constexpr int bBytes = kKvTile * 16;      // score slice per key: [b_hi, b_lo, 1, 1, 0 x 4]
   static constexpr int stage = kBytes + vBytes + bBytes;
   static constexpr int total = 2 * stage;
   static constexpr int slices = (kBytes + vBytes) / 1024 / 4;   // 1 KB DMA slices per wave
@@ -162,6 +163,24 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
   }
+  // The score MFMA takes one more 16-wide K slice: key j supplies
+  // [b_hi, b_lo, 1, 1, 0...] (b_hi + b_lo = bf16 split of the key's bias),
+  // the query supplies [1, 1, -m_hi, -m_lo, 0...] (lanes of the upper half
+  // supply zeros), so the MFMA yields s + bias - m_eff with
+  // m_eff = m_hi + m_lo the query's current reference maximum.
+  float m_eff = 0.f;
+  bool m_set = false;
+  bf16x8_t qx;
+  auto set_qx = [&](float mref) {
+    const bf16_t mh = f32_to_bf16(-mref);
+    const bf16_t ml = f32_to_bf16(-mref - bf16_to_f32(mh));
+    m_eff = -(bf16_to_f32(mh) + bf16_to_f32(ml));
+    const bf16_t one = 0x3F80;
+    const bf16_t v[8] = {one, one, mh, ml, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qx[i] = __builtin_bit_cast(__bf16, half == 0 ? v[i] : static_cast<bf16_t>(0));
+  };
+  set_qx(0.f);
 
   const size_t kv_row = static_cast<size_t>(Hkv) * D;   // elements between positions
   const bf16_t* kg = kc + static_cast<size_t>(g) * D;
@@ -201,8 +220,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   };
   auto fstore = [&](int buf) {
     if (tid < kKvTile) {
-      float* bb = reinterpret_cast<float*>(lds + buf * L::stage + L::kBytes + L::vBytes);
-      bb[tid] = ((rf & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((rf & KVR_FLAG_SINK) ? bias_sink : 0.f);
+      const float b = ((rf & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((rf & KVR_FLAG_SINK) ? bias_sink : 0.f);
+      const bf16_t bh = f32_to_bf16(b);
+      const bf16_t bl = f32_to_bf16(b - bf16_to_f32(bh));
+      u32x4_t ch;
+      ch[0] = static_cast<uint32_t>(bh) | (static_cast<uint32_t>(bl) << 16);
+      ch[1] = 0x3F803F80u;   // bf16 1.0, 1.0: multiply the query's -m_hi, -m_lo
+      ch[2] = 0u;
+      ch[3] = 0u;
+      *reinterpret_cast<u32x4_t*>(lds + buf * L::stage + L::kBytes + L::vBytes + tid * 16) = ch;
     }
   };
 
@@ -215,7 +241,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   for (int db = 0; db < D / 32; ++db)
 #pragma unroll
     for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
-  float m = -INFINITY, l = 0.f;
+  float l = 0.f;
 
   issue(c0, 0);
   fload(c0);
@@ -231,9 +257,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
     }
     const uint8_t* kb = lds + cur * L::stage;
     const uint8_t* vb = kb + L::kBytes;
-    const float* bb = reinterpret_cast<const float*>(vb + L::vBytes);
+    const uint8_t* bb = vb + L::vBytes;
 
-    // S^T = K Q^T for the two 32-key halves of the tile
+    // S^T = K Q^T + (bias - m_eff) for the two 32-key halves of the tile
     f32x16_t s[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
@@ -246,45 +272,51 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
             kb + key * (D * 2) + (kchunk<D>(key, ks * 2 + half) << 4));
         s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[sb], 0, 0, 0);
       }
+      const bf16x8_t ab = *reinterpret_cast<const bf16x8_t*>(bb + key * 16);
+      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, qx, s[sb], 0, 0, 0);
     }
-    // bias (4 consecutive keys per LDS read), causal test on partially
-    // visible tiles, tile maximum
-    const bool partial = c >= nf;
-    const int lim = u - c * kKvTile;   // keys kl > lim lie in the future
-    float mt = -INFINITY;
+    // causal test only on partially visible tiles (uniform branch)
+    if (c >= nf) {
+      const int lim = u - c * kKvTile;   // keys kl > lim lie in the future
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int kl = sb * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
+          if (kl > lim) s[sb][t] = -INFINITY;
+        }
+    }
+    float mt = -INFINITY;   // tile maximum of s + bias - m_eff
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) {
-        const int kl0 = sb * 32 + 8 * t4 + 4 * half;
-        const float4 b4 = *reinterpret_cast<const float4*>(bb + kl0);
-        const float bv[4] = {b4.x, b4.y, b4.z, b4.w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float x = s[sb][4 * t4 + j] + bv[j];
-          if (partial && kl0 + j > lim) x = -INFINITY;
-          s[sb][4 * t4 + j] = x;
-          mt = fmaxf(mt, x);
-        }
-      }
+      for (int t = 0; t < 16; ++t) mt = fmaxf(mt, s[sb][t]);
     mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
-    const bool bump = mt > m + 8.f;
+    // Lazy maximum: m_eff moves only when the tile exceeds it by more than 8
+    // (log2 units) or is the query's first visible tile, so probabilities
+    // stay below 2^8 and most tiles skip rescaling.  After a move the tile's
+    // scores are re-based by the shift.
+    const bool bump = (mt > 8.f) || (!m_set && mt != -INFINITY);
+    float shift = 0.f;
     if (__builtin_amdgcn_ballot_w64(bump) != 0) {
-      const float mn = bump ? mt : m;
-      const float corr = (m == -INFINITY) ? 0.f : fast_exp2(m - mn);
-      l *= corr;
+      if (bump) {
+        const float old = m_eff;
+        set_qx(m_eff + mt);
+        shift = m_eff - old;
+        const float corr = m_set ? fast_exp2(-shift) : 0.f;
+        l *= corr;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) o[db][t] *= corr;
-      m = mn;
+          for (int t = 0; t < 16; ++t) o[db][t] *= corr;
+        m_set = true;
+      }
     }
-    const float mu = (m == -INFINITY) ? 0.f : m;
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const float e = fast_exp2(s[sb][t] - mu);
+        const float e = fast_exp2(s[sb][t] - shift);
         s[sb][t] = e;
         l += e;
       }
@@ -337,7 +369,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   l += __shfl_xor(l, 32, 64);
   if (half == 0) {
     float* pm = part_ml + slot * 2 * kQRows;
-    pm[ql] = m;
+    pm[ql] = m_set ? m_eff : -INFINITY;
     pm[kQRows + ql] = l;
   }
 }
