@@ -57,6 +57,43 @@ def flop_counts(w: wl.Workload, T: np.ndarray):
     }
 
 
+# Kernel sources per bench kernel name (the traffic figure is only valid for
+# the exact sources the counters were taken on).
+KERNEL_SOURCES = {
+    "gateup": ["packed_partial_prefill_amd/csrc/gemm.hip", "packed_partial_prefill_amd/csrc/common.h",
+               "packed_partial_prefill_amd/csrc/kvr_internal.h"],
+    "down": ["packed_partial_prefill_amd/csrc/gemm.hip", "packed_partial_prefill_amd/csrc/common.h",
+             "packed_partial_prefill_amd/csrc/kvr_internal.h"],
+    "attn": ["packed_partial_prefill_amd/csrc/attention.hip", "packed_partial_prefill_amd/csrc/common.h",
+             "packed_partial_prefill_amd/csrc/kvr_internal.h"],
+}
+
+
+def profiled_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE summaries under profiles/ (scaled by a plain-copy
+    calibration), or None when none matches the current kernel sources."""
+    import glob
+    import hashlib
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        for line in open(path):
+            if not line.startswith("traffic "):
+                continue
+            kv = dict(item.split("=", 1) for item in line.split()[1:])
+            if kv.get("kernel") != kernel:
+                continue
+            h = hashlib.sha256()
+            for f in kv["sources"].split(","):
+                fp = os.path.join(ROOT, f)
+                if not os.path.exists(fp):
+                    break
+                h.update(open(fp, "rb").read())
+            else:
+                if h.hexdigest() == kv["sources_sha256"]:
+                    return float(kv["bytes_per_launch"])
+    return None
+
+
 def cpu_baseline(w: wl.Workload, T: np.ndarray, min_seconds: float = 10.0,
                  max_reps: int = 12) -> dict:
     """The oracle (float64 numpy) on the same workload, on this host's cores:
@@ -177,8 +214,10 @@ def main(argv=None) -> int:
     t_dom = kms[dom_id] / klaunch[dom_id] * 1e-3
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     achieved = fc[dom] / t_dom / 1e12
+    traffic = profiled_traffic(dom)
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": None if traffic is None else round(traffic),
                 "us_per_launch": round(t_dom * 1e6, 2)}
     t_attn = per_kernel.get("attn", 0.0) * 1e-6 + per_kernel.get("attn_merge", 0.0) * 1e-6
     attn = None
