@@ -1,18 +1,18 @@
-"""Benchmark of the packed selective-recompute layer on one MI355X.
+"""Benchmark of the packed selective-recompute path on one MI355X.
 
-A step is one pass of the whole hot path over one batch: the repair-set
-build (T_tau and its runs from the block boundaries) followed by one
-repaired layer (plan, gather, RMSNorm, QKV, RoPE + K/V write-back, packed
-biased attention, O projection, RMSNorm, gate/up + SwiGLU, down).  The
-default workload is the 7B-shaped single layer at 16K context with seam
-windows (tau = 6, B = 756, 5% budget).  Inputs are seeded synthetic data,
-resident in HBM before the timed region.  The layer is idempotent (the same
-T is rewritten with the same fresh K/V each step), so steps repeat the same
-work.
-
-Prints one JSON line on stdout; progress goes to stderr.
+Default: a step is one pass of the whole hot path over one batch — the
+repair-set build (T_tau and its runs from the block boundaries) followed by
+one repaired layer (plan, gather, RMSNorm, QKV, RoPE + K/V write-back, packed
+biased attention, O projection, RMSNorm, gate/up + SwiGLU, down) — on the
+7B-shaped single layer at 16K context with seam windows (tau = 6, B = 756,
+5% budget).  Inputs are seeded synthetic data, resident in HBM before the
+timed region.  The layer is idempotent (the same T is rewritten with the same
+fresh K/V each step), so steps repeat the same work.  Prints one JSON line on
+stdout; progress goes to stderr.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py --schedule interval --workload NAME   # sequential maximal-interval replay
+    python bench.py --table18                              # packed vs interval-wise sweep
 """
 from __future__ import annotations
 
@@ -32,6 +32,7 @@ import workloads as wl  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP32_TFLOPS = 157.3
+METRIC = "repaired tokens/sec per layer @5% budget, 16K ctx; attn HBM GB/s vs peak"
 
 
 def log(msg: str) -> None:
@@ -57,22 +58,11 @@ def flop_counts(w: wl.Workload, T: np.ndarray):
     }
 
 
-# Kernel sources per bench kernel name (the traffic figure is only valid for
-# the exact sources the counters were taken on).
-KERNEL_SOURCES = {
-    "gateup": ["packed_partial_prefill_amd/csrc/gemm.hip", "packed_partial_prefill_amd/csrc/common.h",
-               "packed_partial_prefill_amd/csrc/kvr_internal.h"],
-    "down": ["packed_partial_prefill_amd/csrc/gemm.hip", "packed_partial_prefill_amd/csrc/common.h",
-             "packed_partial_prefill_amd/csrc/kvr_internal.h"],
-    "attn": ["packed_partial_prefill_amd/csrc/attention.hip", "packed_partial_prefill_amd/csrc/common.h",
-             "packed_partial_prefill_amd/csrc/kvr_internal.h"],
-}
-
-
 def profiled_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3
     FETCH_SIZE / WRITE_SIZE summaries under profiles/ (scaled by a plain-copy
-    calibration), or None when none matches the current kernel sources."""
+    calibration), or None when none matches the current kernel sources (each
+    summary records the SHA-256 of the sources its counters were taken on)."""
     import glob
     import hashlib
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
@@ -94,30 +84,143 @@ def profiled_traffic(kernel: str):
     return None
 
 
-def cpu_baseline(w: wl.Workload, T: np.ndarray, min_seconds: float = 10.0,
-                 max_reps: int = 12) -> dict:
+def cpu_baseline(w: wl.Workload, T: np.ndarray, min_seconds: float = 10.0, max_reps: int = 12,
+                 max_rows: int = 1024) -> dict:
     """The oracle (float64 numpy) on the same workload, on this host's cores:
-    full repaired layers over all B rows, repeated until about min_seconds of
-    CPU work; the median repetition gives the rate."""
+    one repaired layer (layer 0 of a stack) over the support's first
+    min(B, max_rows) rows — exact for those rows, since a repair's first rows
+    depend only on keys at or before their positions — repeated until about
+    min_seconds of CPU work; the median repetition gives repaired tokens/s
+    per layer."""
     import oracle
     from threadpoolctl import threadpool_info
+    rows = T[:max_rows].astype(np.int64)
+    n = int(rows[-1]) + 1
     wnp = wl.layer_weights(w, 0)
     K0, V0 = wl.kv_cache(w, 0)
     X = wl.hidden_states(w)
     times = []
     t_start = time.perf_counter()
     while len(times) < max_reps and (time.perf_counter() - t_start) < min_seconds:
-        K, V = K0.astype(np.float64), V0.astype(np.float64)
-        f = wl.initial_flags(w)
+        K, V = K0[:n].astype(np.float64), V0[:n].astype(np.float64)
+        f = wl.initial_flags(w)[:n].copy()
         t0 = time.perf_counter()
-        oracle.stack_repair(w, [(wnp, K, V)], f, T.astype(np.int64), X)
+        oracle.stack_repair(w, [(wnp, K, V)], f, rows, X)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": round(len(T) / dt, 3), "unit": "tokens/s", "cores": int(threads),
+    what = "all" if len(rows) == len(T) else f"the first {len(rows)} of"
+    return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"{len(times)} full layer repairs of {w.name} (all B={len(T)} rows each), "
+            "sample": f"{len(times)} one-layer repairs of {w.name} over {what} B={len(T)} rows, "
                       f"float64 numpy oracle, median {dt:.2f} s, {sum(times):.1f} s total"}
+
+
+class Setup:
+    """Device inputs of one workload (weights and caches of every layer)."""
+
+    def __init__(self, w: wl.Workload, dws=None):
+        import torch
+        import oracle
+        import packed_partial_prefill_amd as kvr
+        from tests.gpu_harness import cfg_of, dev_cache, dev_weights, workspace
+        self.w, self.kvr, self.torch = w, kvr, torch
+        self.L = w.n_layers
+        s, e = wl.blocks(w)
+        self.ds, self.de = torch.from_numpy(s).cuda(), torch.from_numpy(e).cuda()
+        cap = w.n_tokens
+        self.dT_all = torch.empty(cap, dtype=torch.int32, device="cuda")
+        self.rs, self.rl = torch.empty_like(self.dT_all), torch.empty_like(self.dT_all)
+        self.counts = torch.empty(4, dtype=torch.int32, device="cuda")
+        self.flags = torch.from_numpy(wl.initial_flags(w)).cuda()
+        self.seams = w.support == "seams"
+        if self.seams:
+            n, _, _ = kvr.kvr_build_repair_set(self.ds, self.de, w.n_tokens, w.tau,
+                                               kvr.KVR_SEAM_ASYMMETRIC, self.dT_all, self.rs,
+                                               self.rl, self.counts)
+            self.dT = self.dT_all[:n]
+        else:
+            self.dT = torch.from_numpy(wl.explicit_support(w)).cuda()
+        self.T = self.dT.cpu().numpy()
+        self.B = len(self.T)
+        starts, lens = oracle.runs(self.T)   # host copy of the runs, for the interval schedule
+        self.runs = [(int(a), int(b)) for a, b in zip(starts, lens)]
+        self.R = len(self.runs)
+        if dws is None:
+            dws = []
+            for li in range(self.L):
+                wnp = wl.layer_weights(w, li)
+                dws.append(dev_weights(w, wnp))
+                del wnp
+        self.dws = dws
+        self.caches = []
+        for li in range(self.L):
+            K0, V0 = wl.kv_cache(w, li)
+            self.caches.append(dev_cache(w, K0, V0))
+            del K0, V0
+        self.X = torch.from_numpy(wl.hidden_states(w)).cuda()
+        self.x_out = torch.empty((self.B, w.hidden), dtype=torch.float32, device="cuda")
+        self.cfg = cfg_of(w)
+        self.ws = workspace(self.cfg, self.B, w.n_tokens)
+        self.stream = torch.cuda.current_stream()
+        # interval-wise replay: one support tensor and output per run
+        self.run_T = [torch.arange(a, a + ln, dtype=torch.int32, device="cuda")
+                      for a, ln in self.runs]
+        self.run_out = [torch.empty((ln, w.hidden), dtype=torch.float32, device="cuda")
+                        for _, ln in self.runs]
+        self.run_ws = workspace(self.cfg, max(ln for _, ln in self.runs), w.n_tokens)
+
+    def repair(self, dT, x_out, ws):
+        kvr = self.kvr
+        if self.L == 1:
+            kvr.kvr_layer_repair(self.cfg, self.dws[0], self.caches[0][0], self.caches[0][1],
+                                 self.flags, dT, self.X, x_out, ws, stream=self.stream)
+        else:
+            kvr.kvr_stack_repair(self.cfg, self.dws, self.caches, self.flags, dT, self.X, x_out,
+                                 ws, stream=self.stream)
+
+    def step_packed(self):
+        if self.seams:
+            self.kvr.kvr_build_repair_set(self.ds, self.de, self.w.n_tokens, self.w.tau,
+                                          self.kvr.KVR_SEAM_ASYMMETRIC, self.dT_all, self.rs,
+                                          self.rl, self.counts, sync=False, stream=self.stream)
+        self.repair(self.dT, self.x_out, self.ws)
+
+    def step_interval(self):
+        """Sequential maximal-interval replay (Budgeted KV-Cache Repair,
+        section 7.1): one full traversal of the layers per run, in order."""
+        for dT, out in zip(self.run_T, self.run_out):
+            self.repair(dT, out, self.run_ws)
+
+    def time_steps(self, step, steps: int, warmup: int) -> float:
+        torch = self.torch
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def run_table18(a) -> int:
+    """Packed vs interval-wise refresh at the Table 18 geometry (Qwen3-8B
+    shape, 36 layers, B = 64, R = 1/4/16, N = 2K/8K, M(U) matched)."""
+    dws = None
+    for w in wl.TABLE18:
+        log(f"[table18] {w.name}")
+        st = Setup(w, dws)
+        dws = st.dws
+        t_packed = st.time_steps(st.step_packed, a.steps, a.warmup)
+        t_interval = st.time_steps(st.step_interval, a.steps, a.warmup)
+        print(json.dumps({"workload": w.name, "N": w.n_tokens, "B": st.B, "R": st.R,
+                          "layers": st.L, "pairs_per_head": int(np.sum(st.T.astype(np.int64) + 1)),
+                          "packed_ms": round(t_packed, 4), "interval_ms": round(t_interval, 4),
+                          "interval_over_packed": round(t_interval / t_packed, 3),
+                          "unit": "ms per full refresh"}), flush=True)
+        del st
+    return 0
 
 
 def main(argv=None) -> int:
@@ -126,6 +229,8 @@ def main(argv=None) -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=wl.QWEN7_LAYER_SEAMS.name, choices=sorted(wl.WORKLOADS))
+    ap.add_argument("--schedule", default="packed", choices=("packed", "interval"))
+    ap.add_argument("--table18", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
@@ -137,50 +242,18 @@ def main(argv=None) -> int:
         return 2
 
     import torch
-    import packed_partial_prefill_amd as kvr
-    from tests.gpu_harness import build_seams_gpu, cfg_of, dev_cache, dev_weights, workspace
+    torch.cuda.set_device(0)
+    if a.table18:
+        return run_table18(a)
 
     w = wl.WORKLOADS[a.workload]
-    assert w.n_layers == 1, "bench workloads are single layers"
-    torch.cuda.set_device(0)
     log(f"[bench] workload {w.name}: generating inputs")
-    s, e = wl.blocks(w)
-    ds, de = torch.from_numpy(s).cuda(), torch.from_numpy(e).cuda()
-    cap = w.n_tokens
-    dT_all = torch.empty(cap, dtype=torch.int32, device="cuda")
-    rs, rl = torch.empty_like(dT_all), torch.empty_like(dT_all)
-    counts = torch.empty(4, dtype=torch.int32, device="cuda")
-    flags = torch.from_numpy(wl.initial_flags(w)).cuda()
-    seams = w.support == "seams"
-    if seams:
-        n, R, _ = kvr.kvr_build_repair_set(ds, de, w.n_tokens, w.tau, kvr.KVR_SEAM_ASYMMETRIC,
-                                           dT_all, rs, rl, counts)
-        dT = dT_all[:n]
-    else:
-        T_np = wl.explicit_support(w)
-        dT = torch.from_numpy(T_np).cuda()
-        R = 1
-    T = dT.cpu().numpy()
-    B = len(T)
-    wnp = wl.layer_weights(w, 0)
-    dw = dev_weights(w, wnp)
-    del wnp
-    K0, V0 = wl.kv_cache(w, 0)
-    kc, vc = dev_cache(w, K0, V0)
-    del K0, V0
-    X = torch.from_numpy(wl.hidden_states(w)).cuda()
-    x_out = torch.empty((B, w.hidden), dtype=torch.float32, device="cuda")
-    cfg = cfg_of(w)
-    ws = workspace(cfg, B, w.n_tokens)
-    stream = torch.cuda.current_stream()
+    st = Setup(w)
+    kvr = st.kvr
+    B, L, T = st.B, st.L, st.T
+    step = st.step_packed if a.schedule == "packed" else st.step_interval
 
-    def step():
-        if seams:
-            kvr.kvr_build_repair_set(ds, de, w.n_tokens, w.tau, kvr.KVR_SEAM_ASYMMETRIC, dT_all,
-                                     rs, rl, counts, sync=False, stream=stream)
-        kvr.kvr_layer_repair(cfg, dw, kc, vc, flags, dT, X, x_out, ws, stream=stream)
-
-    log(f"[bench] B={B} R={R}: warmup {a.warmup}")
+    log(f"[bench] B={B} R={st.R} layers={L} schedule={a.schedule}: warmup {a.warmup}")
     for _ in range(a.warmup):
         step()
     torch.cuda.synchronize()
@@ -209,19 +282,21 @@ def main(argv=None) -> int:
     t1 = time.perf_counter()
     kms, klaunch = kvr.kvr_timing_end()
     ms_per_step = (t1 - t0) * 1e3 / a.steps
-    value = B / (ms_per_step * 1e-3)
+    value = B * L / (ms_per_step * 1e-3)      # repaired token-layers per second
 
     t_dom = kms[dom_id] / klaunch[dom_id] * 1e-3
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    achieved = fc[dom] / t_dom / 1e12
-    traffic = profiled_traffic(dom)
+    per_layer_dom = kms[dom_id] * 1e-3 / (a.steps * L)   # seconds of the dominant kernel per layer
+    achieved = fc[dom] / per_layer_dom / 1e12
+    traffic = profiled_traffic(dom) if (a.schedule == "packed" and
+                                        w.name == wl.QWEN7_LAYER_SEAMS.name) else None
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": None if traffic is None else round(traffic),
                 "us_per_launch": round(t_dom * 1e6, 2)}
-    t_attn = per_kernel.get("attn", 0.0) * 1e-6 + per_kernel.get("attn_merge", 0.0) * 1e-6
+    t_attn = (per_kernel.get("attn", 0.0) + per_kernel.get("attn_merge", 0.0)) * 1e-6
     attn = None
-    if t_attn > 0:
+    if t_attn > 0 and a.schedule == "packed":
         gbs = (fc["attn_kv_bytes"] + fc["attn_q_o_bytes"]) / t_attn / 1e9
         tf = fc["attn"] / t_attn / 1e12
         attn = {"hbm_gbps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -246,19 +321,22 @@ def main(argv=None) -> int:
         cpu = cpu_baseline(w, T)
 
     out = {
-        "metric": "repaired tokens/sec per layer @5% budget, 16K ctx; attn HBM GB/s vs peak",
+        "metric": METRIC,
         "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
         "config": {"workload": w.name, "hidden": w.hidden, "n_q_heads": w.n_q_heads,
                    "n_kv_heads": w.n_kv_heads, "head_dim": w.head_dim,
-                   "intermediate": w.intermediate, "n_tokens": w.n_tokens, "B": B, "R": int(R),
-                   "layers": 1},
+                   "intermediate": w.intermediate, "n_tokens": w.n_tokens, "B": B, "R": st.R,
+                   "layers": L, "schedule": a.schedule},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "attn": attn,
         "gemm_mfma_frac": round(gemm_tf / peak, 4),
         "kernel_us": per_kernel,
+        "stack_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "gemm_us_per_layer": round(gemm_t * 1e6, 1),
+        "attn_us_per_layer": round(t_attn * 1e6, 1),
     }
     print(json.dumps(out), flush=True)
     return 0

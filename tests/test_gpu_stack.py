@@ -149,3 +149,40 @@ def test_qwen15_stack28_16k_degenerate():
     for li in (0, 13, w.n_layers - 1):
         assert_close(w, cpu(dcs[li][0]), cpu(fresh[li][0]), f"layer {li} K, all rows")
         assert_close(w, cpu(dcs[li][1]), cpu(fresh[li][1]), f"layer {li} V, all rows")
+
+
+def test_interval_wise_replay_equals_packed():
+    """Sequential maximal-interval replay (Budgeted KV-Cache Repair, section
+    7.1), one kvr_stack_repair call per run, equals the packed layer-major
+    call (section 13.2 argues they agree in real arithmetic) and the oracle's
+    interval-major replay."""
+    w = wl.Workload("small-stack-intervals", 103, hidden=256, n_q_heads=8, n_kv_heads=2,
+                    head_dim=64, intermediate=512, n_layers=3, n_tokens=768, block_size=128,
+                    dtype="bf16", alpha=-1.0, beta=-2.0, tau=5)
+    log(f"[stack] {w.name}: packed vs interval-wise")
+    m = kvr()
+    dT, (starts, lens), h, flags, _ = build_seams_gpu(w)
+    T = dT.cpu().numpy().astype(np.int64)
+    X = wl.hidden_states(w)
+    dX = torch.from_numpy(X).cuda()
+    cfg = cfg_of(w)
+    dws, dcs, host = _upload_layers(w)
+    caches_b = [(k.clone(), v.clone()) for k, v in dcs]
+    flags_b = flags.clone()
+    x_p = torch.empty((len(T), w.hidden), dtype=torch.float32, device="cuda")
+    m.kvr_stack_repair(cfg, dws, dcs, flags, dT, dX, x_p, workspace(cfg, len(T), w.n_tokens))
+    outs = []
+    for a, ln in zip(starts, lens):
+        Tr = torch.arange(int(a), int(a) + int(ln), dtype=torch.int32, device="cuda")
+        o = torch.empty((int(ln), w.hidden), dtype=torch.float32, device="cuda")
+        m.kvr_stack_repair(cfg, dws, caches_b, flags_b, Tr, dX, o, workspace(cfg, int(ln), w.n_tokens))
+        outs.append(o)
+    x_i = torch.cat(outs)
+    torch.cuda.synchronize()
+    assert len(starts) == 6
+    yi = oracle.interval_major(cfg, host, wl.initial_flags(w), T, X)
+    assert_close(w, cpu(x_i), yi, "interval-wise vs oracle interval-major")
+    assert_close(w, cpu(x_p), cpu(x_i), "packed vs interval-wise")
+    assert torch.equal(flags, flags_b)
+    for li in range(w.n_layers):
+        assert_close(w, cpu(dcs[li][0][dT.long()]), cpu(caches_b[li][0][dT.long()]), f"layer {li} K")

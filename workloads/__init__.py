@@ -59,10 +59,11 @@ class Workload:
     alpha: float
     beta: float
     tau: int = 0                    # seam half-width (support == "seams")
-    support: str = "seams"          # seams | contiguous | matched | isolated | explicit
+    support: str = "seams"          # seams | contiguous | matched | isolated | intervals | explicit
     budget_percent: float = 0.0     # isolated supports: B = min(S, ceil(S*b/100))
     support_start: int = 0          # contiguous / matched supports: first position
-    support_len: int = 0            # contiguous / matched supports: length
+    support_len: int = 0            # contiguous / matched / intervals supports: length B
+    n_intervals: int = 1            # intervals supports: number of equal runs R
     rms_eps: float = 1e-6
     rope_theta: float = 1e6
     qkv_bias: bool = False
@@ -119,9 +120,25 @@ QWEN15_STACK_DEGENERATE = Workload("qwen2.5-1.5b-stack28-16k-degenerate", 5, hid
                                    block_size=256, dtype="bf16", alpha=0.0, beta=0.0,
                                    tau=128)
 
+# Qwen3-8B-shaped stacks at the execution-benchmark geometry of Budgeted
+# KV-Cache Repair, section 13.3 (Table 18): 36 layers, B = 64 selected
+# positions in R = 1, 4 or 16 equal intervals, N = 2048 or 8192.  The
+# intervals are centred at (k + 1/2) N / R, so the mean selected position is
+# (N - 1) / 2 and sum(u + 1) is the same for every R at one N (65,568 at 2K,
+# 262,176 at 8K, as the section states).  Q/K normalisation of that model is
+# not part of this path's operator set; the shape is used for timing.
+def _qwen3_8b(n_tokens: int, n_intervals: int) -> Workload:
+    return Workload(f"qwen3-8b-stack36-{n_tokens // 1024}k-b64-r{n_intervals}", 6, hidden=4096,
+                    n_q_heads=32, n_kv_heads=8, head_dim=128, intermediate=12288, n_layers=36,
+                    n_tokens=n_tokens, block_size=n_tokens, dtype="bf16", alpha=-1.0, beta=-2.0,
+                    support="intervals", support_len=64, n_intervals=n_intervals)
+
+
+TABLE18 = [_qwen3_8b(n, r) for n in (2048, 8192) for r in (1, 4, 16)]
+
 WORKLOADS = {w.name: w for w in (TINY, QWEN15_LAYER, QWEN7_LAYER_SEAMS, QWEN7_LAYER_CONTIG,
                                  QWEN7_LAYER_MATCHED, QWEN7_STACK_ISOLATED,
-                                 QWEN15_STACK_DEGENERATE)}
+                                 QWEN15_STACK_DEGENERATE, *TABLE18)}
 
 
 # ----------------------------------------------------------------------------
@@ -294,7 +311,21 @@ def explicit_support(w: Workload) -> Optional[np.ndarray]:
         return np.arange(w.support_start, w.support_start + w.support_len, dtype=np.int32)
     if w.support == "isolated":
         return isolated_support(w)
+    if w.support == "intervals":
+        return interval_support(w.n_tokens, w.support_len, w.n_intervals)
     raise ValueError(w.support)
+
+
+def interval_support(n_tokens: int, B: int, R: int) -> np.ndarray:
+    """R equal runs of B/R positions centred at (k + 1/2) * N / R."""
+    ln = B // R
+    if ln * R != B or (n_tokens // R) < ln:
+        raise ValueError("B must split into R runs that fit their N/R slots")
+    out = []
+    for k in range(R):
+        c = (2 * k + 1) * n_tokens // (2 * R)
+        out.extend(range(c - ln // 2, c - ln // 2 + ln))
+    return np.array(out, dtype=np.int32)
 
 
 def random_partition(rng: np.random.Generator, n_tokens: int, m: int) -> Tuple[np.ndarray, np.ndarray]:
