@@ -101,7 +101,7 @@ size_t esize(kvr_dtype dt) { return dt == KVR_BF16 ? 2 : 4; }
 // Workspace layout; offsets are 256-byte aligned from an aligned base.
 struct Layout {
   size_t tab, n_full, n_total, nbuf, part, q, o, mlp, attn, total;
-  int split_qkv, split_o, split_down;
+  kvr::GemmPlan g_qkv, g_o, g_gateup, g_down;
 };
 
 size_t up256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -110,12 +110,15 @@ Layout layout_for(const kvr_config* c, const kvr::Shape& sh, int B, int n_tokens
   Layout L{};
   const size_t es = esize(c->dtype);
   const int nt = kvr::plan_tiles(B, sh.group);
-  L.split_qkv = kvr::gemm_splits_for(c->dtype, B, sh.qkv_cols(), sh.hidden);
-  L.split_o = kvr::gemm_splits_for(c->dtype, B, sh.hidden, sh.hq * sh.d);
-  L.split_down = kvr::gemm_splits_for(c->dtype, B, sh.hidden, sh.inter);
-  size_t part_floats = static_cast<size_t>(L.split_qkv) * B * sh.qkv_cols();
-  part_floats = std::max(part_floats, static_cast<size_t>(L.split_o) * B * sh.hidden);
-  part_floats = std::max(part_floats, static_cast<size_t>(L.split_down) * B * sh.hidden);
+  L.g_qkv = kvr::gemm_plan_for(c->dtype, B, sh.qkv_cols(), sh.hidden, false);
+  L.g_o = kvr::gemm_plan_for(c->dtype, B, sh.hidden, sh.hq * sh.d, false);
+  L.g_gateup = kvr::gemm_plan_for(c->dtype, B, sh.inter, sh.hidden, true);
+  L.g_down = kvr::gemm_plan_for(c->dtype, B, sh.hidden, sh.inter, false);
+  size_t part_floats = static_cast<size_t>(L.g_qkv.splits) * B * sh.qkv_cols();
+  part_floats = std::max(part_floats, static_cast<size_t>(L.g_o.splits) * B * sh.hidden);
+  part_floats = std::max(part_floats, static_cast<size_t>(L.g_down.splits) * B * sh.hidden);
+  if (!L.g_gateup.fused)
+    part_floats = std::max(part_floats, static_cast<size_t>(L.g_gateup.splits) * B * 2 * sh.inter);
   size_t off = 0;
   L.tab = off;     off = up256(off + static_cast<size_t>(B) * (sh.d / 2) * sizeof(float2));
   L.n_full = off;  off = up256(off + static_cast<size_t>(nt) * 4);
@@ -202,9 +205,9 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
     kvr::WeightSegs qkv{{W.wq, W.wk, W.wv},
                         {0, sh.hq * sh.d, (sh.hq + sh.hkv) * sh.d, qkv_n}, 3};
     KVR_RUN(KVR_KERNEL_QKV, stream, "qkv gemm",
-            kvr::launch_gemm_partial(dt, nbuf, qkv, B, qkv_n, sh.hidden, L.split_qkv, part, stream));
+            kvr::launch_gemm_partial(dt, nbuf, qkv, B, qkv_n, sh.hidden, L.g_qkv, part, stream));
     KVR_RUN(KVR_KERNEL_ROPE, stream, "rope+writeback",
-            kvr::launch_rope_writeback(dt, part, L.split_qkv, static_cast<size_t>(B) * qkv_n,
+            kvr::launch_rope_writeback(dt, part, L.g_qkv.splits, static_cast<size_t>(B) * qkv_n,
                                        static_cast<const float*>(W.bq),
                                        static_cast<const float*>(W.bk),
                                        static_cast<const float*>(W.bv), tab, d_T, B, sh,
@@ -218,24 +221,24 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
               kvr::launch_attention_merge(dt, B, N, sh, n_total, attn_ws, obuf, stream));
     kvr::WeightSegs wo{{W.wo, nullptr, nullptr}, {0, sh.hidden, sh.hidden, sh.hidden}, 1};
     KVR_RUN(KVR_KERNEL_OPROJ, stream, "o gemm",
-            kvr::launch_gemm_partial(dt, obuf, wo, B, sh.hidden, sh.hq * sh.d, L.split_o, part,
+            kvr::launch_gemm_partial(dt, obuf, wo, B, sh.hidden, sh.hq * sh.d, L.g_o, part,
                                      stream));
     KVR_RUN(KVR_KERNEL_NORM, stream, "residual+norm",
-            kvr::launch_residual_norm(dt, x_out, part, L.split_o,
+            kvr::launch_residual_norm(dt, x_out, part, L.g_o.splits,
                                       static_cast<size_t>(B) * sh.hidden,
                                       static_cast<const float*>(W.mlp_norm), cfg->rms_eps, nbuf,
                                       B, sh.hidden, stream));
     KVR_RUN(KVR_KERNEL_GATEUP, stream, "gate/up gemm",
-            kvr::launch_gemm_swiglu(dt, nbuf, W.w_gate, W.w_up, B, sh.inter, sh.hidden, mlp,
-                                    stream));
+            kvr::launch_gemm_swiglu(dt, nbuf, W.w_gate, W.w_up, B, sh.inter, sh.hidden, L.g_gateup,
+                                    part, mlp, stream));
     kvr::WeightSegs wd{{W.w_down, nullptr, nullptr}, {0, sh.hidden, sh.hidden, sh.hidden}, 1};
     KVR_RUN(KVR_KERNEL_DOWN, stream, "down gemm",
-            kvr::launch_gemm_partial(dt, mlp, wd, B, sh.hidden, sh.inter, L.split_down, part,
+            kvr::launch_gemm_partial(dt, mlp, wd, B, sh.hidden, sh.inter, L.g_down, part,
                                      stream));
     const bool last = (l + 1 == n_layers);
     KVR_RUN(last ? KVR_KERNEL_FINAL : KVR_KERNEL_NORM, stream, "residual+norm",
             kvr::launch_residual_norm(
-                dt, x_out, part, L.split_down, static_cast<size_t>(B) * sh.hidden,
+                dt, x_out, part, L.g_down.splits, static_cast<size_t>(B) * sh.hidden,
                 last ? nullptr : static_cast<const float*>(w[l + 1].attn_norm), cfg->rms_eps,
                 nbuf, B, sh.hidden, stream));
   }

@@ -414,9 +414,16 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
   *reinterpret_cast<u32x4_t*>(o + (static_cast<size_t>(r) * Hq + h) * D + d0) = outv;
 }
 
-int attn_split_tiles(int n_tokens) {
-  (void)n_tokens;
-  return 32;
+// KV tiles per split: 32 (2048 keys) when the launch has plenty of
+// workgroups; halved (down to 4) while the grid has fewer than 1024, so that
+// small packed sets (few query tiles) still spread over every CU.  Roughly
+// half of a causal grid exits at once (splits past a tile's last key).
+int attn_split_tiles(int B, int n_tokens, const Shape& sh) {
+  const long qk = static_cast<long>(plan_tiles(B, sh.group)) * sh.hkv;
+  const int kv_tiles = (n_tokens + kKvTile - 1) / kKvTile;
+  int st = 32;
+  while (st > 4 && qk * ((kv_tiles + st - 1) / st) < 1024) st /= 2;
+  return st;
 }
 
 }  // namespace
@@ -424,7 +431,7 @@ int attn_split_tiles(int n_tokens) {
 size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh) {
   if (dt != KVR_BF16) return 0;
   const int nt = plan_tiles(B, sh.group);
-  const int st = attn_split_tiles(n_tokens);
+  const int st = attn_split_tiles(B, n_tokens, sh);
   const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
   return static_cast<size_t>(nt) * sh.hkv * ns * (sh.d + 2) * kQRows * sizeof(float);
 }
@@ -444,7 +451,7 @@ hipError_t launch_mfma(const void* q, const void* k_cache, const void* v_cache,
     attr = true;
   }
   const int nt = plan_tiles(B, sh.group);
-  const int st = attn_split_tiles(n_tokens);
+  const int st = attn_split_tiles(B, n_tokens, sh);
   const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
   const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
   float* part_o = static_cast<float*>(ws);
@@ -463,7 +470,7 @@ template <int D>
 hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_total, void* ws,
                         void* o_out, hipStream_t stream) {
   const int nt = plan_tiles(B, sh.group);
-  const int st = attn_split_tiles(n_tokens);
+  const int st = attn_split_tiles(B, n_tokens, sh);
   const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
   const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
   const float* part_o = static_cast<const float*>(ws);

@@ -4,6 +4,8 @@
 //
 // bf16 storage runs on the MFMA kernel below; float32 storage runs on an
 // LDS-tiled float32 FMA kernel (no reduced-precision matrix modes).
+#include <cmath>
+
 #include "common.h"
 #include "kvr_internal.h"
 
@@ -100,22 +102,28 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fma(const T* __restrict__ A, 
 // ---------------------------------------------------------------------------
 // bf16 MFMA kernel (gfx950 v_mfma_f32_32x32x16_bf16), float32 accumulation.
 //
-// Workgroup tile 256 (M) x 256 (N), 8 waves; wave w owns rows (w/2)*64 .. +64
-// and a 128-column slice (2 x 4 blocks of 32x32).  K advances 32 at a time
-// through four LDS stages that are filled straight from global memory by
-// global_load_lds_dwordx4 (no register staging), three stages ahead of the
+// A workgroup computes a BM (rows of A) x BN (rows of W) tile with WM x WN
+// waves; each wave owns TM x TN blocks of 32 x 32.  K advances 32 at a time
+// through NS LDS stages that are filled straight from global memory by
+// global_load_lds_dwordx4 (no register staging), NS - 1 stages ahead of the
 // MFMAs; the barrier that recycles a stage sits in the middle of each step,
 // after the first half of its MFMAs is issued, so the matrix core stays busy
-// while the waves synchronise.  Each stage holds a 256 x 32 tile of A and of W as 64-byte rows of
-// four 16-byte chunks; chunk c of row r sits at c ^ (((r >> 1) ^ (r >> 3)) & 3),
-// so any 8 consecutive rows read by an MFMA operand load fall in distinct
-// 16-byte slots of 128 bytes and any 16 in distinct slots of 256 bytes (no
-// bank conflicts whether the LDS serves 8 or 16 lanes per pass).
-// The stage buffers are separate LDS objects picked at compile time, which
-// lets the compiler keep the three newer stages in flight while a stage is
-// consumed.  MFMA operand layout (32x32x16): lane l supplies row/column l%32
-// and k = 8*(l/32) .. +7 of the 16-wide K slice; accumulator t of lane l is
-// D[8*(t/4) + 4*(l/32) + t%4][l%32].
+// while the waves synchronise.  A stage holds the tile's BM x 32 slice of A
+// and BN x 32 slice of W as 64-byte rows of four 16-byte chunks; chunk c of
+// row r sits at c ^ (((r >> 1) ^ (r >> 3)) & 3), so any 8 consecutive rows
+// read by an MFMA operand load fall in distinct 16-byte slots of 128 bytes
+// and any 16 in distinct slots of 256 bytes (no bank conflicts whether the
+// LDS serves 8 or 16 lanes per pass).  The stage buffers are separate LDS
+// objects picked at compile time, which lets the compiler keep the newer
+// stages in flight while one is consumed.  MFMA operand layout (32x32x16):
+// lane l supplies row/column l%32 and k = 8*(l/32) .. +7 of the 16-wide K
+// slice; accumulator t of lane l is D[8*(t/4) + 4*(l/32) + t%4][l%32].
+//
+// Tile shapes: 256 x 256 (8 waves) for large M; 128 x 128 (4 waves, two
+// workgroups per CU) and 64 x 128 (2 waves, three per CU, deeper pipeline)
+// when M is small and the weights, not the matrix core, set the pace: there
+// a launch needs many workgroups, each with several stages of weights in
+// flight, to keep HBM busy.
 //
 // Workgroups are numbered along M fastest, then N panel, then K split, and
 // block b is mapped so that each XCD (b % 8) takes one contiguous run of that
@@ -125,27 +133,37 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fma(const T* __restrict__ A, 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
-constexpr int MB = 256, NB = 256, KB = 32, kStages = 4;
-constexpr int kTileBytes = MB * KB * 2;   // 16 KB: one 256 x 32 bf16 tile
+constexpr int KB = 32;
 constexpr int kXcds = 8;
 
-__shared__ __attribute__((aligned(16))) uint8_t g_a0[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_a1[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_a2[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_a3[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_w0[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_w1[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_w2[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t g_w3[kTileBytes];
+template <int BM_, int BN_, int WM_, int WN_, int NS_, int OCC_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, NS = NS_;
+  static constexpr int occupancy = OCC_;               // workgroups per CU it is sized for
+  static constexpr int TM = BM / (32 * WM), TN = BN / (32 * WN);
+  static constexpr int waves = WM * WN, threads = 64 * waves;
+  static constexpr int waves_per_simd = (OCC_ * waves + 3) / 4;
+  static constexpr int LA = BM / 16 / waves;           // 1 KB DMA slices per wave per stage (A)
+  static constexpr int LW = BN / 16 / waves;           // ... (W)
+  static constexpr int LS = LA + LW;
+  static constexpr int ABytes = BM * KB * 2, WBytes = BN * KB * 2;
+  static_assert(TM * 32 * WM == BM && TN * 32 * WN == BN, "wave blocks tile the workgroup");
+  static_assert(LA * 16 * waves == BM && LW * 16 * waves == BN, "whole DMA slices per wave");
+  static_assert(TN % 2 == 0, "gate and up blocks pair up in the fused SwiGLU epilogue");
+  static_assert(NS >= 3 && NS <= 6 && (NS - 2) * LS < 64, "pipeline depth and vmcnt range");
+  static_assert(NS * (ABytes + WBytes) * OCC_ <= 160 * 1024, "LDS per CU");
+};
 
-template <int S> __device__ __forceinline__ uint8_t* a_stage() {
-  if constexpr (S == 0) return g_a0; else if constexpr (S == 1) return g_a1;
-  else if constexpr (S == 2) return g_a2; else return g_a3;
-}
-template <int S> __device__ __forceinline__ uint8_t* w_stage() {
-  if constexpr (S == 0) return g_w0; else if constexpr (S == 1) return g_w1;
-  else if constexpr (S == 2) return g_w2; else return g_w3;
-}
+// The tile shapes the library launches.
+using TileL = Tile<256, 256, 4, 2, 4, 1>;
+using TileM = Tile<128, 128, 2, 2, 4, 2>;
+using TileS = Tile<64, 128, 1, 2, 6, 2>;
+
+template <class C>
+struct Stages {
+  uint8_t* a[C::NS];
+  uint8_t* w[C::NS];
+};
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * (KB * 2) + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
@@ -161,76 +179,105 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
 }
 
-// Wave arrangement: WM x WN waves, each owning TM x TN blocks of 32 x 32.
-template <int WM, int WN, int TM, int TN>
-struct Cfg {
-  static_assert(WM * TM * 32 == MB && WN * TN * 32 == NB, "256 x 256 workgroup tile");
-  static constexpr int waves = WM * WN;
-  static constexpr int threads = 64 * waves;
-  static constexpr int loads = (MB / 16) / waves;   // 1 KB DMA slices per wave per operand
-};
-
 template <class C>
 struct GemmThread {
-  const bf16_t* asrc[C::loads];   // this lane's global source (A), at the split's first k
-  const bf16_t* wsrc[C::loads];   // ... (W)
-  int dst[C::loads];              // wave-uniform LDS byte offset of each 1 KB slice
-  int arow[4], wrow[4];
+  const bf16_t* asrc[C::LA];   // this lane's global source (A), at the split's first k
+  const bf16_t* wsrc[C::LW];   // ... (W)
+  int adst[C::LA], wdst[C::LW];  // wave-uniform LDS byte offset of each 1 KB slice
+  int arow[C::TM], wrow[C::TN];
   int khalf;
 };
 
 template <class C, int S>
-__device__ __forceinline__ void issue_stage(const GemmThread<C>& g, int kb) {
+__device__ __forceinline__ void issue_stage(const GemmThread<C>& g, const Stages<C>& st, int kb) {
 #pragma unroll
-  for (int j = 0; j < C::loads; ++j) {
-    __builtin_amdgcn_global_load_lds(KVR_GLB(g.asrc[j] + kb), KVR_LDS(a_stage<S>() + g.dst[j]), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(KVR_GLB(g.wsrc[j] + kb), KVR_LDS(w_stage<S>() + g.dst[j]), 16, 0, 0);
-  }
+  for (int j = 0; j < C::LA; ++j)
+    __builtin_amdgcn_global_load_lds(KVR_GLB(g.asrc[j] + kb), KVR_LDS(st.a[S] + g.adst[j]), 16, 0, 0);
+#pragma unroll
+  for (int j = 0; j < C::LW; ++j)
+    __builtin_amdgcn_global_load_lds(KVR_GLB(g.wsrc[j] + kb), KVR_LDS(st.w[S] + g.wdst[j]), 16, 0, 0);
 }
 
-template <class C, int TM, int TN, int S>
-__device__ __forceinline__ void mma_half(const GemmThread<C>& g, int ks, f32x16_t (&acc)[TM][TN]) {
-  const uint8_t* a = a_stage<S>();
-  const uint8_t* w = w_stage<S>();
+template <class C, int S>
+__device__ __forceinline__ void mma_half(const GemmThread<C>& g, const Stages<C>& st, int ks,
+                                         f32x16_t (&acc)[C::TM][C::TN]) {
+  const uint8_t* a = st.a[S];
+  const uint8_t* w = st.w[S];
   const int chunk = ks * 2 + g.khalf;
-  bf16x8_t fa[TM], fw[TN];
+  bf16x8_t fa[C::TM], fw[C::TN];
 #pragma unroll
-  for (int mb = 0; mb < TM; ++mb) fa[mb] = *reinterpret_cast<const bf16x8_t*>(a + swz(g.arow[mb], chunk));
+  for (int mb = 0; mb < C::TM; ++mb) fa[mb] = *reinterpret_cast<const bf16x8_t*>(a + swz(g.arow[mb], chunk));
 #pragma unroll
-  for (int nb = 0; nb < TN; ++nb) fw[nb] = *reinterpret_cast<const bf16x8_t*>(w + swz(g.wrow[nb], chunk));
+  for (int nb = 0; nb < C::TN; ++nb) fw[nb] = *reinterpret_cast<const bf16x8_t*>(w + swz(g.wrow[nb], chunk));
 #pragma unroll
-  for (int mb = 0; mb < TM; ++mb)
+  for (int mb = 0; mb < C::TM; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < TN; ++nb)
+    for (int nb = 0; nb < C::TN; ++nb)
       acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fw[nb], acc[mb][nb], 0, 0, 0);
 }
 
 // One K step on stage S (its data was certified by the previous barrier):
 // the first 16-wide half is read and its MFMAs issued; then, with those in
-// flight, wait until the next stage's DMA has landed (one newer stage may
+// flight, wait until the next stage's DMA has landed (NS - 3 newer stages may
 // stay in flight), barrier (every wave is past the previous stage), refill
-// the previous stage's buffers with the step three ahead (clamped to the last
+// the previous stage's buffers with the step NS - 1 ahead (clamped to the last
 // step: a refill past the end is never read), and run the second half.
-template <class C, int TM, int TN, int S>
-__device__ __forceinline__ void k_step(const GemmThread<C>& g, int i, int nsteps,
-                                       f32x16_t (&acc)[TM][TN]) {
-  mma_half<C, TM, TN, S>(g, 0, acc);
-  wait_vmcnt<2 * C::loads>();
+template <class C, int S>
+__device__ __forceinline__ void k_step(const GemmThread<C>& g, const Stages<C>& st, int i,
+                                       int nsteps, f32x16_t (&acc)[C::TM][C::TN]) {
+  mma_half<C, S>(g, st, 0, acc);
+  wait_vmcnt<(C::NS - 3) * C::LS>();
   __builtin_amdgcn_s_barrier();
-  issue_stage<C, (S + 3) % kStages>(g, min(i + 3, nsteps - 1) * KB);
-  mma_half<C, TM, TN, S>(g, 1, acc);
+  issue_stage<C, (S + C::NS - 1) % C::NS>(g, st, min(i + C::NS - 1, nsteps - 1) * KB);
+  mma_half<C, S>(g, st, 1, acc);
+}
+
+// NS consecutive steps starting on stage S = 0.
+template <class C, int S>
+__device__ __forceinline__ void k_round(const GemmThread<C>& g, const Stages<C>& st, int i,
+                                        int nsteps, f32x16_t (&acc)[C::TM][C::TN]) {
+  k_step<C, S>(g, st, i + S, nsteps, acc);
+  if constexpr (S + 1 < C::NS) k_round<C, S + 1>(g, st, i, nsteps, acc);
+}
+
+// The last nsteps - i (< NS) steps.
+template <class C, int S>
+__device__ __forceinline__ void k_tail(const GemmThread<C>& g, const Stages<C>& st, int i,
+                                       int nsteps, f32x16_t (&acc)[C::TM][C::TN]) {
+  if (i + S < nsteps) {
+    k_step<C, S>(g, st, i + S, nsteps, acc);
+    if constexpr (S + 2 < C::NS) k_tail<C, S + 1>(g, st, i, nsteps, acc);
+  }
+}
+
+template <class C, int S>
+__device__ __forceinline__ void k_prologue(const GemmThread<C>& g, const Stages<C>& st, int nsteps) {
+  issue_stage<C, S>(g, st, min(S, nsteps - 1) * KB);
+  if constexpr (S + 2 < C::NS) k_prologue<C, S + 1>(g, st, nsteps);
 }
 
 // MODE 0: part[split][M][N] = A * W^T over this split's K range (W segmented).
-// MODE 1: W.w[0] = W_gate, W.w[1] = W_up; the tile holds 128 gate rows and the
-//         same 128 up rows; out[M][N] = bf16(SiLU(gate) * up), full K.  A wave's
+// MODE 1: W.w[0] = W_gate, W.w[1] = W_up; the tile holds BN/2 gate rows and the
+//         same BN/2 up rows; out[M][N] = bf16(SiLU(gate) * up), full K.  A wave's
 //         first TN/2 column blocks are gate columns, the last TN/2 the matching
 //         up columns, so both factors of an output meet in one lane.
-template <int MODE, int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_mfma(
+template <int MODE, class C>
+__global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
     const bf16_t* __restrict__ A, WeightSegs W, int M, int N, int K, int k_per_split,
     int tiles_m, int tiles_n, int splits, float* __restrict__ part, bf16_t* __restrict__ out) {
-  using C = Cfg<WM, WN, TM, TN>;
+  constexpr int TM = C::TM, TN = C::TN, BM = C::BM, BN = C::BN;
+  __shared__ __attribute__((aligned(16))) uint8_t a0[C::ABytes], a1[C::ABytes], a2[C::ABytes],
+      a3[C::ABytes], a4[C::NS > 4 ? C::ABytes : 16], a5[C::NS > 5 ? C::ABytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t w0[C::WBytes], w1[C::WBytes], w2[C::WBytes],
+      w3[C::WBytes], w4[C::NS > 4 ? C::WBytes : 16], w5[C::NS > 5 ? C::WBytes : 16];
+  Stages<C> st;
+  {
+    uint8_t* as[6] = {a0, a1, a2, a3, a4, a5};
+    uint8_t* ws[6] = {w0, w1, w2, w3, w4, w5};
+#pragma unroll
+    for (int s = 0; s < C::NS; ++s) { st.a[s] = as[s]; st.w[s] = ws[s]; }
+  }
+
   // XCD-aware order: t = ((split * tiles_n) + n) * tiles_m + m
   const int total = tiles_m * tiles_n * splits;
   const int b = blockIdx.x, xcd = b % kXcds, q = total / kXcds, rem = total % kXcds;
@@ -238,22 +285,29 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_mfma(
   const int tm = t % tiles_m, tn = (t / tiles_m) % tiles_n, split = t / (tiles_m * tiles_n);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int m0 = tm * MB;
-  const int n0 = tn * (MODE == 1 ? NB / 2 : NB);
+  const int wm = wave / C::WN, wn = wave % C::WN;
+  const int m0 = tm * BM;
+  const int n0 = tn * (MODE == 1 ? BN / 2 : BN);
   const int k0 = split * k_per_split;
   const int k1 = min(K, k0 + k_per_split);
   const int nsteps = k1 > k0 ? (k1 - k0) / KB : 0;
 
   GemmThread<C> g;
 #pragma unroll
-  for (int j = 0; j < C::loads; ++j) {
-    const int row0 = (wave * C::loads + j) * 16;
+  for (int j = 0; j < C::LA; ++j) {
+    const int row0 = (wave * C::LA + j) * 16;
     const int row = row0 + (lane >> 2);                      // tile row this lane fetches
     const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);   // logical chunk of its slot
-    g.dst[j] = row0 * (KB * 2);
+    g.adst[j] = row0 * (KB * 2);
     const int m = min(m0 + row, M - 1);
     g.asrc[j] = A + static_cast<size_t>(m) * K + k0 + chunk * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < C::LW; ++j) {
+    const int row0 = (wave * C::LW + j) * 16;
+    const int row = row0 + (lane >> 2);
+    const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+    g.wdst[j] = row0 * (KB * 2);
     const bf16_t* wr;
     if (MODE == 0) {
       const int n = min(n0 + row, N - 1);
@@ -262,8 +316,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_mfma(
       if (W.nseg > 2 && n >= W.n_begin[2]) sj = 2;
       wr = static_cast<const bf16_t*>(W.w[sj]) + static_cast<size_t>(n - W.n_begin[sj]) * K;
     } else {
-      const int n = min(n0 + (row & 127), N - 1);
-      wr = static_cast<const bf16_t*>(W.w[row >> 7]) + static_cast<size_t>(n) * K;
+      const int n = min(n0 + row % (BN / 2), N - 1);
+      wr = static_cast<const bf16_t*>(W.w[row / (BN / 2)]) + static_cast<size_t>(n) * K;
     }
     g.wsrc[j] = wr + k0 + chunk * 8;
   }
@@ -272,7 +326,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_mfma(
 #pragma unroll
   for (int nb = 0; nb < TN; ++nb) {
     if (MODE == 0) g.wrow[nb] = (wn * TN + nb) * 32 + (lane & 31);
-    else g.wrow[nb] = (nb < TN / 2 ? 0 : NB / 2) + (wn * (TN / 2) + nb % (TN / 2)) * 32 + (lane & 31);
+    else g.wrow[nb] = (nb < TN / 2 ? 0 : BN / 2) + (wn * (TN / 2) + nb % (TN / 2)) * 32 + (lane & 31);
   }
   g.khalf = lane >> 5;
 
@@ -285,21 +339,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_mfma(
       for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
 
   if (nsteps > 0) {
-    issue_stage<C, 0>(g, 0);
-    issue_stage<C, 1>(g, min(1, nsteps - 1) * KB);
-    issue_stage<C, 2>(g, min(2, nsteps - 1) * KB);
-    wait_vmcnt<4 * C::loads>();       // stage 0 landed; stages 1 and 2 may be in flight
+    k_prologue<C, 0>(g, st, nsteps);            // stages 0 .. NS-2
+    wait_vmcnt<(C::NS - 2) * C::LS>();          // stage 0 landed; the rest may be in flight
     __builtin_amdgcn_s_barrier();
     int i = 0;
-    for (; i + 4 <= nsteps; i += 4) {
-      k_step<C, TM, TN, 0>(g, i, nsteps, acc);
-      k_step<C, TM, TN, 1>(g, i + 1, nsteps, acc);
-      k_step<C, TM, TN, 2>(g, i + 2, nsteps, acc);
-      k_step<C, TM, TN, 3>(g, i + 3, nsteps, acc);
-    }
-    if (i < nsteps) k_step<C, TM, TN, 0>(g, i, nsteps, acc);
-    if (i + 1 < nsteps) k_step<C, TM, TN, 1>(g, i + 1, nsteps, acc);
-    if (i + 2 < nsteps) k_step<C, TM, TN, 2>(g, i + 2, nsteps, acc);
+    for (; i + C::NS <= nsteps; i += C::NS) k_round<C, 0>(g, st, i, nsteps, acc);
+    k_tail<C, 0>(g, st, i, nsteps, acc);
     wait_vmcnt<0>();
   }
 
@@ -332,44 +377,118 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void k_gemm_mfma(
   }
 }
 
-// Wave arrangement used by the library.
-#ifndef KVR_GEMM_WAVES_M
-#define KVR_GEMM_WAVES_M 4
-#endif
-constexpr int kWM = KVR_GEMM_WAVES_M, kWN = 2, kTM = 8 / kWM, kTN = 4;
-constexpr int MT = 64 * kWM * kWN;
+// out[m][n] = SiLU(sum_s part[s][m][n]) * sum_s part[s][m][N + n] (part rows
+// hold the gate columns, then the up columns), stored in bf16.
+constexpr int kRedThreads = 256;
+__global__ __launch_bounds__(kRedThreads) void k_swiglu_reduce(const float* __restrict__ part,
+                                                               int splits, int M, int N,
+                                                               bf16_t* __restrict__ out) {
+  const size_t n4 = static_cast<size_t>(N) >> 2;
+  const size_t idx = static_cast<size_t>(blockIdx.x) * kRedThreads + threadIdx.x;
+  if (idx >= static_cast<size_t>(M) * n4) return;
+  const size_t m = idx / n4, j = idx - m * n4;
+  const size_t stride4 = static_cast<size_t>(M) * 2 * n4;
+  const float4* g4 = reinterpret_cast<const float4*>(part) + m * 2 * n4 + j;
+  float4 g = g4[0], u = g4[n4];
+  for (int s = 1; s < splits; ++s) {
+    const float4 a = g4[s * stride4], c = g4[s * stride4 + n4];
+    g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+    u.x += c.x; u.y += c.y; u.z += c.z; u.w += c.w;
+  }
+  uint2 p;
+  p.x = static_cast<uint32_t>(f32_to_bf16(g.x / (1.f + expf(-g.x)) * u.x)) |
+        (static_cast<uint32_t>(f32_to_bf16(g.y / (1.f + expf(-g.y)) * u.y)) << 16);
+  p.y = static_cast<uint32_t>(f32_to_bf16(g.z / (1.f + expf(-g.z)) * u.z)) |
+        (static_cast<uint32_t>(f32_to_bf16(g.w / (1.f + expf(-g.w)) * u.w)) << 16);
+  reinterpret_cast<uint2*>(out)[idx] = p;
+}
+
+template <int MODE, class C>
+void launch_mfma(const bf16_t* A, const WeightSegs& W, int M, int N, int K, int splits,
+                 float* part, bf16_t* out, hipStream_t stream) {
+  const int kps = ((K / splits + KB - 1) / KB) * KB;
+  const int tm = (M + C::BM - 1) / C::BM;
+  const int tn = MODE == 1 ? (N + C::BN / 2 - 1) / (C::BN / 2) : (N + C::BN - 1) / C::BN;
+  hipLaunchKernelGGL((k_gemm_mfma<MODE, C>), dim3(tm * tn * splits), dim3(C::threads), 0, stream,
+                     A, W, M, N, K, kps, tm, tn, splits, part, out);
+}
+
+template <int MODE>
+void launch_variant(int variant, const bf16_t* A, const WeightSegs& W, int M, int N, int K,
+                    int splits, float* part, bf16_t* out, hipStream_t stream) {
+  switch (variant) {
+    case 0: launch_mfma<MODE, TileL>(A, W, M, N, K, splits, part, out, stream); break;
+    case 1: launch_mfma<MODE, TileM>(A, W, M, N, K, splits, part, out, stream); break;
+    default: launch_mfma<MODE, TileS>(A, W, M, N, K, splits, part, out, stream); break;
+  }
+}
+
+struct VariantGeom { int bm, bn, occupancy; };
+constexpr VariantGeom kGeom[3] = {{TileL::BM, TileL::BN, TileL::occupancy},
+                                  {TileM::BM, TileM::BN, TileM::occupancy},
+                                  {TileS::BM, TileS::BN, TileS::occupancy}};
 
 }  // namespace
 
-// Split-K factor for the partial-output GEMMs: the smallest split that
-// minimises the critical path (waves of 256 workgroups, one per CU, times the
-// K steps per workgroup).  float32 storage does not split.
-int gemm_splits_for(kvr_dtype dt, int M, int N, int K) {
-  if (dt != KVR_BF16) return 1;
-  const long tiles = static_cast<long>((M + MB - 1) / MB) * ((N + NB - 1) / NB);
-  int best = 1;
-  long best_cost = -1;
-  for (int s = 1; s <= 8; ++s) {
-    const long kps = ((K / s + KB - 1) / KB) * KB;
-    if (kps < 2 * KB && s > 1) break;
-    const long cost = ((tiles * s + 255) / 256) * kps;
-    if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = s; }
+// Launch plan for C[M, N] = A[M, K] W[N, K]^T.
+//
+// Large M (> 512): 256 x 256 tiles; the K split is the smallest that
+// minimises the critical path, rounds of 256 resident workgroups times K
+// steps per workgroup (the launch is MFMA-bound).
+// Small M: the launch streams weights (HBM-bound) and what matters is having
+// enough workgroups in flight: 128 x 128 tiles up to M = 512, 64 x 128 up to
+// M = 128, and the K split that divides the K steps evenly and brings the
+// launch closest to one workgroup per CU (measured on the Qwen2.5-1.5B and
+// Qwen3-8B projection shapes: fewer leave CUs idle, more add float32 partial
+// traffic and a second round).
+// swiglu: the gate/up pair (W = [Wg; Wu], 2N columns).  The SwiGLU is fused
+// into the epilogue when the unsplit launch has enough workgroups; otherwise
+// gate and up are computed as split-K partials and reduced by a row kernel.
+// float32 storage uses the FMA kernel and never splits.
+GemmPlan gemm_plan_for(kvr_dtype dt, int M, int N, int K, bool swiglu) {
+  if (dt != KVR_BF16) return GemmPlan{0, 1, swiglu};
+  const int cols = swiglu ? 2 * N : N;
+  const int ksteps = K / KB;
+  if (M > 512) {
+    if (swiglu) return GemmPlan{0, 1, true};
+    const long tiles = static_cast<long>((M + TileL::BM - 1) / TileL::BM) * ((cols + TileL::BN - 1) / TileL::BN);
+    int best = 1;
+    long best_cost = -1;
+    for (int s = 1; s <= 8; ++s) {
+      const long kps = (ksteps + s - 1) / s;
+      if (kps < 2 && s > 1) break;
+      const long cost = ((tiles * s + 255) / 256) * kps;
+      if (best_cost < 0 || cost < best_cost) { best_cost = cost; best = s; }
+    }
+    return GemmPlan{0, best, false};
   }
-  return best;
+  const int variant = M <= 128 ? 2 : 1;
+  const VariantGeom vg = kGeom[variant];
+  const long tiles_m = (M + vg.bm - 1) / vg.bm;
+  constexpr long kTarget = 256;
+  if (swiglu && tiles_m * ((N + vg.bn / 2 - 1) / (vg.bn / 2)) >= kTarget / 2)
+    return GemmPlan{variant, 1, true};
+  const long tiles = tiles_m * ((cols + vg.bn - 1) / vg.bn);
+  int best = 1;
+  double best_dist = 1e30;
+  for (int s = 1; s <= 16; ++s) {
+    if (ksteps / s < 4) break;
+    if (ksteps % s != 0) continue;
+    const double dist = std::fabs(std::log(static_cast<double>(tiles * s) / kTarget));
+    if (dist < best_dist - 1e-9) { best_dist = dist; best = s; }
+  }
+  return GemmPlan{variant, best, false};
 }
 
 hipError_t launch_gemm_partial(kvr_dtype dt, const void* A, const WeightSegs& W, int M, int N,
-                               int K, int splits, float* part, hipStream_t stream) {
+                               int K, const GemmPlan& plan, float* part, hipStream_t stream) {
   if (M == 0) return hipSuccess;
   if (dt == KVR_BF16) {
-    const int kps = ((K / splits + KB - 1) / KB) * KB;
-    const int tm = (M + MB - 1) / MB, tn = (N + NB - 1) / NB;
-    hipLaunchKernelGGL((k_gemm_mfma<0, kWM, kWN, kTM, kTN>), dim3(tm * tn * splits), dim3(MT), 0, stream,
-                       static_cast<const bf16_t*>(A), W, M, N, K, kps, tm, tn, splits, part,
-                       nullptr);
+    launch_variant<0>(plan.variant, static_cast<const bf16_t*>(A), W, M, N, K, plan.splits, part,
+                      nullptr, stream);
   } else {
-    const int kps = ((K / splits + 63) / 64) * 64;
-    dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile, splits);
+    const int kps = ((K / plan.splits + 63) / 64) * 64;
+    dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile, plan.splits);
     hipLaunchKernelGGL((k_gemm_fma<float, 0>), grid, dim3(kThreads), 0, stream,
                        static_cast<const float*>(A), W, M, N, K, kps, part, nullptr);
   }
@@ -377,15 +496,24 @@ hipError_t launch_gemm_partial(kvr_dtype dt, const void* A, const WeightSegs& W,
 }
 
 hipError_t launch_gemm_swiglu(kvr_dtype dt, const void* A, const void* Wg, const void* Wu, int M,
-                              int N, int K, void* out, hipStream_t stream) {
+                              int N, int K, const GemmPlan& plan, float* part, void* out,
+                              hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  WeightSegs W{{Wg, Wu, nullptr}, {0, N, N, N}, 2};
   if (dt == KVR_BF16) {
-    const int tm = (M + MB - 1) / MB, tn = (N + NB / 2 - 1) / (NB / 2);
-    hipLaunchKernelGGL((k_gemm_mfma<1, kWM, kWN, kTM, kTN>), dim3(tm * tn), dim3(MT), 0, stream,
-                       static_cast<const bf16_t*>(A), W, M, N, K, K, tm, tn, 1, nullptr,
-                       static_cast<bf16_t*>(out));
+    const bf16_t* a = static_cast<const bf16_t*>(A);
+    if (plan.fused) {
+      WeightSegs W{{Wg, Wu, nullptr}, {0, N, N, N}, 2};
+      launch_variant<1>(plan.variant, a, W, M, N, K, 1, nullptr, static_cast<bf16_t*>(out), stream);
+    } else {
+      WeightSegs W{{Wg, Wu, nullptr}, {0, N, 2 * N, 2 * N}, 2};
+      launch_variant<0>(plan.variant, a, W, M, 2 * N, K, plan.splits, part, nullptr, stream);
+      const size_t n = static_cast<size_t>(M) * (N / 4);
+      hipLaunchKernelGGL(k_swiglu_reduce, dim3(static_cast<unsigned>((n + kRedThreads - 1) / kRedThreads)),
+                         dim3(kRedThreads), 0, stream, part, plan.splits, M, N,
+                         static_cast<bf16_t*>(out));
+    }
   } else {
+    WeightSegs W{{Wg, Wu, nullptr}, {0, N, N, N}, 2};
     dim3 grid((N + kTile - 1) / kTile, (M + kTile - 1) / kTile, 1);
     hipLaunchKernelGGL((k_gemm_fma<float, 1>), grid, dim3(kThreads), 0, stream,
                        static_cast<const float*>(A), W, M, N, K, K, nullptr,

@@ -48,14 +48,24 @@ struct WeightSegs {
   int n_begin[4];
   int nseg;
 };
+// How one projection is launched: tile shape (variant), K split, and for the
+// gate/up pair whether SwiGLU runs in the GEMM epilogue (fused, no split) or
+// in a reduction of float32 partials.
+struct GemmPlan {
+  int variant;
+  int splits;
+  bool fused;
+};
+GemmPlan gemm_plan_for(kvr_dtype dt, int M, int N, int K, bool swiglu);
 // part[s][M][N] (float32) = A[M, K-slice s] * W[N, K-slice s]^T for
-// s < splits (K split evenly in multiples of 64).
+// s < plan.splits (K split evenly in multiples of 32).
 hipError_t launch_gemm_partial(kvr_dtype dt, const void* A, const WeightSegs& W, int M, int N,
-                               int K, int splits, float* part, hipStream_t stream);
-// out[M][N] = SiLU(A Wg^T) * (A Wu^T), stored in dtype dt.
+                               int K, const GemmPlan& plan, float* part, hipStream_t stream);
+// out[M][N] = SiLU(A Wg^T) * (A Wu^T), stored in dtype dt; part holds
+// plan.splits * M * 2N floats when the plan is not fused.
 hipError_t launch_gemm_swiglu(kvr_dtype dt, const void* A, const void* Wg, const void* Wu, int M,
-                              int N, int K, void* out, hipStream_t stream);
-int gemm_splits_for(kvr_dtype dt, int M, int N, int K);
+                              int N, int K, const GemmPlan& plan, float* part, void* out,
+                              hipStream_t stream);
 
 // ---- rope.hip -----------------------------------------------------------------
 hipError_t launch_rope_writeback(kvr_dtype dt, const float* qkv_part, int splits,

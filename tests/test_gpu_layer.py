@@ -117,3 +117,12 @@ def test_qwen7_layer_16k_contiguous():
 @pytest.mark.timeout(600)
 def test_qwen7_layer_16k_matched():
     run_layer_case(wl.QWEN7_LAYER_MATCHED, check_rows=128)
+
+
+@pytest.mark.timeout(600)
+def test_qwen3_8b_layer_b64_16_intervals():
+    """64 packed rows at the Qwen3-8B execution-benchmark geometry: exercises
+    the small-M projection path (64-row MFMA tiles, even K splits, fused
+    gate/up epilogue) against the oracle on every row."""
+    w = next(x for x in wl.TABLE18 if x.n_tokens == 8192 and x.n_intervals == 16)
+    run_layer_case(w)
