@@ -15,24 +15,28 @@ Sources (cited by title and section; no line numbers):
   (section 13.2, Eq. 23-24).
 * The cross-attention reuse specification page (page 4): blocks (section
   6.1), mixed cache and metadata (section 6.2), the seam set T_tau with the
-  asymmetric true-prefix rule (section 6.3), the biased operator F and its
-  degeneration (section 6.4).
+  asymmetric true-prefix rule (section 6.3), the biased operator F, its
+  inference mode without write-back and its degeneration (section 6.4).
+* "Budgeted KV-Cache Repair" section 7.1, Eq. 2: the Shift operation
+  (positional correction of the retained suffix after a deletion).
 
 Arithmetic is float64 throughout (inputs are widened from their float32 /
 bf16 storage).  Matrix products use numpy's matmul as a library step; there
 is no blocking, fusion or reordering beyond the definitions.
 
-Readings where the pages are silent are listed in the design doc; every function
-here is pinned by tests under ``tests/`` (no function is parity-unpinned).
+Where the pages are silent, the reading taken is stated in the docstring of
+the function that takes it; every function here is pinned by tests under
+``tests/`` (no function is parity-unpinned).
 """
 from .repair_set import (BadBlocks, BadSupport, attn_tile_plan, budget, check_support,
                          runs, seam_set, validate_blocks)
 from .layer import (FLAG_LOCAL, FLAG_SINK, attention_bias, biased_attention_row,
                     interval_major, layer_repair, rms_norm, rope, silu, stack_repair)
+from .cache_ops import inference_attention, shift_cache
 
 __all__ = [
     "BadBlocks", "BadSupport", "attn_tile_plan", "budget", "check_support", "runs",
     "seam_set", "validate_blocks", "FLAG_LOCAL", "FLAG_SINK", "attention_bias",
     "biased_attention_row", "interval_major", "layer_repair", "rms_norm", "rope", "silu",
-    "stack_repair",
+    "stack_repair", "inference_attention", "shift_cache",
 ]
