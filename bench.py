@@ -13,6 +13,8 @@ stdout; progress goes to stderr.
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
     python bench.py --schedule interval --workload NAME   # sequential maximal-interval replay
     python bench.py --table18                              # packed vs interval-wise sweep
+    python bench.py --op inference                         # inference-mode F at decode sizes
+    python bench.py --op shift                             # Shift over the 28-layer 7B cache
 """
 from __future__ import annotations
 
@@ -223,6 +225,102 @@ def run_table18(a) -> int:
     return 0
 
 
+def _event_trials(torch, fn, trials: int, warmup: int, flush_bytes: int = 0):
+    """Median microseconds of fn() over `trials` runs, each bracketed by HIP
+    events on the current stream; when flush_bytes > 0 a scratch buffer of
+    that size is written before every run (outside the events) so that the
+    256 MB Infinity Cache holds none of the operands."""
+    scratch = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+    for _ in range(warmup):
+        fn()
+    times = []
+    for _ in range(trials):
+        if scratch is not None:
+            scratch.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+    return float(np.median(times))
+
+
+def run_inference_bench(a) -> int:
+    """Inference-mode F (cross-attention reuse page, 6.4): biased attention
+    of the last B positions over the 7B mixed cache, no write-back.  HBM-bound
+    at decode sizes: the K/V rows 0..u_max are read once per call.  The
+    Infinity Cache is flushed before every trial."""
+    import torch
+    import packed_partial_prefill_amd as kvr
+    from tests.gpu_harness import cfg_of, dev_cache
+    for w in (wl.QWEN7_DECODE_16K, wl.QWEN7_DECODE_32K):
+        K0, V0 = wl.kv_cache(w, 0)
+        kc, vc = dev_cache(w, K0, V0)
+        del K0, V0
+        flags = torch.from_numpy(wl.initial_flags(w)).cuda()
+        cfg = cfg_of(w)
+        for B in (1, 8, 64):
+            pos = np.arange(w.n_tokens - B, w.n_tokens, dtype=np.int32)
+            dq = torch.from_numpy(wl.queries(w, B)).cuda()
+            dpos = torch.from_numpy(pos).cuda()
+            o = torch.empty((B, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+            ws = torch.empty(kvr.kvr_attention_workspace_bytes(cfg, B, w.n_tokens),
+                             dtype=torch.uint8, device="cuda")
+            fn = lambda: kvr.kvr_biased_attention(cfg, kc, vc, flags, dq, dpos, o, ws)
+            us = _event_trials(torch, fn, a.steps, a.warmup, flush_bytes=512 << 20)
+            kvr.kvr_timing_begin((1 << kvr.KVR_KERNEL_COUNT) - 1)
+            for _ in range(5):
+                fn()
+            torch.cuda.synchronize()
+            kms, kn = kvr.kvr_timing_end()
+            parts = {n: round(kms[i] / kn[i] * 1e3, 2) for i, n in enumerate(kvr.KERNEL_NAMES) if kn[i]}
+            kv_bytes = (int(pos.max()) + 1) * w.n_kv_heads * w.head_dim * 2 * 2
+            qo_bytes = 2 * B * w.n_q_heads * w.head_dim * 4
+            gbs = (kv_bytes + qo_bytes) / (us * 1e-6) / 1e9
+            print(json.dumps({"op": "inference_attention", "workload": w.name, "N": w.n_tokens,
+                              "B": B, "us": round(us, 2), "hbm_gbps": round(gbs, 1),
+                              "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                              "bytes": kv_bytes + qo_bytes, "kernel_us": parts,
+                              "flush": "512 MiB written before each trial"}), flush=True)
+        del kc, vc
+    return 0
+
+
+def run_shift_bench(a) -> int:
+    """Shift (Budgeted KV-Cache Repair, 7.1, Eq. 2) over the 28-layer 7B cache:
+    delete [support_start, support_start + support_len), re-rotate the
+    suffix keys, move values and metadata.  Pure HBM stream."""
+    import torch
+    import packed_partial_prefill_amd as kvr
+    from tests.gpu_harness import cfg_of, dev_cache
+    w = wl.QWEN7_SHIFT
+    cfg = cfg_of(w)
+    a0, d = w.support_start, w.support_len
+    n_out = w.n_tokens - d
+    src, dst = [], []
+    for li in range(w.n_layers):
+        K0, V0 = wl.kv_cache(w, li)
+        src.append(dev_cache(w, K0, V0))
+        dst.append((torch.empty((n_out, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16,
+                                device="cuda"),
+                    torch.empty((n_out, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16,
+                                device="cuda")))
+    fs = torch.from_numpy(wl.initial_flags(w)).cuda()
+    fd = torch.empty(n_out, dtype=torch.uint8, device="cuda")
+    fn = lambda: kvr.kvr_shift_cache(cfg, src, dst, a0, d, flags_src=fs, flags_dst=fd,
+                                     mark=kvr.KVR_FLAG_LOCAL)
+    us = _event_trials(torch, fn, a.steps, a.warmup)
+    row = w.n_kv_heads * w.head_dim * 2 * 2              # K and V bytes of one position
+    nbytes = 2 * n_out * row * w.n_layers + 2 * n_out    # read + write, plus flags
+    gbs = nbytes / (us * 1e-6) / 1e9
+    print(json.dumps({"op": "shift_cache", "workload": w.name, "N": w.n_tokens,
+                      "deleted": [a0, a0 + d], "layers": w.n_layers, "us": round(us, 2),
+                      "hbm_gbps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "bytes": nbytes}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -231,6 +329,9 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=wl.QWEN7_LAYER_SEAMS.name, choices=sorted(wl.WORKLOADS))
     ap.add_argument("--schedule", default="packed", choices=("packed", "interval"))
     ap.add_argument("--table18", action="store_true")
+    ap.add_argument("--op", default="repair", choices=("repair", "inference", "shift"),
+                    help="repair (default, the one-line contract), or the inference-mode "
+                         "attention / Shift measurements (JSON lines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calib-mib", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
@@ -245,6 +346,10 @@ def main(argv=None) -> int:
     torch.cuda.set_device(0)
     if a.table18:
         return run_table18(a)
+    if a.op == "inference":
+        return run_inference_bench(a)
+    if a.op == "shift":
+        return run_shift_bench(a)
 
     w = wl.WORKLOADS[a.workload]
     log(f"[bench] workload {w.name}: generating inputs")

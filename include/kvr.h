@@ -228,6 +228,75 @@ kvr_status kvr_stack_repair(const kvr_config* cfg, int32_t n_layers, const kvr_l
                             int32_t B, const float* x_in, int32_t x_in_rows, float* x_out,
                             void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* Workspace bytes needed by kvr_biased_attention for B query rows over an
+ * n_tokens-position cache; 0 on invalid arguments. */
+size_t kvr_attention_workspace_bytes(const kvr_config* cfg, int32_t B, int32_t n_tokens);
+
+/*
+ * kvr_biased_attention - the operator F in inference mode (cross-attention
+ * reuse page, 6.4, "prefill / decode, inference mode"): attention only, over
+ * the mixed cache with the metadata logit bias, and no write-back:
+ *
+ *   o[r, h] = sum_j softmax_j(<q[r, h], k_j>/sqrt(d) + alpha*local_j +
+ *             beta*sink_j) v_j   over j = 0..d_pos[r] inclusive,
+ *
+ * keys and values of KV head h / (Hq/Hkv).  The query at position u sees
+ * its own position, as the repair's attention does; a decode step writes
+ * the new token's K/V at u (and its flags byte) before calling.
+ *
+ *   q        device float32 [B, Hq, d], post-RoPE (rotated at d_pos[r]).
+ *   d_pos    device int32 [B], strictly increasing, in [0, n_tokens)
+ *            (checkable with kvr_check_support, not checked here).
+ *   cache    K, V [n_tokens, Hkv, d] in cfg->dtype; read only.
+ *   flags    device uint8 [n_tokens] (KVR_FLAG_LOCAL | KVR_FLAG_SINK); read only.
+ *   o        device float32 [B, Hq, d]; must not alias q.
+ *   ws       device workspace of at least kvr_attention_workspace_bytes() bytes.
+ *
+ * Only cfg's dtype, head counts, head_dim, alpha and beta are read.
+ * Errors (before any device work): null or misaligned (16-byte) pointers,
+ * o == q, B < 0, B > n_tokens -> INVALID_ARGUMENT; head_dim not 64/128 or
+ * Hq % Hkv != 0 -> UNSUPPORTED; ws_bytes too small -> WORKSPACE.  B = 0 is a
+ * successful no-op.
+ */
+kvr_status kvr_biased_attention(const kvr_config* cfg, kvr_kv cache, const uint8_t* flags,
+                                int32_t n_tokens, const float* q, const int32_t* d_pos,
+                                int32_t B, float* o, void* ws, size_t ws_bytes,
+                                hipStream_t stream);
+
+/*
+ * kvr_shift_cache - the Shift step that precedes a repair (Budgeted KV-Cache
+ * Repair, section 7.1, Eq. 2): delete positions [del_start, del_start +
+ * del_len) of the cached sequence and position-correct the retained suffix.
+ * For every layer, destination row r is
+ *   r <  del_start:  src row r, copied bit for bit;
+ *   r >= del_start:  src row i = r + del_len with K~ = R_{i-d} R_i^{-1} K_i
+ *                    and V~ = V_i, where d = del_len and R_i is the rotary
+ *                    map with rope_theta, rotate-half pairing (j, j + d_h/2).
+ * R_{i-d} R_i^{-1} turns pair j by -d * theta^(-2j/d_h) whatever i is; the
+ * cosine and sine are evaluated in float64 and the rotation in float32, then
+ * rounded to cfg->dtype.
+ *
+ *   src, dst        host arrays [n_layers] of caches: src K, V [n_tokens, Hkv,
+ *                   d_h], dst K, V [n_tokens - del_len, Hkv, d_h], cfg->dtype.
+ *                   No dst buffer may overlap any src buffer (not in place).
+ *   flags_src/dst   device uint8 [n_tokens] -> [n_tokens - del_len], moved
+ *                   with their rows; `mark` is OR-ed into every moved suffix
+ *                   row (e.g. KVR_FLAG_LOCAL: the shifted keys still carry
+ *                   the deleted span's influence).  Both NULL: no flags.
+ *   block_src/dst   device int32 block ids, moved likewise (both NULL or both set).
+ *
+ * Only cfg's dtype, head counts, head_dim and rope_theta are read.
+ * Errors (before any device work): null or misaligned (16-byte) pointers,
+ * overlapping src/dst, n_layers < 1, del_start < 0, del_len < 0,
+ * del_start + del_len > n_tokens, non-positive rope_theta ->
+ * INVALID_ARGUMENT; head_dim not 64/128 -> UNSUPPORTED.  del_len = 0 copies.
+ */
+kvr_status kvr_shift_cache(const kvr_config* cfg, int32_t n_layers, const kvr_kv* src,
+                           const kvr_kv* dst, const uint8_t* flags_src, uint8_t* flags_dst,
+                           const int32_t* block_src, int32_t* block_dst, int32_t n_tokens,
+                           int32_t del_start, int32_t del_len, uint8_t mark,
+                           hipStream_t stream);
+
 /* Human-readable name of a status. */
 const char* kvr_status_string(kvr_status s);
 /* Detail of the last error returned on the calling thread ("" if none). */
@@ -253,7 +322,9 @@ enum {
   KVR_KERNEL_GATEUP = 7,    /* gate/up GEMM with SwiGLU epilogue           */
   KVR_KERNEL_DOWN = 8,      /* down projection GEMM                        */
   KVR_KERNEL_FINAL = 9,     /* last residual sum into x_out                */
-  KVR_KERNEL_COUNT = 10
+  KVR_KERNEL_QPREP = 10,    /* query scaling (kvr_biased_attention)        */
+  KVR_KERNEL_SHIFT = 11,    /* Shift re-rotation / move (kvr_shift_cache)  */
+  KVR_KERNEL_COUNT = 12
 };
 kvr_status kvr_timing_begin(uint32_t mask);
 kvr_status kvr_timing_end(double* total_ms, int32_t* launches);

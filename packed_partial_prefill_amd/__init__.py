@@ -27,7 +27,7 @@ KVR_FLAG_LOCAL, KVR_FLAG_SINK = 1, 2
 KVR_SEAM_ASYMMETRIC, KVR_INIT_META = 1, 2
 KVR_ATTN_QROWS, KVR_ATTN_KV_TILE = 128, 64
 KERNEL_NAMES = ["plan", "norm", "qkv", "rope", "attn", "attn_merge", "oproj", "gateup", "down",
-                "final"]
+                "final", "qprep", "shift"]
 KVR_KERNEL_COUNT = len(KERNEL_NAMES)
 
 
@@ -81,6 +81,11 @@ _sigs = {
     "kvr_stack_repair": (C.c_int, [C.POINTER(kvr_config), _I, C.POINTER(kvr_layer_weights),
                                    C.POINTER(kvr_kv), C.POINTER(kvr_meta), _P, _I, _P, _I, _P,
                                    _P, C.c_size_t, _P]),
+    "kvr_attention_workspace_bytes": (C.c_size_t, [C.POINTER(kvr_config), _I, _I]),
+    "kvr_biased_attention": (C.c_int, [C.POINTER(kvr_config), kvr_kv, _P, _I, _P, _P, _I, _P, _P,
+                                       C.c_size_t, _P]),
+    "kvr_shift_cache": (C.c_int, [C.POINTER(kvr_config), _I, C.POINTER(kvr_kv), C.POINTER(kvr_kv),
+                                  _P, _P, _P, _P, _I, _I, _I, C.c_uint8, _P]),
     "kvr_status_string": (C.c_char_p, [C.c_int]),
     "kvr_last_error": (C.c_char_p, []),
     "kvr_timing_begin": (C.c_int, [C.c_uint32]),
@@ -201,6 +206,43 @@ def kvr_stack_repair(cfg: Config, weights: Sequence[dict], caches: Sequence[Tupl
     _check(_lib.kvr_stack_repair(C.byref(c), L, ws_arr, kv_arr, C.byref(meta), _ptr(d_T),
                                  d_T.numel(), _ptr(x_in), x_in.shape[0], _ptr(x_out), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def kvr_attention_workspace_bytes(cfg: Config, B: int, n_tokens: int) -> int:
+    c = cfg.c()
+    n = _lib.kvr_attention_workspace_bytes(C.byref(c), B, n_tokens)
+    if n == 0:
+        raise KvrError(-1, "invalid shape for kvr_attention_workspace_bytes")
+    return int(n)
+
+
+def kvr_biased_attention(cfg: Config, k_cache, v_cache, flags, q, d_pos, o, ws,
+                         stream=None) -> None:
+    """Inference-mode F: o [B, Hq, d] (float32) = biased attention of the
+    post-RoPE queries q [B, Hq, d] (float32) at positions d_pos over the
+    cache, without write-back."""
+    c = cfg.c()
+    _check(_lib.kvr_biased_attention(C.byref(c), kvr_kv(_ptr(k_cache), _ptr(v_cache)),
+                                     _ptr(flags), k_cache.shape[0], _ptr(q), _ptr(d_pos),
+                                     d_pos.numel(), _ptr(o), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def kvr_shift_cache(cfg: Config, src: Sequence[Tuple], dst: Sequence[Tuple], del_start: int,
+                    del_len: int, flags_src=None, flags_dst=None, block_src=None,
+                    block_dst=None, mark: int = 0, stream=None) -> None:
+    """Shift (Eq. 2): dst caches (n_tokens - del_len rows) from src caches
+    with [del_start, del_start + del_len) deleted and the suffix keys
+    re-rotated; flags / block ids move with their rows."""
+    c = cfg.c()
+    L = len(src)
+    if len(dst) != L:
+        raise ValueError("one destination (k, v) per source layer")
+    s_arr = (kvr_kv * L)(*[kvr_kv(_ptr(k), _ptr(v)) for k, v in src])
+    d_arr = (kvr_kv * L)(*[kvr_kv(_ptr(k), _ptr(v)) for k, v in dst])
+    _check(_lib.kvr_shift_cache(C.byref(c), L, s_arr, d_arr, _ptr(flags_src), _ptr(flags_dst),
+                                _ptr(block_src), _ptr(block_dst), src[0][0].shape[0], del_start,
+                                del_len, mark, _stream(stream)))
 
 
 def kvr_status_string(st: int) -> str:

@@ -2,6 +2,7 @@
 // Validates arguments before touching the device, carves the caller's
 // workspace, and enqueues the per-layer kernel sequence on the caller's
 // stream (no synchronisation, no device allocation).
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -69,16 +70,30 @@ struct Launch {
   } while (0)
 
 // ---------------------------------------------------------------- config
-kvr_status check_config(const kvr_config* c, kvr::Shape* sh) {
+// dtype and attention heads: what every entry point reads.
+kvr_status check_heads(const kvr_config* c, kvr::Shape* sh) {
   if (!c) return fail(KVR_ERR_INVALID_ARGUMENT, "cfg is NULL");
   if (c->dtype != KVR_F32 && c->dtype != KVR_BF16)
     return fail(KVR_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(c->dtype));
-  if (c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->intermediate <= 0)
-    return fail(KVR_ERR_INVALID_ARGUMENT, "non-positive shape");
+  if (c->n_q_heads <= 0 || c->n_kv_heads <= 0)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "non-positive head counts");
   if (c->head_dim != 64 && c->head_dim != 128)
     return fail(KVR_ERR_UNSUPPORTED, "head_dim %d (64 or 128 supported)", c->head_dim);
   if (c->n_q_heads % c->n_kv_heads)
     return fail(KVR_ERR_UNSUPPORTED, "n_q_heads %% n_kv_heads != 0");
+  *sh = kvr::Shape{};
+  sh->hq = c->n_q_heads;
+  sh->hkv = c->n_kv_heads;
+  sh->d = c->head_dim;
+  sh->group = c->n_q_heads / c->n_kv_heads;
+  return KVR_OK;
+}
+
+kvr_status check_config(const kvr_config* c, kvr::Shape* sh) {
+  kvr_status st = check_heads(c, sh);
+  if (st != KVR_OK) return st;
+  if (c->hidden <= 0 || c->intermediate <= 0)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "non-positive shape");
   if (c->hidden % 64 || c->intermediate % 64)
     return fail(KVR_ERR_UNSUPPORTED, "hidden and intermediate must be multiples of 64");
   if (c->hidden > 8192) return fail(KVR_ERR_UNSUPPORTED, "hidden > 8192");
@@ -128,6 +143,24 @@ Layout layout_for(const kvr_config* c, const kvr::Shape& sh, int B, int n_tokens
   L.q = off;       off = up256(off + static_cast<size_t>(B) * sh.hq * sh.d * es);
   L.o = off;       off = up256(off + static_cast<size_t>(B) * sh.hq * sh.d * es);
   L.mlp = off;     off = up256(off + static_cast<size_t>(B) * sh.inter * es);
+  L.attn = off;    off = up256(off + kvr::attention_workspace_bytes(c->dtype, B, n_tokens, sh));
+  L.total = off;
+  return L;
+}
+
+// Workspace of kvr_biased_attention: plan, scaled queries, split-KV partials.
+struct AttnLayout {
+  size_t n_full, n_total, q, attn, total;
+};
+
+AttnLayout attn_layout_for(const kvr_config* c, const kvr::Shape& sh, int B, int n_tokens) {
+  AttnLayout L{};
+  const int nt = kvr::plan_tiles(B, sh.group);
+  size_t off = 0;
+  L.n_full = off;  off = up256(off + static_cast<size_t>(nt) * 4);
+  L.n_total = off; off = up256(off + static_cast<size_t>(nt) * 4);
+  L.q = off;
+  if (c->dtype == KVR_BF16) off = up256(off + static_cast<size_t>(B) * sh.hq * sh.d * 2);
   L.attn = off;    off = up256(off + kvr::attention_workspace_bytes(c->dtype, B, n_tokens, sh));
   L.total = off;
   return L;
@@ -218,7 +251,7 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
                                   cfg->alpha, cfg->beta, n_full, n_total, attn_ws, obuf, stream));
     if (kvr::attention_needs_merge(dt))
       KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "attention merge",
-              kvr::launch_attention_merge(dt, B, N, sh, n_total, attn_ws, obuf, stream));
+              kvr::launch_attention_merge(dt, B, N, sh, n_total, attn_ws, obuf, false, stream));
     kvr::WeightSegs wo{{W.wo, nullptr, nullptr}, {0, sh.hidden, sh.hidden, sh.hidden}, 1};
     KVR_RUN(KVR_KERNEL_OPROJ, stream, "o gemm",
             kvr::launch_gemm_partial(dt, obuf, wo, B, sh.hidden, sh.hq * sh.d, L.g_o, part,
@@ -340,6 +373,134 @@ kvr_status kvr_stack_repair(const kvr_config* cfg, int32_t n_layers, const kvr_l
                             void* ws, size_t ws_bytes, hipStream_t stream) {
   return run_stack(cfg, n_layers, w, caches, meta, d_T, B, x_in, x_in_rows, x_out, ws, ws_bytes,
                    stream);
+}
+
+size_t kvr_attention_workspace_bytes(const kvr_config* cfg, int32_t B, int32_t n_tokens) {
+  kvr::Shape sh;
+  if (check_heads(cfg, &sh) != KVR_OK || B < 0 || n_tokens <= 0 || B > n_tokens) return 0;
+  return attn_layout_for(cfg, sh, B, n_tokens).total + 256;
+}
+
+kvr_status kvr_biased_attention(const kvr_config* cfg, kvr_kv cache, const uint8_t* flags,
+                                int32_t n_tokens, const float* q, const int32_t* d_pos,
+                                int32_t B, float* o, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  g_err[0] = '\0';
+  kvr::Shape sh;
+  kvr_status st = check_heads(cfg, &sh);
+  if (st != KVR_OK) return st;
+  if (!std::isfinite(cfg->alpha) || !std::isfinite(cfg->beta))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "alpha and beta must be finite");
+  if (n_tokens <= 0) return fail(KVR_ERR_INVALID_ARGUMENT, "n_tokens must be positive");
+  if (B < 0 || B > n_tokens)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d outside [0, n_tokens=%d]", B, n_tokens);
+  if (B == 0) return KVR_OK;
+  if (!dev_ok(q) || !dev_ok(d_pos) || !dev_ok(o) || !dev_ok(ws) || !dev_ok(flags) ||
+      !dev_ok(cache.k) || !dev_ok(cache.v))
+    return fail(KVR_ERR_INVALID_ARGUMENT,
+                "q, d_pos, o, ws, flags and cache pointers must be non-NULL and 16-byte aligned");
+  if (static_cast<const void*>(o) == static_cast<const void*>(q))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "o must not alias q");
+  const AttnLayout L = attn_layout_for(cfg, sh, B, n_tokens);
+  uint8_t* base = reinterpret_cast<uint8_t*>(up256(reinterpret_cast<uintptr_t>(ws)));
+  const size_t slack = static_cast<size_t>(base - static_cast<uint8_t*>(ws));
+  if (ws_bytes < L.total + slack)
+    return fail(KVR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total + slack);
+
+  const kvr_dtype dt = cfg->dtype;
+  int32_t* n_full = reinterpret_cast<int32_t*>(base + L.n_full);
+  int32_t* n_total = reinterpret_cast<int32_t*>(base + L.n_total);
+  void* attn_ws = base + L.attn;
+  // float32 storage attends on the caller's queries directly (the row kernel
+  // applies 1/sqrt(d) itself); bf16 takes them scaled and rounded once
+  const void* qk = q;
+  if (dt == KVR_BF16) {
+    qk = base + L.q;
+    KVR_RUN(KVR_KERNEL_QPREP, stream, "query prep",
+            kvr::launch_prep_queries(dt, q, static_cast<size_t>(B) * sh.hq * sh.d,
+                                     kvr::attention_q_scale(dt, sh.d), base + L.q, stream));
+  }
+  KVR_RUN(KVR_KERNEL_PLAN, stream, "plan",
+          kvr::launch_build_plan(d_pos, B, sh.group, n_full, n_total, stream));
+  KVR_RUN(KVR_KERNEL_ATTN, stream, "attention",
+          kvr::launch_attention(dt, qk, cache.k, cache.v, flags, d_pos, B, n_tokens, sh,
+                                cfg->alpha, cfg->beta, n_full, n_total, attn_ws, o, stream));
+  if (kvr::attention_needs_merge(dt))
+    KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "attention merge",
+            kvr::launch_attention_merge(dt, B, n_tokens, sh, n_total, attn_ws, o, true, stream));
+  return KVR_OK;
+}
+
+kvr_status kvr_shift_cache(const kvr_config* cfg, int32_t n_layers, const kvr_kv* src,
+                           const kvr_kv* dst, const uint8_t* flags_src, uint8_t* flags_dst,
+                           const int32_t* block_src, int32_t* block_dst, int32_t n_tokens,
+                           int32_t del_start, int32_t del_len, uint8_t mark,
+                           hipStream_t stream) {
+  g_err[0] = '\0';
+  kvr::Shape sh;
+  kvr_status st = check_heads(cfg, &sh);
+  if (st != KVR_OK) return st;
+  if (!std::isfinite(cfg->rope_theta) || cfg->rope_theta <= 0.0)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "rope_theta must be finite and positive");
+  if (n_layers < 1 || !src || !dst)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "n_layers must be >= 1 with src and dst arrays");
+  if (n_tokens < 0 || del_start < 0 || del_len < 0 ||
+      static_cast<int64_t>(del_start) + del_len > n_tokens)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "span [%d, %d + %d) outside [0, %d)", del_start,
+                del_start, del_len, n_tokens);
+  if ((flags_src == nullptr) != (flags_dst == nullptr) ||
+      (block_src == nullptr) != (block_dst == nullptr))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "flags and block ids: both src and dst, or neither");
+  if ((flags_dst && (!aligned16(flags_src) || !aligned16(flags_dst))) ||
+      (block_dst && (!aligned16(block_src) || !aligned16(block_dst))))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "metadata pointers not 16-byte aligned");
+  const int n_out = n_tokens - del_len;
+  const size_t row_bytes = static_cast<size_t>(sh.hkv) * sh.d * esize(cfg->dtype);
+  struct Range { uintptr_t lo, hi; };
+  std::vector<Range> srcs, dsts;
+  for (int l = 0; l < n_layers; ++l) {
+    if (!dev_ok(src[l].k) || !dev_ok(src[l].v) || !dev_ok(dst[l].k) || !dev_ok(dst[l].v))
+      return fail(KVR_ERR_INVALID_ARGUMENT, "layer %d: cache pointers NULL or not 16-byte aligned", l);
+    for (const void* p : {src[l].k, src[l].v}) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+      srcs.push_back({a, a + row_bytes * n_tokens});
+    }
+    for (const void* p : {static_cast<const void*>(dst[l].k), static_cast<const void*>(dst[l].v)}) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+      dsts.push_back({a, a + row_bytes * n_out});
+    }
+  }
+  if (flags_dst) {
+    srcs.push_back({reinterpret_cast<uintptr_t>(flags_src), reinterpret_cast<uintptr_t>(flags_src) + n_tokens});
+    dsts.push_back({reinterpret_cast<uintptr_t>(flags_dst), reinterpret_cast<uintptr_t>(flags_dst) + n_out});
+  }
+  if (block_dst) {
+    srcs.push_back({reinterpret_cast<uintptr_t>(block_src), reinterpret_cast<uintptr_t>(block_src) + 4u * n_tokens});
+    dsts.push_back({reinterpret_cast<uintptr_t>(block_dst), reinterpret_cast<uintptr_t>(block_dst) + 4u * n_out});
+  }
+  for (const Range& d : dsts)
+    for (const Range& s : srcs)
+      if (d.lo < s.hi && s.lo < d.hi && d.lo < d.hi && s.lo < s.hi)
+        return fail(KVR_ERR_INVALID_ARGUMENT, "a destination buffer overlaps a source buffer");
+  if (n_out == 0) return KVR_OK;
+
+  for (int l0 = 0; l0 < n_layers; l0 += kvr::kShiftMaxLayers) {
+    const int nl = std::min(kvr::kShiftMaxLayers, n_layers - l0);
+    kvr::ShiftLayers L{};
+    for (int j = 0; j < nl; ++j) {
+      L.src_k[j] = src[l0 + j].k;
+      L.src_v[j] = src[l0 + j].v;
+      L.dst_k[j] = dst[l0 + j].k;
+      L.dst_v[j] = dst[l0 + j].v;
+    }
+    KVR_RUN(KVR_KERNEL_SHIFT, stream, "shift",
+            kvr::launch_shift(cfg->dtype, L, nl, n_out, sh, del_start, del_len, cfg->rope_theta,
+                              stream));
+  }
+  KVR_RUN(KVR_KERNEL_SHIFT, stream, "shift metadata",
+          kvr::launch_shift_meta(flags_src, flags_dst, block_src, block_dst, n_out, del_start,
+                                 del_len, mark, stream));
+  return KVR_OK;
 }
 
 const char* kvr_status_string(kvr_status s) {

@@ -359,15 +359,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   const size_t slot = (static_cast<size_t>(qt) * Hkv + g) * n_splits + sp;
   const int ql = wave * 32 + (lane & 31);
   float* po = part_o + slot * D * kQRows;
+  if (p < P) {   // columns past the last pair are never merged
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int d = db * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
-      po[d * kQRows + ql] = o[db][t];
-    }
+      for (int t = 0; t < 16; ++t) {
+        const int d = db * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
+        po[d * kQRows + ql] = o[db][t];
+      }
+  }
   l += __shfl_xor(l, 32, 64);
-  if (half == 0) {
+  if (half == 0 && p < P) {
     float* pm = part_ml + slot * 2 * kQRows;
     pm[ql] = m_set ? m_eff : -INFINITY;
     pm[kQRows + ql] = l;
@@ -376,13 +378,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
 
 // Merge the split-KV partials: workgroup (query tile, KV group, 16-row slice
 // of d); thread (pair ql, 8 consecutive d).  Split weights 2^(m_s - max m),
-// normalised by the weighted sums; each thread writes one 16-byte chunk of
-// its pair's output row.
-template <int D>
+// normalised by the weighted sums; each thread writes its pair's 8 outputs
+// (one 16-byte chunk of bf16, or two of float32).
+template <int D, typename OutT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ n_total, int B, int Hq, int Hkv, int G, int split_tiles,
-    int n_splits, bf16_t* __restrict__ o) {
+    int n_splits, OutT* __restrict__ o) {
   const int qt = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x;
   const int ql = tid & (kQRows - 1);
@@ -405,13 +407,19 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     for (int i = 0; i < 8; ++i) acc[i] += w * po[i * kQRows];
   }
   const float inv = 1.f / denom;
-  u32x4_t outv;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    outv[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i] * inv)) |
-              (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1] * inv)) << 16);
   const int r = p / G, h = g * G + (p - r * G);
-  *reinterpret_cast<u32x4_t*>(o + (static_cast<size_t>(r) * Hq + h) * D + d0) = outv;
+  OutT* dst = o + (static_cast<size_t>(r) * Hq + h) * D + d0;
+  if constexpr (sizeof(OutT) == 2) {
+    u32x4_t outv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      outv[i] = static_cast<uint32_t>(f32_to_bf16(acc[2 * i] * inv)) |
+                (static_cast<uint32_t>(f32_to_bf16(acc[2 * i + 1] * inv)) << 16);
+    *reinterpret_cast<u32x4_t*>(dst) = outv;
+  } else {
+    reinterpret_cast<float4*>(dst)[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    reinterpret_cast<float4*>(dst)[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  }
 }
 
 // KV tiles per split: 32 (2048 keys) when the launch has plenty of
@@ -466,7 +474,7 @@ hipError_t launch_mfma(const void* q, const void* k_cache, const void* v_cache,
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, typename OutT>
 hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_total, void* ws,
                         void* o_out, hipStream_t stream) {
   const int nt = plan_tiles(B, sh.group);
@@ -475,10 +483,9 @@ hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_t
   const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
   const float* part_o = static_cast<const float*>(ws);
   const float* part_ml = part_o + slots * sh.d * kQRows;
-  hipLaunchKernelGGL(k_attn_merge<D>, dim3(nt, sh.hkv, D / 16), dim3(kAttnThreads), 0, stream,
-                     part_o,
-                     part_ml, n_total, B, sh.hq, sh.hkv, sh.group, st, ns,
-                     static_cast<bf16_t*>(o_out));
+  hipLaunchKernelGGL((k_attn_merge<D, OutT>), dim3(nt, sh.hkv, D / 16), dim3(kAttnThreads), 0,
+                     stream, part_o, part_ml, n_total, B, sh.hq, sh.hkv, sh.group, st, ns,
+                     static_cast<OutT*>(o_out));
   return hipGetLastError();
 }
 }  // namespace
@@ -512,10 +519,14 @@ bool attention_needs_merge(kvr_dtype dt) { return dt == KVR_BF16; }
 
 hipError_t launch_attention_merge(kvr_dtype dt, int B, int n_tokens, const Shape& sh,
                                   const int32_t* plan_n_total, void* ws, void* o_out,
-                                  hipStream_t stream) {
+                                  bool out_f32, hipStream_t stream) {
   if (B == 0 || dt != KVR_BF16) return hipSuccess;
-  if (sh.d == 128) return launch_merge<128>(B, n_tokens, sh, plan_n_total, ws, o_out, stream);
-  return launch_merge<64>(B, n_tokens, sh, plan_n_total, ws, o_out, stream);
+  if (out_f32) {
+    if (sh.d == 128) return launch_merge<128, float>(B, n_tokens, sh, plan_n_total, ws, o_out, stream);
+    return launch_merge<64, float>(B, n_tokens, sh, plan_n_total, ws, o_out, stream);
+  }
+  if (sh.d == 128) return launch_merge<128, bf16_t>(B, n_tokens, sh, plan_n_total, ws, o_out, stream);
+  return launch_merge<64, bf16_t>(B, n_tokens, sh, plan_n_total, ws, o_out, stream);
 }
 
 }  // namespace kvr

@@ -74,6 +74,27 @@ hipError_t launch_rope_writeback(kvr_dtype dt, const float* qkv_part, int splits
                                  const Shape& sh, float q_scale, void* q_out, void* k_cache,
                                  void* v_cache, uint8_t* flags, hipStream_t stream);
 
+// q_out[i] = q[i] * scale stored in dtype dt (n elements, a multiple of 4).
+hipError_t launch_prep_queries(kvr_dtype dt, const float* q, size_t n, float scale, void* q_out,
+                               hipStream_t stream);
+
+// ---- shift.hip ----------------------------------------------------------------
+constexpr int kShiftMaxLayers = 32;   // layers per launch (kernel-argument arrays)
+struct ShiftLayers {
+  const void* src_k[kShiftMaxLayers];
+  const void* src_v[kShiftMaxLayers];
+  void* dst_k[kShiftMaxLayers];
+  void* dst_v[kShiftMaxLayers];
+};
+// Cache rows [0, n_out) of each layer's dst from src with rows
+// [del_start, del_start + del_len) deleted; moved keys re-rotated by -del_len.
+hipError_t launch_shift(kvr_dtype dt, const ShiftLayers& L, int n_layers, int n_out,
+                        const Shape& sh, int del_start, int del_len, double theta,
+                        hipStream_t stream);
+hipError_t launch_shift_meta(const uint8_t* f_src, uint8_t* f_dst, const int32_t* b_src,
+                             int32_t* b_dst, int n_out, int del_start, int del_len, uint8_t mark,
+                             hipStream_t stream);
+
 // ---- attention.hip ----------------------------------------------------------
 size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh);
 hipError_t launch_attention(kvr_dtype dt, const void* q, const void* k_cache,
@@ -82,9 +103,10 @@ hipError_t launch_attention(kvr_dtype dt, const void* q, const void* k_cache,
                             const int32_t* plan_n_full, const int32_t* plan_n_total, void* ws,
                             void* o_out, hipStream_t stream);
 bool attention_needs_merge(kvr_dtype dt);
+// o_out: [B, Hq, d] in bf16, or float32 when out_f32.
 hipError_t launch_attention_merge(kvr_dtype dt, int B, int n_tokens, const Shape& sh,
                                   const int32_t* plan_n_total, void* ws, void* o_out,
-                                  hipStream_t stream);
+                                  bool out_f32, hipStream_t stream);
 // Factor the RoPE kernel folds into the stored queries for this path.
 float attention_q_scale(kvr_dtype dt, int head_dim);
 

@@ -102,7 +102,33 @@ __global__ __launch_bounds__(kThreads) void k_rope_writeback(
   if (threadIdx.x == 0) flags[u] = static_cast<uint8_t>(flags[u] & ~(KVR_FLAG_LOCAL | KVR_FLAG_SINK));
 }
 
+// Queries handed in from outside the repair (inference mode): scaled by the
+// attention kernel's score factor and stored in the cache's dtype.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void k_prep_queries(const float4* __restrict__ q,
+                                                           size_t n4, float scale,
+                                                           T* __restrict__ out) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = q[i];
+  put4<T>(out + 4 * i, make_float4(v.x * scale, v.y * scale, v.z * scale, v.w * scale));
+}
+
 }  // namespace
+
+hipError_t launch_prep_queries(kvr_dtype dt, const float* q, size_t n, float scale, void* q_out,
+                               hipStream_t stream) {
+  const size_t n4 = n / 4;
+  if (n4 == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((n4 + kThreads - 1) / kThreads));
+  if (dt == KVR_BF16)
+    hipLaunchKernelGGL(k_prep_queries<bf16_t>, grid, dim3(kThreads), 0, stream,
+                       reinterpret_cast<const float4*>(q), n4, scale, static_cast<bf16_t*>(q_out));
+  else
+    hipLaunchKernelGGL(k_prep_queries<float>, grid, dim3(kThreads), 0, stream,
+                       reinterpret_cast<const float4*>(q), n4, scale, static_cast<float*>(q_out));
+  return hipGetLastError();
+}
 
 hipError_t launch_rope_writeback(kvr_dtype dt, const float* qkv_part, int splits,
                                  size_t split_stride, const float* bq, const float* bk,

@@ -22,6 +22,7 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
               "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
+              "kvr_attention_workspace_bytes", "kvr_biased_attention", "kvr_shift_cache",
               "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
         assert n in names
 
@@ -133,5 +134,70 @@ def test_status_strings(kvr):
 def test_python_binding_has_the_c_names(kvr):
     for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
               "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
+              "kvr_attention_workspace_bytes", "kvr_biased_attention", "kvr_shift_cache",
               "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
         assert callable(getattr(kvr, n))
+
+
+def _attn(kvr, cfg=None, B=4, n_tokens=512, q=FAKE, pos=FAKE, o=FAKE + 8192, ws_bytes=1 << 40,
+          flags=FAKE, k=FAKE):
+    lib = kvr.lib()
+    cfg = cfg or _cfg(kvr)
+    return lib.kvr_biased_attention(C.byref(cfg), kvr.kvr_kv(k, FAKE), flags, n_tokens, q, pos,
+                                    B, o, FAKE, ws_bytes, None)
+
+
+def test_biased_attention_host_validation(kvr):
+    # only the attention fields of the config are read: a zero hidden size is fine
+    assert _attn(kvr, cfg=_cfg(kvr, hidden=0, intermediate=0), ws_bytes=16) == -6
+    assert _attn(kvr, cfg=_cfg(kvr, head_dim=96)) == -2
+    assert _attn(kvr, cfg=_cfg(kvr, n_q_heads=6, n_kv_heads=4)) == -2
+    assert _attn(kvr, cfg=_cfg(kvr, alpha=float("nan"))) == -1
+    assert _attn(kvr, B=-1) == -1
+    assert _attn(kvr, B=513) == -1
+    assert _attn(kvr, q=None) == -1
+    assert _attn(kvr, pos=FAKE + 4) == -1
+    assert _attn(kvr, o=FAKE) == -1                        # o aliases q
+    assert _attn(kvr, flags=None) == -1
+    assert _attn(kvr, k=None) == -1
+    assert _attn(kvr, ws_bytes=16) == -6
+    assert _attn(kvr, B=0) == 0
+    lib = kvr.lib()
+    c = _cfg(kvr)
+    a = lib.kvr_attention_workspace_bytes(C.byref(c), 1, 512)
+    b = lib.kvr_attention_workspace_bytes(C.byref(c), 64, 512)
+    assert 0 < a <= b
+    assert lib.kvr_attention_workspace_bytes(C.byref(c), 600, 512) == 0
+
+
+def _shift(kvr, cfg=None, n_layers=2, n_tokens=100, a=10, d=5, src=None, dst=None, fs=None,
+           fd=None, bs=None, bd=None):
+    lib = kvr.lib()
+    cfg = cfg or _cfg(kvr)
+    row = cfg.n_kv_heads * cfg.head_dim * 4              # float32 rows
+    span = row * n_tokens
+    src = src or [(FAKE + 2 * l * span, FAKE + (2 * l + 1) * span) for l in range(n_layers)]
+    base = FAKE + 2 * n_layers * span + 4096
+    dst = dst or [(base + 2 * l * span, base + (2 * l + 1) * span) for l in range(n_layers)]
+    s_arr = (kvr.kvr_kv * n_layers)(*[kvr.kvr_kv(k, v) for k, v in src])
+    d_arr = (kvr.kvr_kv * n_layers)(*[kvr.kvr_kv(k, v) for k, v in dst])
+    return lib.kvr_shift_cache(C.byref(cfg), n_layers, s_arr, d_arr, fs, fd, bs, bd, n_tokens,
+                               a, d, 0, None)
+
+
+def test_shift_cache_host_validation(kvr):
+    assert _shift(kvr, cfg=_cfg(kvr, head_dim=80)) == -2
+    assert _shift(kvr, cfg=_cfg(kvr, rope_theta=-1.0)) == -1
+    assert _shift(kvr, n_layers=0) == -1
+    assert _shift(kvr, a=-1) == -1
+    assert _shift(kvr, d=-1) == -1
+    assert _shift(kvr, a=96, d=5) == -1                    # span past the end
+    assert _shift(kvr, src=[(None, FAKE), (FAKE, FAKE)]) == -1
+    assert _shift(kvr, fs=FAKE) == -1                      # flags src without dst
+    assert _shift(kvr, bs=FAKE, bd=FAKE + 8) == -1         # misaligned block ids
+    # in place (dst == src) and partial overlaps are refused
+    src = [(FAKE, FAKE + (1 << 16)), (FAKE + (2 << 16), FAKE + (3 << 16))]
+    assert _shift(kvr, src=src, dst=src) == -1
+    dst = [(FAKE + (8 << 16), FAKE + (9 << 16)), (FAKE + (1 << 16) + 512, FAKE + (10 << 16))]
+    assert _shift(kvr, src=src, dst=dst) == -1
+    assert _shift(kvr, n_tokens=5, a=0, d=5) == 0          # nothing left: no device work

@@ -40,7 +40,7 @@ CHUNK = 1 << 22
 SEED_ROOT = 1234
 
 T_KCACHE, T_VCACHE, T_X, T_ATTN_NORM, T_WQ, T_WK, T_WV, T_WO, T_MLP_NORM, \
-    T_WGATE, T_WUP, T_WDOWN, T_SUPPORT, T_BQ, T_BK, T_BV = range(16)
+    T_WGATE, T_WUP, T_WDOWN, T_SUPPORT, T_BQ, T_BK, T_BV, T_QUERY = range(17)
 
 
 @dataclass(frozen=True)
@@ -59,7 +59,7 @@ class Workload:
     alpha: float
     beta: float
     tau: int = 0                    # seam half-width (support == "seams")
-    support: str = "seams"          # seams | contiguous | matched | isolated | intervals | explicit
+    support: str = "seams"          # seams | contiguous | matched | isolated | intervals | suffix | span
     budget_percent: float = 0.0     # isolated supports: B = min(S, ceil(S*b/100))
     support_start: int = 0          # contiguous / matched supports: first position
     support_len: int = 0            # contiguous / matched / intervals supports: length B
@@ -136,9 +136,27 @@ def _qwen3_8b(n_tokens: int, n_intervals: int) -> Workload:
 
 TABLE18 = [_qwen3_8b(n, r) for n in (2048, 8192) for r in (1, 4, 16)]
 
+# Inference mode (attention only, no write-back) at decode sizes: the last
+# B = support_len positions query the 7B mixed cache (seam geometry flags).
+QWEN7_DECODE_16K = Workload("qwen2.5-7b-decode-16k", 7, hidden=3584, n_q_heads=28, n_kv_heads=4,
+                            head_dim=128, intermediate=18944, n_layers=1, n_tokens=16384,
+                            block_size=256, dtype="bf16", alpha=-1.0, beta=-2.0,
+                            support="suffix", support_len=8)
+QWEN7_DECODE_32K = Workload("qwen2.5-7b-decode-32k", 8, hidden=3584, n_q_heads=28, n_kv_heads=4,
+                            head_dim=128, intermediate=18944, n_layers=1, n_tokens=32768,
+                            block_size=512, dtype="bf16", alpha=-1.5, beta=-3.0,
+                            support="suffix", support_len=8)
+# Shift (deletion + positional correction) over a 28-layer 7B cache: the
+# span [support_start, support_start + support_len) is deleted.
+QWEN7_SHIFT = Workload("qwen2.5-7b-shift28-16k", 9, hidden=3584, n_q_heads=28, n_kv_heads=4,
+                       head_dim=128, intermediate=18944, n_layers=28, n_tokens=16384,
+                       block_size=256, dtype="bf16", alpha=-1.0, beta=-2.0, support="span",
+                       support_start=4096, support_len=1024)
+
 WORKLOADS = {w.name: w for w in (TINY, QWEN15_LAYER, QWEN7_LAYER_SEAMS, QWEN7_LAYER_CONTIG,
                                  QWEN7_LAYER_MATCHED, QWEN7_STACK_ISOLATED,
-                                 QWEN15_STACK_DEGENERATE, *TABLE18)}
+                                 QWEN15_STACK_DEGENERATE, *TABLE18, QWEN7_DECODE_16K,
+                                 QWEN7_DECODE_32K, QWEN7_SHIFT)}
 
 
 # ----------------------------------------------------------------------------
@@ -254,6 +272,16 @@ def hidden_states(w: Workload, threads: Optional[int] = None) -> np.ndarray:
     return out.reshape(w.n_tokens, w.hidden)
 
 
+def queries(w: Workload, B: int, threads: Optional[int] = None) -> np.ndarray:
+    """Post-RoPE queries [B, Hq, d] ~ N(0,1) handed to inference-mode
+    attention; float32 at the boundary (never bf16-rounded)."""
+    n = B * w.n_q_heads * w.head_dim
+    out = np.empty(n, dtype=np.float32)
+    _normal_chunks((SEED_ROOT, w.cfg_id, 0, T_QUERY), n, out,
+                   threads if threads is not None else default_threads())
+    return out.reshape(B, w.n_q_heads, w.head_dim)
+
+
 def kv_cache(w: Workload, layer: int, threads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Retained cache of one layer: K, V [N, Hkv, d] ~ N(0,1)."""
     shp = (w.n_tokens, w.n_kv_heads, w.head_dim)
@@ -313,6 +341,8 @@ def explicit_support(w: Workload) -> Optional[np.ndarray]:
         return isolated_support(w)
     if w.support == "intervals":
         return interval_support(w.n_tokens, w.support_len, w.n_intervals)
+    if w.support == "suffix":
+        return np.arange(w.n_tokens - w.support_len, w.n_tokens, dtype=np.int32)
     raise ValueError(w.support)
 
 
