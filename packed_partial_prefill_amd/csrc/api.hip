@@ -155,6 +155,11 @@ struct AttnLayout {
 
 AttnLayout attn_layout_for(const kvr_config* c, const kvr::Shape& sh, int B, int n_tokens) {
   AttnLayout L{};
+  if (kvr::decode_supported(c->dtype, B, sh)) {   // few pairs: chunk partials only
+    L.attn = 0;
+    L.total = up256(kvr::decode_workspace_bytes(B, n_tokens, sh));
+    return L;
+  }
   const int nt = kvr::plan_tiles(B, sh.group);
   size_t off = 0;
   L.n_full = off;  off = up256(off + static_cast<size_t>(nt) * 4);
@@ -408,6 +413,15 @@ kvr_status kvr_biased_attention(const kvr_config* cfg, kvr_kv cache, const uint8
     return fail(KVR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total + slack);
 
   const kvr_dtype dt = cfg->dtype;
+  if (kvr::decode_supported(dt, B, sh)) {
+    // decode sizes: one streaming pass over the cache plus a chunk merge
+    KVR_RUN(KVR_KERNEL_ATTN, stream, "decode attention",
+            kvr::launch_attention_decode(q, d_pos, B, n_tokens, cache.k, cache.v, flags, sh,
+                                         cfg->alpha, cfg->beta, base + L.attn, o, stream));
+    KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "decode merge",
+            kvr::launch_attention_decode_merge(d_pos, B, n_tokens, sh, base + L.attn, o, stream));
+    return KVR_OK;
+  }
   int32_t* n_full = reinterpret_cast<int32_t*>(base + L.n_full);
   int32_t* n_total = reinterpret_cast<int32_t*>(base + L.n_total);
   void* attn_ws = base + L.attn;

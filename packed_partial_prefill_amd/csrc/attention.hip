@@ -422,6 +422,308 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Inference-mode decode kernel: few pairs per KV head (B * G <= 64), the
+// whole cache streamed once, HBM-bound.
+//
+// Workgroup (chunk c, KV head g) owns keys [256c, 256c + 256); each of its 4
+// waves owns one 64-key tile and issues that tile's K and V DMA (32 KB at
+// d = 128) at once, so every CU keeps its workgroup's 128 KB in flight.
+// Queries are read in float32, scaled by log2(e)/sqrt(d) and rounded to bf16
+// on load.  Each wave forms S^T = K Q^T for its tile and all pairs (one or
+// two 32-pair column blocks) as soon as its K slices land (V is still in
+// flight), adds the log2(e)-scaled metadata bias, masks keys past each
+// pair's position, and accumulates O^T = V^T P^T with the same operand
+// layouts as the packed kernel above.  The waves run independently until
+// their 4 (max, sum, O) are merged through LDS; the workgroup writes one
+// partial per pair and k_decode_merge combines the chunks.
+// ---------------------------------------------------------------------------
+constexpr int kDecKeys = 4 * kKvTile;   // keys per workgroup
+constexpr int kDecMaxPairs = 64;
+
+template <int D>
+struct DecLds {
+  static constexpr int kvWave = 2 * kKvTile * D * 2;                 // K and V tile of one wave
+  static constexpr int kv = 4 * kvWave;
+  static constexpr int otRow = D + 4;                                // floats per pair row (padded)
+  static constexpr int ot = 4 * kDecMaxPairs * otRow * 4;            // O of 4 waves
+  static constexpr int body = kv > ot ? kv : ot;
+  static constexpr int ml = 4 * kDecMaxPairs * 2 * 4;
+  static constexpr int total = body + ml;
+};
+
+template <int D, int NCB>
+__global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
+    const float* __restrict__ q, const int32_t* __restrict__ pos, int B, int n_tokens,
+    const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    const uint8_t* __restrict__ flags, int Hq, int Hkv, int G, float q_scale, float bias_local,
+    float bias_sink, float* __restrict__ part_o, float* __restrict__ part_ml) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  using L = DecLds<D>;
+  constexpr int KCH = D / 8;
+  constexpr int ROWS = 1024 / (D * 2);
+  constexpr int KSL = kKvTile / ROWS;              // 1 KB slices per operand per tile
+  constexpr int PAIRS = 32 * NCB;
+  const int c = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int P = B * G;
+  const int u_max = pos[B - 1];
+  if (c * kDecKeys > u_max) return;                // whole chunk in every pair's future
+  const int key0 = c * kDecKeys + wave * kKvTile;
+  const bool active = key0 <= u_max;
+
+  uint8_t* kb = lds + wave * L::kvWave;
+  uint8_t* vb = kb + kKvTile * D * 2;
+  float* ml = reinterpret_cast<float*>(lds + L::body);
+
+  // queries of this lane's pair columns and the flags of key key0 + lane
+  // (issued first, so that one wait below covers them with the K tile)
+  float qv[NCB][D / 16][8];
+  int ucol[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int p = min(cb * 32 + (lane & 31), P - 1);
+    const int r = p / G;
+    const int h = g * G + (p - r * G);
+    ucol[cb] = pos[r];
+    const float* qrow = q + (static_cast<size_t>(r) * Hq + h) * D + 8 * half;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const float4 a = *reinterpret_cast<const float4*>(qrow + ks * 16);
+      const float4 b = *reinterpret_cast<const float4*>(qrow + ks * 16 + 4);
+      qv[cb][ks][0] = a.x; qv[cb][ks][1] = a.y; qv[cb][ks][2] = a.z; qv[cb][ks][3] = a.w;
+      qv[cb][ks][4] = b.x; qv[cb][ks][5] = b.y; qv[cb][ks][6] = b.z; qv[cb][ks][7] = b.w;
+    }
+  }
+  const uint8_t fl = flags[min(key0 + lane, n_tokens - 1)];
+
+  const size_t kv_row = static_cast<size_t>(Hkv) * D;
+  if (active) {
+    const bf16_t* kg = kc + static_cast<size_t>(g) * D;
+    const bf16_t* vg = vc + static_cast<size_t>(g) * D;
+#pragma unroll
+    for (int j = 0; j < KSL; ++j) {   // K slices, then V slices
+      const int row = j * ROWS + lane / KCH;
+      const int key = min(key0 + row, n_tokens - 1);   // rows past the cache are masked
+      __builtin_amdgcn_global_load_lds(KVR_GLB(kg + key * kv_row + kchunk<D>(row, lane % KCH) * 8),
+                                       KVR_LDS(kb + j * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < KSL; ++j) {
+      const int row = j * ROWS + lane / KCH;
+      const int key = min(key0 + row, n_tokens - 1);
+      __builtin_amdgcn_global_load_lds(KVR_GLB(vg + key * kv_row + vchunk(row, lane % KCH) * 8),
+                                       KVR_LDS(vb + j * 1024), 16, 0, 0);
+    }
+  }
+  const float bias_mine =
+      ((fl & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((fl & KVR_FLAG_SINK) ? bias_sink : 0.f);
+
+  bf16x8_t qf[NCB][D / 16];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[cb][ks][i] = static_cast<__bf16>(qv[cb][ks][i] * q_scale);
+
+  const int tr_key = (lane & 15) >> 2;
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  f32x16_t o[NCB][D / 32];
+  float m[NCB], l[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    m[cb] = -INFINITY;
+    l[cb] = 0.f;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) o[cb][db][t] = 0.f;
+  }
+
+  if (active) {
+    // the bias of the 32 keys this lane holds scores for (key kl's flags
+    // were loaded by lane kl)
+    float kbias[2][16];
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+        kbias[sb][t] = __shfl(bias_mine, sb * 32 + 8 * (t >> 2) + 4 * half + (t & 3), 64);
+    attn_wait_vmcnt<KSL>();   // K tile landed (V may still be in flight)
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      f32x16_t s[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s[sb][t] = 0.f;
+        const int key = sb * 32 + (lane & 31);
+#pragma unroll
+        for (int ks = 0; ks < D / 16; ++ks) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+              kb + key * (D * 2) + (kchunk<D>(key, ks * 2 + half) << 4));
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cb][ks], s[sb], 0, 0, 0);
+        }
+        // bias, then keys past the pair's position masked
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int kl = sb * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
+          const float sv = s[sb][t] + kbias[sb][t];
+          s[sb][t] = (key0 + kl <= ucol[cb]) ? sv : -INFINITY;
+        }
+      }
+      float mt = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) mt = fmaxf(mt, s[sb][t]);
+      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      m[cb] = mt;
+      float ls = 0.f;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const float e = mt == -INFINITY ? 0.f : fast_exp2(s[sb][t] - mt);
+          s[sb][t] = e;
+          ls += e;
+        }
+      l[cb] = ls + __shfl_xor(ls, 32, 64);
+      if (cb == 0) attn_wait_vmcnt<0>();   // V tile landed
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          bf16x8_t pb;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[sb][hs * 8 + i]);
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) {
+            s16x4_t x[2];
+#pragma unroll
+            for (int ins = 0; ins < 2; ++ins) {
+              const int key = sb * 32 + hs * 16 + 8 * ins + 4 * half + tr_key;
+              const int d = db * 32 + tr_d;
+              const uint8_t* addr = vb + key * (D * 2) + (vchunk(key, d >> 3) << 4) + (d & 7) * 2;
+              x[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  (__attribute__((address_space(3))) s16x4_t*)(addr));
+            }
+            const s16x4_t x0 = x[0], x1 = x[1];
+            const short av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+            bf16x8_t a;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(__bf16, av[i]);
+            o[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[cb][db], 0, 0, 0);
+          }
+        }
+    }
+  }
+  __syncthreads();   // every wave is done with its K / V tile: the LDS is reused below
+
+  // per-wave (m, l) and O rows [pair][d] (row stride D + 4 floats; each lane
+  // stores its accumulators' 4 consecutive d values as one 16-byte word)
+  float* ot = reinterpret_cast<float*>(lds) + wave * kDecMaxPairs * L::otRow;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    const int col = cb * 32 + (lane & 31);
+    if (half == 0) {
+      ml[(wave * kDecMaxPairs + col) * 2] = m[cb];
+      ml[(wave * kDecMaxPairs + col) * 2 + 1] = l[cb];
+    }
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int t4 = 0; t4 < 4; ++t4) {
+        const int d = db * 32 + 8 * t4 + 4 * half;
+        *reinterpret_cast<float4*>(ot + col * L::otRow + d) =
+            make_float4(o[cb][db][4 * t4], o[cb][db][4 * t4 + 1], o[cb][db][4 * t4 + 2],
+                        o[cb][db][4 * t4 + 3]);
+      }
+  }
+  __syncthreads();
+
+  const int npairs = min(P, PAIRS);
+  const size_t slot0 = (static_cast<size_t>(c) * Hkv + g) * P;
+  const float* ot_all = reinterpret_cast<const float*>(lds);
+  for (int idx = tid; idx < npairs * (D / 4); idx += kAttnThreads) {
+    const int p = idx / (D / 4), d = (idx - p * (D / 4)) * 4;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * kDecMaxPairs + p) * 2]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float ls = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mw = ml[(w * kDecMaxPairs + p) * 2];
+        if (mw == -INFINITY) continue;
+        const float e = fast_exp2(mw - M);
+        ls += e * ml[(w * kDecMaxPairs + p) * 2 + 1];
+        const float4 v = *reinterpret_cast<const float4*>(ot_all + (w * kDecMaxPairs + p) * L::otRow + d);
+        acc.x += e * v.x; acc.y += e * v.y; acc.z += e * v.z; acc.w += e * v.w;
+      }
+    }
+    *reinterpret_cast<float4*>(part_o + (slot0 + p) * D + d) = acc;
+    if (d == 0) {
+      part_ml[(slot0 + p) * 2] = M;
+      part_ml[(slot0 + p) * 2 + 1] = ls;
+    }
+  }
+}
+
+// Combines the chunk partials of one (pair, KV head).  1024 threads: the
+// running maximum is a block reduction over the chunks; then thread (d, sg)
+// accumulates chunks sg, sg + SG, ... (SG = 1024 / D groups, loads unrolled
+// so several are in flight) and the groups are summed through LDS.
+constexpr int kMergeThreads = 1024;
+
+template <int D>
+__global__ __launch_bounds__(kMergeThreads) void k_decode_merge(
+    const float* __restrict__ part_o, const float* __restrict__ part_ml,
+    const int32_t* __restrict__ pos, int B, int Hq, int Hkv, int G, float* __restrict__ o) {
+  constexpr int SG = kMergeThreads / D;
+  __shared__ float red[kMergeThreads];
+  __shared__ float redl[kMergeThreads];
+  const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const int P = B * G;
+  const int ns = pos[B - 1] / kDecKeys + 1;        // chunks that wrote partials
+  const size_t stride = static_cast<size_t>(Hkv) * P;   // slots between chunks
+  const size_t slot0 = static_cast<size_t>(g) * P + p;
+  float M = -INFINITY;
+  for (int s = tid; s < ns; s += kMergeThreads) M = fmaxf(M, part_ml[(slot0 + s * stride) * 2]);
+  red[tid] = M;
+  __syncthreads();
+  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
+    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
+    __syncthreads();
+  }
+  M = red[0];
+  __syncthreads();
+  const int d = tid % D, sg = tid / D;
+  float acc = 0.f, l = 0.f;
+#pragma unroll 4
+  for (int s = sg; s < ns; s += SG) {
+    const size_t slot = slot0 + s * stride;
+    const float ms = part_ml[slot * 2];
+    const float e = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
+    l += e * part_ml[slot * 2 + 1];
+    acc += e * part_o[slot * D + d];
+  }
+  red[tid] = acc;
+  redl[tid] = l;
+  __syncthreads();
+  if (sg == 0) {
+#pragma unroll
+    for (int j = 1; j < SG; ++j) {
+      acc += red[tid + j * D];
+      l += redl[tid + j * D];
+    }
+    const int r = p / G, h = g * G + (p - r * G);
+    o[(static_cast<size_t>(r) * Hq + h) * D + d] = acc / l;
+  }
+}
+
 // KV tiles per split: 32 (2048 keys) when the launch has plenty of
 // workgroups; halved (down to 4) while the grid has fewer than 1024, so that
 // small packed sets (few query tiles) still spread over every CU.  Roughly
@@ -435,6 +737,15 @@ int attn_split_tiles(int B, int n_tokens, const Shape& sh) {
 }
 
 }  // namespace
+
+bool decode_supported(kvr_dtype dt, int B, const Shape& sh) {
+  return dt == KVR_BF16 && B >= 1 && static_cast<long>(B) * sh.group <= kDecMaxPairs;
+}
+
+size_t decode_workspace_bytes(int B, int n_tokens, const Shape& sh) {
+  const size_t chunks = (n_tokens + kDecKeys - 1) / kDecKeys;
+  return chunks * sh.hkv * B * sh.group * (sh.d + 2) * sizeof(float);
+}
 
 size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh) {
   if (dt != KVR_BF16) return 0;
@@ -489,6 +800,69 @@ hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_t
   return hipGetLastError();
 }
 }  // namespace
+
+namespace {
+template <int D, int NCB>
+hipError_t launch_decode_t(const float* q, const int32_t* pos, int B, int n_tokens,
+                           const void* k_cache, const void* v_cache, const uint8_t* flags,
+                           const Shape& sh, float alpha, float beta, void* ws, float* o,
+                           hipStream_t stream) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_decode<D, NCB>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       DecLds<D>::total);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  const int chunks = (n_tokens + kDecKeys - 1) / kDecKeys;
+  const int P = B * sh.group;
+  float* part_o = static_cast<float*>(ws);
+  float* part_ml = part_o + static_cast<size_t>(chunks) * sh.hkv * P * sh.d;
+  const float log2e = 1.4426950408889634f;
+  hipLaunchKernelGGL((k_attn_decode<D, NCB>), dim3(chunks, sh.hkv), dim3(kAttnThreads),
+                     DecLds<D>::total, stream, q, pos, B, n_tokens,
+                     static_cast<const bf16_t*>(k_cache), static_cast<const bf16_t*>(v_cache),
+                     flags, sh.hq, sh.hkv, sh.group, log2e / sqrtf(static_cast<float>(D)),
+                     alpha * log2e, beta * log2e, part_o, part_ml);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_decode_merge_t(const int32_t* pos, int B, int n_tokens, const Shape& sh,
+                                 void* ws, float* o, hipStream_t stream) {
+  const int chunks = (n_tokens + kDecKeys - 1) / kDecKeys;
+  const int P = B * sh.group;
+  const float* part_o = static_cast<const float*>(ws);
+  const float* part_ml = part_o + static_cast<size_t>(chunks) * sh.hkv * P * sh.d;
+  hipLaunchKernelGGL(k_decode_merge<D>, dim3(P, sh.hkv), dim3(kMergeThreads), 0, stream, part_o,
+                     part_ml, pos, B, sh.hq, sh.hkv, sh.group, o);
+  return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_attention_decode_merge(const int32_t* pos, int B, int n_tokens,
+                                         const Shape& sh, void* ws, float* o,
+                                         hipStream_t stream) {
+  if (sh.d == 128) return launch_decode_merge_t<128>(pos, B, n_tokens, sh, ws, o, stream);
+  return launch_decode_merge_t<64>(pos, B, n_tokens, sh, ws, o, stream);
+}
+
+hipError_t launch_attention_decode(const float* q, const int32_t* pos, int B, int n_tokens,
+                                   const void* k_cache, const void* v_cache,
+                                   const uint8_t* flags, const Shape& sh, float alpha, float beta,
+                                   void* ws, float* o, hipStream_t stream) {
+  const bool two = B * sh.group > 32;
+  if (sh.d == 128)
+    return two ? launch_decode_t<128, 2>(q, pos, B, n_tokens, k_cache, v_cache, flags, sh, alpha,
+                                         beta, ws, o, stream)
+               : launch_decode_t<128, 1>(q, pos, B, n_tokens, k_cache, v_cache, flags, sh, alpha,
+                                         beta, ws, o, stream);
+  return two ? launch_decode_t<64, 2>(q, pos, B, n_tokens, k_cache, v_cache, flags, sh, alpha,
+                                      beta, ws, o, stream)
+             : launch_decode_t<64, 1>(q, pos, B, n_tokens, k_cache, v_cache, flags, sh, alpha,
+                                      beta, ws, o, stream);
+}
 
 // Scale folded into Q by the RoPE kernel for the MFMA path.
 float attention_q_scale(kvr_dtype dt, int head_dim) {

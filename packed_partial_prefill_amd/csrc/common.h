@@ -12,12 +12,10 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// Round-to-nearest-even float32 -> bfloat16 (NaN stays a quiet NaN).
+// Round-to-nearest-even float32 -> bfloat16 (NaN stays NaN): the language
+// conversion, which gfx950 performs with v_cvt_pk_bf16_f32 (no branches).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
 }
 
 // Storage traits: float32 or bfloat16 elements, float32 arithmetic.

@@ -103,6 +103,18 @@ hipError_t launch_attention(kvr_dtype dt, const void* q, const void* k_cache,
                             const int32_t* plan_n_full, const int32_t* plan_n_total, void* ws,
                             void* o_out, hipStream_t stream);
 bool attention_needs_merge(kvr_dtype dt);
+// Inference-mode decode path (bf16, B * group <= 64 pairs per KV head):
+// float32 queries in; chunk partials in ws, then the merge writes float32
+// o [B, Hq, d].
+bool decode_supported(kvr_dtype dt, int B, const Shape& sh);
+size_t decode_workspace_bytes(int B, int n_tokens, const Shape& sh);
+hipError_t launch_attention_decode(const float* q, const int32_t* pos, int B, int n_tokens,
+                                   const void* k_cache, const void* v_cache,
+                                   const uint8_t* flags, const Shape& sh, float alpha, float beta,
+                                   void* ws, float* o, hipStream_t stream);
+hipError_t launch_attention_decode_merge(const int32_t* pos, int B, int n_tokens,
+                                         const Shape& sh, void* ws, float* o,
+                                         hipStream_t stream);
 // o_out: [B, Hq, d] in bf16, or float32 when out_f32.
 hipError_t launch_attention_merge(kvr_dtype dt, int B, int n_tokens, const Shape& sh,
                                   const int32_t* plan_n_total, void* ws, void* o_out,

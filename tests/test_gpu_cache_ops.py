@@ -73,6 +73,18 @@ def test_inference_alpha_beta_zero_without_metadata_is_plain_attention():
     run_inference(w, np.arange(0, 300, 7))
 
 
+@pytest.mark.parametrize("hq,hkv,d,n,pos", [
+    (8, 2, 64, 1000, [5, 300, 999]),                 # d = 64, ragged last chunk
+    (32, 8, 128, 2048, list(range(2040, 2048))),     # 32 pairs: one column block
+    (32, 8, 128, 2048, list(range(2039, 2048))),     # 36 pairs: two column blocks
+    (28, 4, 128, 4096, [100, 3000]),                 # chunks past the last query skipped
+    (8, 8, 128, 513, list(range(0, 513, 9))),        # G = 1, 58 pairs
+])
+def test_inference_decode_path_shapes(hq, hkv, d, n, pos):
+    w = _small(f"inf-decode-{hq}-{hkv}-{d}-{n}", 205, "bf16", hq, hkv, d, n, 128)
+    run_inference(w, np.asarray(pos))
+
+
 @pytest.mark.parametrize("B", [1, 8])
 def test_inference_qwen7_decode_16k(B):
     w = wl.QWEN7_DECODE_16K
