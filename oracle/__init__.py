@@ -19,9 +19,13 @@ Sources (cited by title and section; no line numbers):
   inference mode without write-back and its degeneration (section 6.4).
 * "Budgeted KV-Cache Repair" section 7.1, Eq. 2: the Shift operation
   (positional correction of the retained suffix after a deletion).
+* "Budgeted KV-Cache Repair" sections 3.2 and 7.3 (Eq. 1 / 7, Eq. 8,
+  Algorithm 1): the numeric core of Semantic-Unit Refresh (token relevance,
+  unit scores and ranking, exact-budget fill, forward-envelope window).
 
 Arithmetic is float64 throughout (inputs are widened from their float32 /
-bf16 storage).  Matrix products use numpy's matmul as a library step; there
+bf16 storage), except Semantic-Unit Refresh scoring, which the page fixes
+to float32.  Matrix products use numpy's matmul as a library step; there
 is no blocking, fusion or reordering beyond the definitions.
 
 Where the pages are silent, the reading taken is stated in the docstring of
@@ -33,10 +37,11 @@ from .repair_set import (BadBlocks, BadSupport, attn_tile_plan, budget, check_su
 from .layer import (FLAG_LOCAL, FLAG_SINK, attention_bias, biased_attention_row,
                     interval_major, layer_repair, rms_norm, rope, silu, stack_repair)
 from .cache_ops import inference_attention, shift_cache
+from . import sur
 
 __all__ = [
     "BadBlocks", "BadSupport", "attn_tile_plan", "budget", "check_support", "runs",
     "seam_set", "validate_blocks", "FLAG_LOCAL", "FLAG_SINK", "attention_bias",
     "biased_attention_row", "interval_major", "layer_repair", "rms_norm", "rope", "silu",
-    "stack_repair", "inference_attention", "shift_cache",
+    "stack_repair", "inference_attention", "shift_cache", "sur",
 ]
