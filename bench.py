@@ -15,6 +15,7 @@ stdout; progress goes to stderr.
     python bench.py --table18                              # packed vs interval-wise sweep
     python bench.py --op inference                         # inference-mode F at decode sizes
     python bench.py --op shift                             # Shift over the 28-layer 7B cache
+    python bench.py --op sur                               # SUR scoring + selection, 16K suffix
 """
 from __future__ import annotations
 
@@ -321,6 +322,47 @@ def run_shift_bench(a) -> int:
     return 0
 
 
+def run_sur_bench(a) -> int:
+    """Semantic-Unit Refresh numeric core (Budgeted KV-Cache Repair, 7.3):
+    token relevance over the 16K suffix against a Qwen2.5-7B-sized bf16
+    embedding table (the gathered rows dominate the traffic), then the
+    exact-budget selection.  Infinity Cache flushed before every trial."""
+    import torch
+    import packed_partial_prefill_amd as kvr
+    w = wl.SUR_QWEN7_16K
+    log(f"[bench] {w.name}: generating the embedding table")
+    dE = torch.from_numpy(wl.embedding_table(w)).to(torch.bfloat16).cuda()
+    s, q, starts = wl.sur_ids(w)
+    ds, dq = torch.from_numpy(s).cuda(), torch.from_numpy(q).cuda()
+    dus = torch.from_numpy(starts).cuda()
+    S, U, B = len(s), len(starts), wl.sur_budget(w)
+    r = torch.empty(S, dtype=torch.float32, device="cuda")
+    uscore = torch.empty(U, dtype=torch.float32, device="cuda")
+    T = torch.empty(B, dtype=torch.int32, device="cuda")
+    rs, rl = torch.empty_like(T), torch.empty_like(T)
+    counts = torch.empty(4, dtype=torch.int32, device="cuda")
+    ws = torch.empty(2 * S, dtype=torch.float32, device="cuda")
+    score = lambda: kvr.kvr_sur_scores(dE, kvr.KVR_BF16, ds, dq, r)
+    select = lambda: kvr.kvr_sur_select(r, dus, B, w.pos0, uscore, T, rs, rl, counts, ws,
+                                        sync=False)
+    us_score = _event_trials(torch, score, a.steps, a.warmup, flush_bytes=512 << 20)
+    us_select = _event_trials(torch, select, a.steps, a.warmup, flush_bytes=512 << 20)
+    both = lambda: (score(), select())
+    us_both = _event_trials(torch, both, a.steps, a.warmup, flush_bytes=512 << 20)
+    row_bytes = w.hidden * 2
+    nbytes = S * row_bytes + len(q) * row_bytes + S * 4
+    gbs = nbytes / (us_score * 1e-6) / 1e9
+    flops = 2.0 * S * len(q) * w.hidden
+    print(json.dumps({"op": "sur", "workload": w.name, "vocab": w.vocab, "hidden": w.hidden,
+                      "S": S, "Q": len(q), "units": U, "budget": B,
+                      "us_scores": round(us_score, 2), "us_select": round(us_select, 2),
+                      "us_total": round(us_both, 2), "scores_hbm_gbps": round(gbs, 1),
+                      "scores_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+                      "scores_tflops": round(flops / (us_score * 1e-6) / 1e12, 2),
+                      "bytes": nbytes, "flush": "512 MiB written before each trial"}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -329,7 +371,7 @@ def main(argv=None) -> int:
     ap.add_argument("--workload", default=wl.QWEN7_LAYER_SEAMS.name, choices=sorted(wl.WORKLOADS))
     ap.add_argument("--schedule", default="packed", choices=("packed", "interval"))
     ap.add_argument("--table18", action="store_true")
-    ap.add_argument("--op", default="repair", choices=("repair", "inference", "shift"),
+    ap.add_argument("--op", default="repair", choices=("repair", "inference", "shift", "sur"),
                     help="repair (default, the one-line contract), or the inference-mode "
                          "attention / Shift measurements (JSON lines)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -350,6 +392,8 @@ def main(argv=None) -> int:
         return run_inference_bench(a)
     if a.op == "shift":
         return run_shift_bench(a)
+    if a.op == "sur":
+        return run_sur_bench(a)
 
     w = wl.WORKLOADS[a.workload]
     log(f"[bench] workload {w.name}: generating inputs")

@@ -297,6 +297,66 @@ kvr_status kvr_shift_cache(const kvr_config* cfg, int32_t n_layers, const kvr_kv
                            int32_t del_start, int32_t del_len, uint8_t mark,
                            hipStream_t stream);
 
+/*
+ * kvr_sur_scores - token relevance of Semantic-Unit Refresh (Budgeted
+ * KV-Cache Repair, section 3.2, Eq. 1, and section 7.3, Eq. 7), in float32
+ * as the page prescribes for normalisation and cosine scoring:
+ *
+ *   r[i] = max_{j < Q} <E[s_i], E[q_j]> / (||E[s_i]||_2 ||E[q_j]||_2)
+ *          + 0.25 * 1[s_i occurs among the query ids]
+ *
+ * A zero-norm row scores cosine 0.  bf16 tables are contracted on the MFMA
+ * (products exact in float32, float32 sums); float32 tables in float32 FMA.
+ *
+ *   d_E           device [vocab, hidden] embedding table in `dtype`.
+ *   d_suffix_ids  device int32 [S]: token ids of the retained suffix.
+ *   d_query_ids   device int32 [Q], 1 <= Q <= 256.
+ *   d_r           device float32 [S] out.  A token id outside [0, vocab)
+ *                 gives r = NaN for that token (no row is read out of range).
+ * Errors (before any device work): null or misaligned (16-byte) pointers,
+ * vocab < 1, S < 0, Q outside [1, 256] -> INVALID_ARGUMENT; hidden not a
+ * positive multiple of 64, or above 8192 for a float32 table -> UNSUPPORTED.
+ * S = 0 is a successful no-op.
+ */
+kvr_status kvr_sur_scores(const void* d_E, kvr_dtype dtype, int32_t vocab, int32_t hidden,
+                          const int32_t* d_suffix_ids, int32_t S, const int32_t* d_query_ids,
+                          int32_t Q, float* d_r, hipStream_t stream);
+
+/*
+ * kvr_sur_select - the selection of Semantic-Unit Refresh under an exact
+ * budget (Budgeted KV-Cache Repair, section 7.3 and Algorithm 1, steps
+ * 5-9): each unit scores the mean of its four largest token scores (all of
+ * them below four); units are ranked by score, the earlier unit winning a
+ * tie; whole units are admitted in ranked order while they fit the
+ * remaining allowance w = budget - |A|; the first that does not fit
+ * contributes the width-w window with the largest sum of the forward-decay
+ * envelope u_t = max(e^(r_t - r_max), e^(-1/16) u_{t-1}), u_0 = 0 (Eq. 8),
+ * the earliest on ties, which fills the allowance exactly; the chosen
+ * positions are sorted and coalesced into runs.
+ *
+ *   d_r            device float32 [S] token scores (kvr_sur_scores).
+ *   d_unit_start   device int32 [n_units]: the suffix partition into units,
+ *                  unit u = [start[u], start[u+1]) with start[n_units] = S.
+ *                  start[0] = 0 and strictly increasing below S, checked on
+ *                  the device (KVR_ERR_BAD_BLOCKS in counts[2]).
+ *   budget         |A|, 0 <= budget <= S (the exact budget of Eq. 3 is the
+ *                  caller's: min(S, ceil(S * b / 100))).
+ *   pos0           global position of suffix token 0: T holds pos0 + i.
+ *   d_unit_scores  device float32 [n_units] out: the unit scores.
+ *   out            T, run_start, run_len: device int32 [cap] each; counts:
+ *                  device int32 [3] = (|T|, R, status); cap >= budget.
+ *   d_ws           device workspace of at least 2 * S floats.
+ *   h_counts       host int32 [3] or NULL: when given the call synchronises
+ *                  the stream, copies counts and returns their status.
+ * Errors (before any device work): null or misaligned pointers, S < 1,
+ * n_units outside [1, S], budget outside [0, S], cap < budget, ws_bytes too
+ * small -> INVALID_ARGUMENT / WORKSPACE; n_units > 8192 -> UNSUPPORTED.
+ */
+kvr_status kvr_sur_select(const float* d_r, int32_t S, const int32_t* d_unit_start,
+                          int32_t n_units, int32_t budget, int32_t pos0, float* d_unit_scores,
+                          const kvr_repair_set* out, float* d_ws, size_t ws_bytes,
+                          int32_t* h_counts, hipStream_t stream);
+
 /* Human-readable name of a status. */
 const char* kvr_status_string(kvr_status s);
 /* Detail of the last error returned on the calling thread ("" if none). */
@@ -324,7 +384,9 @@ enum {
   KVR_KERNEL_FINAL = 9,     /* last residual sum into x_out                */
   KVR_KERNEL_QPREP = 10,    /* query scaling (kvr_biased_attention)        */
   KVR_KERNEL_SHIFT = 11,    /* Shift re-rotation / move (kvr_shift_cache)  */
-  KVR_KERNEL_COUNT = 12
+  KVR_KERNEL_SUR_SCORE = 12,/* SUR token relevance (kvr_sur_scores)        */
+  KVR_KERNEL_SUR_SELECT = 13,/* SUR unit scores + selection (kvr_sur_select) */
+  KVR_KERNEL_COUNT = 14
 };
 kvr_status kvr_timing_begin(uint32_t mask);
 kvr_status kvr_timing_end(double* total_ms, int32_t* launches);

@@ -27,7 +27,7 @@ KVR_FLAG_LOCAL, KVR_FLAG_SINK = 1, 2
 KVR_SEAM_ASYMMETRIC, KVR_INIT_META = 1, 2
 KVR_ATTN_QROWS, KVR_ATTN_KV_TILE = 128, 64
 KERNEL_NAMES = ["plan", "norm", "qkv", "rope", "attn", "attn_merge", "oproj", "gateup", "down",
-                "final", "qprep", "shift"]
+                "final", "qprep", "shift", "sur_score", "sur_select"]
 KVR_KERNEL_COUNT = len(KERNEL_NAMES)
 
 
@@ -86,6 +86,9 @@ _sigs = {
                                        C.c_size_t, _P]),
     "kvr_shift_cache": (C.c_int, [C.POINTER(kvr_config), _I, C.POINTER(kvr_kv), C.POINTER(kvr_kv),
                                   _P, _P, _P, _P, _I, _I, _I, C.c_uint8, _P]),
+    "kvr_sur_scores": (C.c_int, [_P, C.c_int, _I, _I, _P, _I, _P, _I, _P, _P]),
+    "kvr_sur_select": (C.c_int, [_P, _I, _P, _I, _I, _I, _P, C.POINTER(kvr_repair_set), _P,
+                                 C.c_size_t, _P, _P]),
     "kvr_status_string": (C.c_char_p, [C.c_int]),
     "kvr_last_error": (C.c_char_p, []),
     "kvr_timing_begin": (C.c_int, [C.c_uint32]),
@@ -243,6 +246,27 @@ def kvr_shift_cache(cfg: Config, src: Sequence[Tuple], dst: Sequence[Tuple], del
     _check(_lib.kvr_shift_cache(C.byref(c), L, s_arr, d_arr, _ptr(flags_src), _ptr(flags_dst),
                                 _ptr(block_src), _ptr(block_dst), src[0][0].shape[0], del_start,
                                 del_len, mark, _stream(stream)))
+
+
+def kvr_sur_scores(E, dtype: int, suffix_ids, query_ids, r, stream=None) -> None:
+    """Eq. 7 token relevance: r [S] (float32) from the embedding table E
+    [vocab, hidden] (bf16 or float32, `dtype`)."""
+    _check(_lib.kvr_sur_scores(_ptr(E), dtype, E.shape[0], E.shape[1], _ptr(suffix_ids),
+                               suffix_ids.numel(), _ptr(query_ids), query_ids.numel(), _ptr(r),
+                               _stream(stream)))
+
+
+def kvr_sur_select(r, unit_start, budget: int, pos0: int, unit_scores, T, run_start, run_len,
+                   counts, ws, sync: bool = True, stream=None) -> Optional[Tuple[int, int, int]]:
+    """Algorithm 1 steps 5-9: returns (|T|, R, status) when ``sync``."""
+    out = kvr_repair_set(_ptr(T), _ptr(run_start), _ptr(run_len), _ptr(counts), T.numel())
+    h = (C.c_int32 * 3)() if sync else None
+    _check(_lib.kvr_sur_select(_ptr(r), r.numel(), _ptr(unit_start), unit_start.numel(), budget,
+                               pos0, _ptr(unit_scores), C.byref(out), _ptr(ws),
+                               ws.numel() * ws.element_size(),
+                               C.cast(h, C.c_void_p) if h is not None else None,
+                               _stream(stream)))
+    return (h[0], h[1], h[2]) if h is not None else None
 
 
 def kvr_status_string(st: int) -> str:

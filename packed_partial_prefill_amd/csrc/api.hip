@@ -517,6 +517,62 @@ kvr_status kvr_shift_cache(const kvr_config* cfg, int32_t n_layers, const kvr_kv
   return KVR_OK;
 }
 
+kvr_status kvr_sur_scores(const void* d_E, kvr_dtype dtype, int32_t vocab, int32_t hidden,
+                          const int32_t* d_suffix_ids, int32_t S, const int32_t* d_query_ids,
+                          int32_t Q, float* d_r, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (dtype != KVR_F32 && dtype != KVR_BF16)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(dtype));
+  if (vocab < 1 || S < 0 || Q < 1 || Q > kvr::kSurMaxQuery)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "vocab=%d, S=%d, Q=%d (1 <= Q <= %d)", vocab, S, Q,
+                kvr::kSurMaxQuery);
+  if (hidden <= 0 || hidden % 64 || (dtype == KVR_F32 && hidden > 8192))
+    return fail(KVR_ERR_UNSUPPORTED, "hidden=%d (a positive multiple of 64; <= 8192 for float32)",
+                hidden);
+  if (S == 0) return KVR_OK;
+  if (!dev_ok(d_E) || !dev_ok(d_suffix_ids) || !dev_ok(d_query_ids) || !dev_ok(d_r))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "pointers must be non-NULL and 16-byte aligned");
+  KVR_RUN(KVR_KERNEL_SUR_SCORE, stream, "sur scores",
+          kvr::launch_sur_scores(dtype, d_E, vocab, hidden, d_suffix_ids, S, d_query_ids, Q, d_r,
+                                 stream));
+  return KVR_OK;
+}
+
+kvr_status kvr_sur_select(const float* d_r, int32_t S, const int32_t* d_unit_start,
+                          int32_t n_units, int32_t budget, int32_t pos0, float* d_unit_scores,
+                          const kvr_repair_set* out, float* d_ws, size_t ws_bytes,
+                          int32_t* h_counts, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (S < 1 || n_units < 1 || n_units > S || budget < 0 || budget > S || pos0 < 0)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "S=%d, n_units=%d, budget=%d, pos0=%d", S, n_units,
+                budget, pos0);
+  if (n_units > kvr::kSurMaxUnitCount)
+    return fail(KVR_ERR_UNSUPPORTED, "n_units=%d > %d", n_units, kvr::kSurMaxUnitCount);
+  if (!dev_ok(d_r) || !dev_ok(d_unit_start) || !dev_ok(d_unit_scores) || !dev_ok(d_ws))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "pointers must be non-NULL and 16-byte aligned");
+  if (!out || !dev_ok(out->T) || !dev_ok(out->run_start) || !dev_ok(out->run_len) ||
+      !dev_ok(out->counts) || out->cap < budget)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "outputs NULL, misaligned or cap < budget");
+  if (ws_bytes < 2 * sizeof(float) * static_cast<size_t>(S))
+    return fail(KVR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes,
+                2 * sizeof(float) * static_cast<size_t>(S));
+  KVR_RUN(KVR_KERNEL_SUR_SELECT, stream, "sur select",
+          kvr::launch_sur_select(d_r, S, d_unit_start, n_units, d_unit_scores, budget, pos0, d_ws,
+                                 out->T, out->run_start, out->run_len, out->counts, out->cap,
+                                 stream));
+  if (!h_counts) return KVR_OK;
+  hipError_t e = hipMemcpyAsync(h_counts, out->counts, 3 * sizeof(int32_t),
+                                hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy counts");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "synchronize");
+  if (h_counts[2] == KVR_ERR_BAD_BLOCKS)
+    return fail(KVR_ERR_BAD_BLOCKS, "unit starts do not partition [0, S)");
+  if (h_counts[2] != KVR_OK)
+    return fail(static_cast<kvr_status>(h_counts[2]), "selection failed (|T| = %d)", h_counts[0]);
+  return KVR_OK;
+}
+
 const char* kvr_status_string(kvr_status s) {
   switch (s) {
     case KVR_OK: return "KVR_OK";

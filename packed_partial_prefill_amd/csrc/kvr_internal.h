@@ -95,6 +95,18 @@ hipError_t launch_shift_meta(const uint8_t* f_src, uint8_t* f_dst, const int32_t
                              int32_t* b_dst, int n_out, int del_start, int del_len, uint8_t mark,
                              hipStream_t stream);
 
+// ---- sur.hip ------------------------------------------------------------------
+constexpr int kSurMaxQuery = 256;
+constexpr int kSurMaxUnitCount = 8192;
+hipError_t launch_sur_scores(kvr_dtype dt, const void* E, int vocab, int hidden,
+                             const int32_t* sid, int S, const int32_t* qid, int Q, float* r,
+                             hipStream_t stream);
+// ws: 2 * S floats (envelope and window sums of the unit that takes a window)
+hipError_t launch_sur_select(const float* r, int S, const int32_t* ustart, int U,
+                             float* uscore, int budget, int pos0, float* ws, int32_t* T,
+                             int32_t* run_start, int32_t* run_len, int32_t* counts, int cap,
+                             hipStream_t stream);
+
 // ---- attention.hip ----------------------------------------------------------
 size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh);
 hipError_t launch_attention(kvr_dtype dt, const void* q, const void* k_cache,

@@ -23,6 +23,7 @@ def test_header_declares_the_entry_points():
     for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
               "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
               "kvr_attention_workspace_bytes", "kvr_biased_attention", "kvr_shift_cache",
+              "kvr_sur_scores", "kvr_sur_select",
               "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
         assert n in names
 
@@ -135,6 +136,7 @@ def test_python_binding_has_the_c_names(kvr):
     for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
               "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
               "kvr_attention_workspace_bytes", "kvr_biased_attention", "kvr_shift_cache",
+              "kvr_sur_scores", "kvr_sur_select",
               "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
         assert callable(getattr(kvr, n))
 
@@ -201,3 +203,37 @@ def test_shift_cache_host_validation(kvr):
     dst = [(FAKE + (8 << 16), FAKE + (9 << 16)), (FAKE + (1 << 16) + 512, FAKE + (10 << 16))]
     assert _shift(kvr, src=src, dst=dst) == -1
     assert _shift(kvr, n_tokens=5, a=0, d=5) == 0          # nothing left: no device work
+
+
+def test_sur_scores_host_validation(kvr):
+    lib = kvr.lib()
+    f = lambda dt=1, V=100, H=128, S=10, Q=4, E=FAKE, r=FAKE + 4096: lib.kvr_sur_scores(
+        E, dt, V, H, FAKE, S, FAKE, Q, r, None)
+    assert f(dt=5) == -1
+    assert f(V=0) == -1
+    assert f(S=-1) == -1
+    assert f(Q=0) == -1
+    assert f(Q=257) == -1
+    assert f(H=100) == -2
+    assert f(dt=0, H=8256) == -2                            # float32 rows > 8192
+    assert f(E=None) == -1
+    assert f(r=FAKE + 4) == -1
+    assert f(S=0) == 0
+
+
+def test_sur_select_host_validation(kvr):
+    lib = kvr.lib()
+    out = kvr.kvr_repair_set(FAKE, FAKE, FAKE, FAKE, 64)
+    def f(S=100, U=5, B=10, pos0=0, ws_bytes=800, out=out, us=FAKE):
+        return lib.kvr_sur_select(FAKE, S, us, U, B, pos0, FAKE, C.byref(out), FAKE, ws_bytes,
+                                  None, None)
+    assert f(S=0) == -1
+    assert f(U=0) == -1
+    assert f(U=101) == -1                                   # more units than tokens
+    assert f(B=-1) == -1
+    assert f(B=101) == -1
+    assert f(pos0=-3) == -1
+    assert f(us=None) == -1
+    assert f(out=kvr.kvr_repair_set(FAKE, FAKE, FAKE, FAKE, 5)) == -1   # cap < budget
+    assert f(ws_bytes=799) == -6
+    assert f(S=10000, U=9000, B=10) == -2                   # too many units for the ranking

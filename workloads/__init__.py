@@ -365,3 +365,68 @@ def random_partition(rng: np.random.Generator, n_tokens: int, m: int) -> Tuple[n
     s = np.concatenate([[0], cuts]).astype(np.int32)
     e = np.concatenate([cuts, [n_tokens]]).astype(np.int32)
     return s, e
+
+
+# ----------------------------------------------------------------------------
+# Semantic-Unit Refresh scoring inputs
+# ----------------------------------------------------------------------------
+T_EMBED, T_SUR_IDS = 32, 33
+
+
+@dataclass(frozen=True)
+class SurWorkload:
+    """Synthetic stand-in for SUR's inputs (Budgeted KV-Cache Repair, 7.3):
+    a frozen embedding table, the retained suffix's token ids, the query's
+    token ids and the suffix's partition into units.  Units have lengths in
+    [8, 128], the range the page's split / merge rules leave."""
+    name: str
+    cfg_id: int
+    vocab: int
+    hidden: int
+    n_suffix: int
+    n_query: int
+    budget_percent: float
+    dtype: str = "bf16"
+    pos0: int = 0
+
+
+SUR_TINY = SurWorkload("sur-tiny-f32", 40, vocab=300, hidden=128, n_suffix=700, n_query=5,
+                       budget_percent=10.0, dtype="f32", pos0=64)
+SUR_QWEN7_16K = SurWorkload("sur-qwen2.5-7b-16k", 41, vocab=152064, hidden=3584, n_suffix=16384,
+                            n_query=48, budget_percent=5.0, pos0=0)
+SUR_WORKLOADS = {w.name: w for w in (SUR_TINY, SUR_QWEN7_16K)}
+
+
+def embedding_table(w: SurWorkload, threads: Optional[int] = None) -> np.ndarray:
+    """[vocab, hidden] ~ N(0, 1), bf16-rounded for bf16 workloads."""
+    n = w.vocab * w.hidden
+    out = np.empty(n, dtype=np.float32)
+    _normal_chunks((SEED_ROOT, w.cfg_id, 0, T_EMBED), n, out,
+                   threads if threads is not None else default_threads(), 1.0, 0.0,
+                   w.dtype == "bf16")
+    return out.reshape(w.vocab, w.hidden)
+
+
+def sur_ids(w: SurWorkload) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """(suffix ids [S], query ids [Q], unit starts): uniform token ids; half
+    of the query tokens are copied from the suffix (so some suffix tokens
+    occur in the query); unit lengths uniform in [8, 128]."""
+    g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
+        [SEED_ROOT, w.cfg_id, 0, T_SUR_IDS])))
+    s = g.integers(0, w.vocab, size=w.n_suffix, dtype=np.int64).astype(np.int32)
+    q = g.integers(0, w.vocab, size=w.n_query, dtype=np.int64).astype(np.int32)
+    k = w.n_query // 2
+    q[:k] = s[g.choice(w.n_suffix, size=k, replace=False)]
+    starts = [0]
+    while True:
+        nxt = starts[-1] + int(g.integers(8, 129))
+        if nxt >= w.n_suffix:
+            break
+        starts.append(nxt)
+    return s, q, np.array(starts, dtype=np.int32)
+
+
+def sur_budget(w: SurWorkload) -> int:
+    """Exact budget B(S, b) = min(S, ceil(S * b / 100)) (Eq. 3), in integers."""
+    num = w.n_suffix * int(round(w.budget_percent * 1000))
+    return min(w.n_suffix, -(-num // 100000))
