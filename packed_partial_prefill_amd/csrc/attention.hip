@@ -121,13 +121,18 @@ struct AttnLds {
 
 // Physical 16-byte chunk of logical chunk c in key row k.  K rows: c ^ (k & 15)
 // (d = 128) or c ^ ((k & 7) ^ ((k >> 3) & 1)) (d = 64), so the 32 rows of an
-// MFMA operand read hit distinct bank slots.  V rows: c ^ (2 * (k & 3)), so
-// the 4 rows x 2 chunks a 16-lane transposing read touches are distinct.
+// MFMA operand read hit distinct bank slots.  V rows (d = 128): c ^ (4 (k & 3)),
+// which measures no bank conflicts for the transposing reads on gfx950
+// (rocprofv3 SQ_LDS_BANK_CONFLICT; c ^ (2 (k & 3)) measured 2-way); d = 64
+// keeps c ^ (2 (k & 3)) within its 8 chunks.
 template <int D>
 __device__ __forceinline__ int kchunk(int key, int c) {
   return c ^ ((D == 128) ? (key & 15) : ((key & 7) ^ ((key >> 3) & 1)));
 }
-__device__ __forceinline__ int vchunk(int key, int c) { return c ^ (2 * (key & 3)); }
+template <int D>
+__device__ __forceinline__ int vchunk(int key, int c) {
+  return c ^ ((D == 128) ? ((key & 3) << 2) : (2 * (key & 3)));
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
     const bool isv = sl >= KSL;
     const int row = (isv ? sl - KSL : sl) * ROWS + lane / KCH;
     const int phys = lane % KCH;
-    const int logical = isv ? vchunk(row, phys) : kchunk<D>(row, phys);   // involutions
+    const int logical = isv ? vchunk<D>(row, phys) : kchunk<D>(row, phys);   // involutions
     s_isv[j] = isv;
     s_row[j] = row;
     s_col[j] = logical * 8;
@@ -336,7 +341,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
           for (int ins = 0; ins < 2; ++ins) {
             const int key = sb * 32 + hs * 16 + 8 * ins + 4 * half + tr_key;
             const int d = db * 32 + tr_d;
-            const uint8_t* addr = vb + key * (D * 2) + (vchunk(key, d >> 3) << 4) + (d & 7) * 2;
+            const uint8_t* addr = vb + key * (D * 2) + (vchunk<D>(key, d >> 3) << 4) + (d & 7) * 2;
             x[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4_t*)(addr));
           }
@@ -512,7 +517,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
     for (int j = 0; j < KSL; ++j) {
       const int row = j * ROWS + lane / KCH;
       const int key = min(key0 + row, n_tokens - 1);
-      __builtin_amdgcn_global_load_lds(KVR_GLB(vg + key * kv_row + vchunk(row, lane % KCH) * 8),
+      __builtin_amdgcn_global_load_lds(KVR_GLB(vg + key * kv_row + vchunk<D>(row, lane % KCH) * 8),
                                        KVR_LDS(vb + j * 1024), 16, 0, 0);
     }
   }
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
             for (int ins = 0; ins < 2; ++ins) {
               const int key = sb * 32 + hs * 16 + 8 * ins + 4 * half + tr_key;
               const int d = db * 32 + tr_d;
-              const uint8_t* addr = vb + key * (D * 2) + (vchunk(key, d >> 3) << 4) + (d & 7) * 2;
+              const uint8_t* addr = vb + key * (D * 2) + (vchunk<D>(key, d >> 3) << 4) + (d & 7) * 2;
               x[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                   (__attribute__((address_space(3))) s16x4_t*)(addr));
             }

@@ -110,10 +110,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fma(const T* __restrict__ A, 
 // after the first half of its MFMAs is issued, so the matrix core stays busy
 // while the waves synchronise.  A stage holds the tile's BM x 32 slice of A
 // and BN x 32 slice of W as 64-byte rows of four 16-byte chunks; chunk c of
-// row r sits at c ^ (((r >> 1) ^ (r >> 3)) & 3), so any 8 consecutive rows
-// read by an MFMA operand load fall in distinct 16-byte slots of 128 bytes
-// and any 16 in distinct slots of 256 bytes (no bank conflicts whether the
-// LDS serves 8 or 16 lanes per pass).  The stage buffers are separate LDS
+// row r sits at c ^ ((r >> 2) & 3).  Of the XOR patterns on the row bits,
+// this one (like bits 3-4) measures no LDS bank conflicts for the MFMA
+// operand reads on gfx950 (rocprofv3 SQ_LDS_BANK_CONFLICT); patterns on bits
+// 0-1 or 1-3 measure 2- to 4-way conflicts.  The stage buffers are separate LDS
 // objects picked at compile time, which lets the compiler keep the newer
 // stages in flight while one is consumed.  MFMA operand layout (32x32x16):
 // lane l supplies row/column l%32 and k = 8*(l/32) .. +7 of the 16-wide K
@@ -166,7 +166,7 @@ struct Stages {
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * (KB * 2) + ((chunk ^ (((row >> 1) ^ (row >> 3)) & 3)) << 4);
+  return row * (KB * 2) + ((chunk ^ ((row >> 2) & 3)) << 4);
 }
 
 #define KVR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -297,7 +297,7 @@ __global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
   for (int j = 0; j < C::LA; ++j) {
     const int row0 = (wave * C::LA + j) * 16;
     const int row = row0 + (lane >> 2);                      // tile row this lane fetches
-    const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);   // logical chunk of its slot
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);   // logical chunk of its slot
     g.adst[j] = row0 * (KB * 2);
     const int m = min(m0 + row, M - 1);
     g.asrc[j] = A + static_cast<size_t>(m) * K + k0 + chunk * 8;
@@ -306,7 +306,7 @@ __global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
   for (int j = 0; j < C::LW; ++j) {
     const int row0 = (wave * C::LW + j) * 16;
     const int row = row0 + (lane >> 2);
-    const int chunk = (lane & 3) ^ (((row >> 1) ^ (row >> 3)) & 3);
+    const int chunk = (lane & 3) ^ ((row >> 2) & 3);
     g.wdst[j] = row0 * (KB * 2);
     const bf16_t* wr;
     if (MODE == 0) {
