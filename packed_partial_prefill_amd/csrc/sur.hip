@@ -24,7 +24,8 @@ constexpr int kSurMaxQ = 256;        // query tokens (8 blocks of 32)
 
 __device__ __forceinline__ bool id_ok(int id, int vocab) { return id >= 0 && id < vocab; }
 
-// bf16 table: workgroup = 32 suffix tokens, its 4 waves splitting the
+// bf16 table, general shapes (any hidden multiple of 64, Q up to 256):
+// workgroup = 32 suffix tokens, its 4 waves splitting the
 // hidden dimension in quarters.  The MFMA forms D[query][token] (A = query
 // rows, B = token rows, k along hidden), so a lane owns one token column and
 // 16 query rows per 32-query block.  Both operands are read straight from
@@ -125,6 +126,180 @@ __global__ __launch_bounds__(kScoreThreads) void k_sur_scores_mfma(
   }
   best = fmaxf(best, __shfl_xor(best, 32, 64));
   if (half == 0 && tok < S) {
+    bool in_q = false;
+    for (int j = 0; j < Q; ++j) in_q |= (qids[j] == id);
+    r[tok] = bad ? NAN : best + (in_q ? 0.25f : 0.f);
+  }
+}
+
+// bf16 table, query-stationary (hidden a multiple of kStatChunk, Q <= 128):
+// a workgroup of 8 waves scores 64 suffix tokens.  The query rows are staged
+// in LDS one hidden chunk of kStatChunk at a time (double-buffered; loaded
+// with coalesced 16-byte lanes and shared by all 8 waves), so each query byte
+// crosses L2 once per 64 tokens instead of once per 32, in whole lines.  Wave
+// w owns tokens 16 (w % 4) .. +15 and the half w / 4 of every chunk; the
+// token rows are read directly in 16x16x32 MFMA layout (4 lanes cover 64
+// contiguous bytes of one row) through a register ring that prefetches the
+// same steps of the next chunk.  D[query][token] accumulates in float32; the
+// two halves meet in LDS at the end.  The query squared norms accumulate from
+// the staging registers: the kStatChunk / 8 consecutive threads of a staging
+// slot cover one query row.
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+constexpr int kStatWaves = 8;
+constexpr int kStatThreads = 64 * kStatWaves;
+constexpr int kStatTokens = 16 * kStatWaves / 2;      // 64 tokens per workgroup
+constexpr int kStatChunk = 256;                        // hidden elements per staged chunk
+constexpr int kStatHalf = kStatChunk / 2;              // per wave half
+constexpr int kStatSteps = kStatHalf / 32;             // 16x16x32 k-steps per half chunk
+constexpr int kStatRow16 = kStatChunk / 8;             // 16-byte pieces per staged row
+
+// 16-byte piece c of staged query row r; the XOR keeps the MFMA operand
+// reads (16 rows x 2 pieces per 32 lanes) and the staging writes free of
+// LDS bank conflicts.
+__device__ __forceinline__ int stat_off(int row, int c) {
+  return row * kStatChunk + 8 * (c ^ ((2 * row) & 31));
+}
+
+template <int QB16>
+__global__ __launch_bounds__(kStatThreads) void k_sur_scores_stat(
+    const bf16_t* __restrict__ E, int vocab, int hidden, const int32_t* __restrict__ sid, int S,
+    const int32_t* __restrict__ qid, int Q, float* __restrict__ r) {
+  constexpr int QP = 16 * QB16;
+  constexpr int SLOTS = QP * kStatRow16 / kStatThreads;
+  static_assert(QP * kStatRow16 % kStatThreads == 0 && kStatThreads % kStatRow16 == 0, "staging map");
+  constexpr int kXr = (kStatWaves / 2) * (4 * QB16 + 1) * 64;   // floats of the half exchange
+  static_assert(kXr <= QP * kStatChunk, "exchange fits the staging buffers");
+  __shared__ __attribute__((aligned(16))) bf16_t qs[2][QP * kStatChunk];
+  __shared__ int qids[kSurMaxQ];
+  __shared__ float qss_s[QP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g4 = lane >> 4;
+  const int tg = wave % (kStatWaves / 2), h = wave / (kStatWaves / 2);
+  for (int j = tid; j < Q; j += kStatThreads) qids[j] = qid[j];
+  __syncthreads();
+  // staging slot i of this thread: query row lin / kStatRow16, piece lin % kStatRow16
+  const bf16_t* srow[SLOTS];
+  int soff[SLOTS];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    const int lin = i * kStatThreads + tid, row = lin / kStatRow16, c = lin % kStatRow16;
+    const int qj = qids[min(row, Q - 1)];
+    srow[i] = E + static_cast<size_t>(id_ok(qj, vocab) ? qj : 0) * hidden + 8 * c;
+    soff[i] = stat_off(row, c);
+  }
+  float qss[SLOTS];
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) qss[i] = 0.f;
+  const int tok = blockIdx.x * kStatTokens + tg * 16 + (lane & 15);
+  const int id = sid[min(tok, S - 1)];
+  const bool bad = !id_ok(id, vocab);
+  const int nch = hidden / kStatChunk;
+  const bf16_t* trow = E + static_cast<size_t>(bad ? 0 : id) * hidden + h * kStatHalf + 8 * g4;
+  bf16x8_t ring[kStatSteps];
+#pragma unroll
+  for (int u = 0; u < kStatSteps; ++u) ring[u] = *reinterpret_cast<const bf16x8_t*>(trow + 32 * u);
+  {
+    bf16x8_t st[SLOTS];
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) st[i] = *reinterpret_cast<const bf16x8_t*>(srow[i]);
+#pragma unroll
+    for (int i = 0; i < SLOTS; ++i) {
+      *reinterpret_cast<bf16x8_t*>(&qs[0][soff[i]]) = st[i];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = static_cast<float>(st[i][e]);
+        qss[i] = fmaf(x, x, qss[i]);
+      }
+    }
+  }
+  __syncthreads();
+  f32x4_t acc[QB16];
+#pragma unroll
+  for (int qb = 0; qb < QB16; ++qb) acc[qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float tss = 0.f;
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    const bool more = c + 1 < nch;
+    bf16x8_t st[SLOTS];
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i)
+        st[i] = *reinterpret_cast<const bf16x8_t*>(srow[i] + (c + 1) * kStatChunk);
+    }
+    const bf16_t* qb_base = qs[buf];
+    const int nxt = min(c + 1, nch - 1) * kStatChunk;
+#pragma unroll
+    for (int u = 0; u < kStatSteps; ++u) {
+      const bf16x8_t cur = ring[u];
+      ring[u] = *reinterpret_cast<const bf16x8_t*>(trow + nxt + 32 * u);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = static_cast<float>(cur[e]);
+        tss = fmaf(x, x, tss);
+      }
+      const int cq = 4 * (h * kStatSteps + u) + g4;
+#pragma unroll
+      for (int qb = 0; qb < QB16; ++qb) {
+        const int row = qb * 16 + (lane & 15);
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(qb_base + stat_off(row, cq));
+        acc[qb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, cur, acc[qb], 0, 0, 0);
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < SLOTS; ++i) {
+        *reinterpret_cast<bf16x8_t*>(&qs[buf ^ 1][soff[i]]) = st[i];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float x = static_cast<float>(st[i][e]);
+          qss[i] = fmaf(x, x, qss[i]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // query norms: a slot's kStatRow16 consecutive threads share its row
+#pragma unroll
+  for (int i = 0; i < SLOTS; ++i) {
+    float v = qss[i];
+#pragma unroll
+    for (int o = 1; o < kStatRow16; o <<= 1) v += __shfl_xor(v, o, 64);
+    const int lin = i * kStatThreads + tid;
+    if (lin % kStatRow16 == 0) qss_s[lin / kStatRow16] = v;
+  }
+  // the second half's partial products join the first half's through LDS
+  // (the staging buffers are free after the loop's last barrier)
+  float* xr = reinterpret_cast<float*>(&qs[0][0]) + tg * (4 * QB16 + 1) * 64;
+  if (h == 1) {
+#pragma unroll
+    for (int qb = 0; qb < QB16; ++qb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xr[(qb * 4 + i) * 64 + lane] = acc[qb][i];
+    xr[4 * QB16 * 64 + lane] = tss;
+  }
+  __syncthreads();
+  if (h != 0) return;
+#pragma unroll
+  for (int qb = 0; qb < QB16; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[qb][i] += xr[(qb * 4 + i) * 64 + lane];
+  tss += xr[4 * QB16 * 64 + lane];
+  tss += __shfl_xor(tss, 16, 64);
+  tss += __shfl_xor(tss, 32, 64);
+  const float tn = sqrtf(tss);
+  // D layout: lane holds token lane % 16, query rows 4 (lane / 16) + i
+  float best = -INFINITY;
+#pragma unroll
+  for (int qb = 0; qb < QB16; ++qb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = qb * 16 + 4 * g4 + i;
+      const float den = sqrtf(qss_s[row]) * tn;
+      const float cv = den > 0.f ? acc[qb][i] / den : 0.f;
+      if (row < Q) best = fmaxf(best, cv);
+    }
+  best = fmaxf(best, __shfl_xor(best, 16, 64));
+  best = fmaxf(best, __shfl_xor(best, 32, 64));
+  if (lane < 16 && tok < S) {
     bool in_q = false;
     for (int j = 0; j < Q; ++j) in_q |= (qids[j] == id);
     r[tok] = bad ? NAN : best + (in_q ? 0.25f : 0.f);
@@ -440,8 +615,20 @@ hipError_t launch_sur_scores(kvr_dtype dt, const void* E, int vocab, int hidden,
                        static_cast<const float*>(E), vocab, hidden, sid, qid, Q, r);
     return hipGetLastError();
   }
-  const dim3 grid((S + 31) / 32);
   const bf16_t* e = static_cast<const bf16_t*>(E);
+  if (hidden % kStatChunk == 0 && Q <= 128) {
+    const dim3 grid((S + kStatTokens - 1) / kStatTokens), block(kStatThreads);
+    switch ((Q + 15) / 16) {
+      case 1: hipLaunchKernelGGL(k_sur_scores_stat<1>, grid, block, 0, stream, e, vocab, hidden, sid, S, qid, Q, r); break;
+      case 2: hipLaunchKernelGGL(k_sur_scores_stat<2>, grid, block, 0, stream, e, vocab, hidden, sid, S, qid, Q, r); break;
+      case 3: hipLaunchKernelGGL(k_sur_scores_stat<3>, grid, block, 0, stream, e, vocab, hidden, sid, S, qid, Q, r); break;
+      case 4: hipLaunchKernelGGL(k_sur_scores_stat<4>, grid, block, 0, stream, e, vocab, hidden, sid, S, qid, Q, r); break;
+      case 5: case 6: hipLaunchKernelGGL(k_sur_scores_stat<6>, grid, block, 0, stream, e, vocab, hidden, sid, S, qid, Q, r); break;
+      default: hipLaunchKernelGGL(k_sur_scores_stat<8>, grid, block, 0, stream, e, vocab, hidden, sid, S, qid, Q, r); break;
+    }
+    return hipGetLastError();
+  }
+  const dim3 grid((S + 31) / 32);
   switch ((Q + 31) / 32) {
     case 1: hipLaunchKernelGGL(k_sur_scores_mfma<1>, grid, dim3(kScoreThreads), 0, stream, e, vocab, hidden, sid, S, qid, Q, r); break;
     case 2: hipLaunchKernelGGL(k_sur_scores_mfma<2>, grid, dim3(kScoreThreads), 0, stream, e, vocab, hidden, sid, S, qid, Q, r); break;

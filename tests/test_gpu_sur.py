@@ -94,11 +94,19 @@ def test_sur_scores_tiny_f32_and_select():
         _check_select(r_np, starts, B, w.pos0, T, rs, rl, us)
 
 
-@pytest.mark.parametrize("Q", [1, 17, 64, 200])
-def test_sur_scores_bf16_query_blocks(Q):
+# (Q, hidden, S): hidden a multiple of 256 with Q <= 128 takes the
+# query-stationary kernel (16-query blocks 1, 2, 3, 4, 6, 8; ragged last
+# workgroup of 64 tokens); other hidden sizes and Q > 128 take the general
+# kernel (32-query blocks).
+@pytest.mark.parametrize("Q,hidden,S", [
+    (1, 1024, 1000), (17, 1024, 1000), (48, 1024, 1000), (64, 1024, 1000), (65, 512, 777),
+    (96, 256, 64), (128, 1024, 1000), (5, 256, 5),
+    (129, 1024, 1000), (200, 1024, 1000), (48, 320, 1000),
+])
+def test_sur_scores_bf16_query_blocks(Q, hidden, S):
     m = kvr()
-    w = wl.SurWorkload(f"sur-bf16-q{Q}", 42, vocab=5000, hidden=1024, n_suffix=1000, n_query=Q,
-                       budget_percent=5.0)
+    w = wl.SurWorkload(f"sur-bf16-q{Q}-h{hidden}-s{S}", 42, vocab=5000, hidden=hidden, n_suffix=S,
+                       n_query=Q, budget_percent=5.0)
     E, dE = _table(w)
     s, q, _ = wl.sur_ids(w)
     r = _gpu_scores(m, w, dE, s, q)
@@ -108,10 +116,11 @@ def test_sur_scores_bf16_query_blocks(Q):
     assert err <= SCORE_TOL
 
 
-def test_sur_scores_bad_ids_are_nan():
+@pytest.mark.parametrize("hidden", [64, 256])
+def test_sur_scores_bad_ids_are_nan(hidden):
     m = kvr()
-    w = wl.SurWorkload("sur-bad-ids", 43, vocab=200, hidden=64, n_suffix=130, n_query=3,
-                       budget_percent=5.0)
+    w = wl.SurWorkload(f"sur-bad-ids-h{hidden}", 43, vocab=200, hidden=hidden, n_suffix=130,
+                       n_query=3, budget_percent=5.0)
     E, dE = _table(w)
     s, q, _ = wl.sur_ids(w)
     s = s.copy()
