@@ -9,6 +9,8 @@
 // float32 storage runs on a VALU kernel: one wave per (row, head), each
 // 64-key step scores one key per lane, then accumulates P*V with every lane
 // owning d/64 output columns.
+#include <type_traits>
+
 #include "common.h"
 #include "kvr_internal.h"
 
@@ -147,13 +149,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   using L = AttnLds<D>;
   constexpr int KCH = D / 8;             // 16-byte chunks per key row
   constexpr int ROWS = 1024 / (D * 2);   // key rows per 1 KB DMA slice
+  // Plain block order (query tile fastest): every XCD takes every KV range.
+  // Grouping the query tiles of one KV range on one XCD (by split, or by a
+  // fixed residue class of (head, split)) measured 33-37% slower.
   const int qt = blockIdx.x, g = blockIdx.y, sp = blockIdx.z;
   const int tot = n_total[qt];
   const int c0 = sp * split_tiles;
   if (c0 >= tot) return;
   const int c1 = min(tot, c0 + split_tiles);
   const int nf = n_full[qt];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = B * G;
 
   // the query column this lane owns
@@ -194,36 +200,55 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   // DMA slices of this wave: slice j covers key rows [j*ROWS, (j+1)*ROWS) of
   // K (j < 64/ROWS) or V.  Lane i lands at byte i*16 of the slice: row
   // i / KCH, physical chunk i % KCH, so it fetches the matching logical chunk.
+  // A tile's source is a wave-uniform base (its first key row of K or V) plus
+  // this lane's loop-invariant 32-bit byte offset.
   constexpr int KSL = kKvTile / ROWS;   // slices per operand per tile (16 or 8)
+  const size_t row_bytes = kv_row * 2;
   int s_row[L::slices], s_col[L::slices], s_dst[L::slices];
+  uint32_t s_off[L::slices];
   bool s_isv[L::slices];
 #pragma unroll
   for (int j = 0; j < L::slices; ++j) {
-    const int sl = wave * L::slices + j;         // 0 .. 2*KSL-1
+    const int sl = wave * L::slices + j;         // 0 .. 2*KSL-1, wave-uniform
     const bool isv = sl >= KSL;
     const int row = (isv ? sl - KSL : sl) * ROWS + lane / KCH;
     const int phys = lane % KCH;
     const int logical = isv ? vchunk<D>(row, phys) : kchunk<D>(row, phys);   // involutions
     s_isv[j] = isv;
     s_row[j] = row;
-    s_col[j] = logical * 8;
+    s_col[j] = logical * 16;
+    s_off[j] = static_cast<uint32_t>(row * row_bytes) + logical * 16;
     s_dst[j] = (isv ? L::kBytes : 0) + (isv ? sl - KSL : sl) * 1024;
   }
-  auto issue = [&](int c, int buf) {
+  const uint8_t* kg8 = reinterpret_cast<const uint8_t*>(kg);
+  const uint8_t* vg8 = reinterpret_cast<const uint8_t*>(vg);
+  auto issue = [&](int c, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     const int kv0 = c * kKvTile;
-    uint8_t* base = lds + buf * L::stage;
+    const uint8_t* kt = kg8 + static_cast<size_t>(kv0) * row_bytes;
+    const uint8_t* vt = vg8 + static_cast<size_t>(kv0) * row_bytes;
+    if (kv0 + kKvTile <= n_tokens) {
 #pragma unroll
-    for (int j = 0; j < L::slices; ++j) {
-      const int key = min(kv0 + s_row[j], n_tokens - 1);   // clamped rows are masked
-      const bf16_t* src = (s_isv[j] ? vg : kg) + key * kv_row + s_col[j];
-      __builtin_amdgcn_global_load_lds(KVR_GLB(src), KVR_LDS(base + s_dst[j]), 16, 0, 0);
+      for (int j = 0; j < L::slices; ++j)
+        __builtin_amdgcn_global_load_lds(KVR_GLB((s_isv[j] ? vt : kt) + s_off[j]),
+                                         KVR_LDS(lds + BUF * L::stage + s_dst[j]), 16, 0, 0);
+    } else {
+      // last, partial tile: rows past the cache repeat its last row (masked)
+#pragma unroll
+      for (int j = 0; j < L::slices; ++j) {
+        const int key = min(kv0 + s_row[j], n_tokens - 1);
+        const uint32_t off = static_cast<uint32_t>((key - kv0) * row_bytes) + s_col[j];
+        __builtin_amdgcn_global_load_lds(KVR_GLB((s_isv[j] ? vt : kt) + off),
+                                         KVR_LDS(lds + BUF * L::stage + s_dst[j]), 16, 0, 0);
+      }
     }
   };
   uint8_t rf = 0;
   auto fload = [&](int c) {
     if (tid < kKvTile) rf = flags[min(c * kKvTile + tid, n_tokens - 1)];
   };
-  auto fstore = [&](int buf) {
+  auto fstore = [&](auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
     if (tid < kKvTile) {
       const float b = ((rf & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((rf & KVR_FLAG_SINK) ? bias_sink : 0.f);
       const bf16_t bh = f32_to_bf16(b);
@@ -233,7 +258,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
       ch[1] = 0x3F803F80u;   // bf16 1.0, 1.0: multiply the query's -m_hi, -m_lo
       ch[2] = 0u;
       ch[3] = 0u;
-      *reinterpret_cast<u32x4_t*>(lds + buf * L::stage + L::kBytes + L::vBytes + tid * 16) = ch;
+      *reinterpret_cast<u32x4_t*>(lds + BUF * L::stage + L::kBytes + L::vBytes + tid * 16) = ch;
     }
   };
 
@@ -248,19 +273,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
     for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
   float l = 0.f;
 
-  issue(c0, 0);
-  fload(c0);
-  fstore(0);
-  attn_wait_vmcnt<0>();
-  __syncthreads();
-  int cur = 0;
-  for (int c = c0; c < c1; ++c) {
+  // One key tile from buffer BUF (compile-time, so every LDS address is a
+  // loop-invariant register plus an immediate offset), prefetching tile c + 1
+  // into the other buffer.
+  auto tile = [&](auto bufc, int c) {
+    constexpr int BUF = decltype(bufc)::value;
     const bool more = c + 1 < c1;
     if (more) {
-      issue(c + 1, cur ^ 1);
+      issue(c + 1, std::integral_constant<int, BUF ^ 1>{});
       fload(c + 1);
     }
-    const uint8_t* kb = lds + cur * L::stage;
+    const uint8_t* kb = lds + BUF * L::stage;
     const uint8_t* vb = kb + L::kBytes;
     const uint8_t* bb = vb + L::vBytes;
 
@@ -300,10 +323,10 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
     // Lazy maximum: m_eff moves only when the tile exceeds it by more than 8
     // (log2 units) or is the query's first visible tile, so probabilities
     // stay below 2^8 and most tiles skip rescaling.  After a move the tile's
-    // scores are re-based by the shift.
+    // scores are re-based by the shift (only in waves where a lane moved).
     const bool bump = (mt > 8.f) || (!m_set && mt != -INFINITY);
-    float shift = 0.f;
     if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+      float shift = 0.f;
       if (bump) {
         const float old = m_eff;
         set_qx(m_eff + mt);
@@ -316,12 +339,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
           for (int t = 0; t < 16; ++t) o[db][t] *= corr;
         m_set = true;
       }
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s[sb][t] -= shift;
     }
+
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const float e = fast_exp2(s[sb][t] - shift);
+        const float e = fast_exp2(s[sb][t]);
         s[sb][t] = e;
         l += e;
       }
@@ -354,10 +382,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
         }
       }
 
-    if (more) fstore(cur ^ 1);
+    if (more) fstore(std::integral_constant<int, BUF ^ 1>{});
     attn_wait_vmcnt<0>();   // the next tile's DMA has landed (this wave's part)
     __syncthreads();
-    cur ^= 1;
+  };
+
+  issue(c0, std::integral_constant<int, 0>{});
+  fload(c0);
+  fstore(std::integral_constant<int, 0>{});
+  attn_wait_vmcnt<0>();
+  __syncthreads();
+  for (int c = c0; c < c1; c += 2) {
+    tile(std::integral_constant<int, 0>{}, c);
+    if (c + 1 < c1) tile(std::integral_constant<int, 1>{}, c + 1);
   }
 
   // partial results: O^T columns (unnormalised), running max and sum

@@ -29,6 +29,17 @@ template <> struct Elem<bf16_t> {
   __device__ __forceinline__ static void store(bf16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
+// Workgroups are dispatched to the 8 XCDs round-robin by linear id, and each
+// XCD has its own L2.  xcd_linear(b, total) maps linear block b to a logical
+// index so that XCD b % 8 takes one contiguous run of the logical order
+// (a bijection on [0, total)): workgroups that share operands, placed next
+// to each other in the logical order, then share one L2.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_linear(int b, int total) {
+  const int xcd = b % kXcds, q = total / kXcds, rem = total % kXcds;
+  return xcd * q + min(xcd, rem) + b / kXcds;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -134,7 +134,6 @@ typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
 
 constexpr int KB = 32;
-constexpr int kXcds = 8;
 
 template <int BM_, int BN_, int WM_, int WN_, int NS_, int OCC_>
 struct Tile {
@@ -280,8 +279,7 @@ __global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
 
   // XCD-aware order: t = ((split * tiles_n) + n) * tiles_m + m
   const int total = tiles_m * tiles_n * splits;
-  const int b = blockIdx.x, xcd = b % kXcds, q = total / kXcds, rem = total % kXcds;
-  const int t = xcd * q + min(xcd, rem) + b / kXcds;
+  const int t = xcd_linear(blockIdx.x, total);
   const int tm = t % tiles_m, tn = (t / tiles_m) % tiles_n, split = t / (tiles_m * tiles_n);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
