@@ -74,9 +74,14 @@ __global__ __launch_bounds__(64) void k_attn_rowwise(const T* __restrict__ q,
 // bf16 MFMA kernel (gfx950 v_mfma_f32_32x32x16_bf16), float32 softmax.
 //
 // A workgroup owns KVR_ATTN_QROWS = 128 (packed row, query head) pairs of one
-// KV head group and a range of 64-key tiles (split-KV); 4 waves x 32 pairs.
-// Every key tile is staged once in LDS for all 128 pairs, double-buffered,
-// by global_load_lds_dwordx4 (no register staging): K and V both in their
+// KV head group and a range of 64-key tiles (split-KV), 32 pairs per wave.
+// Every key tile is staged once in LDS for all the workgroup's pairs by
+// global_load_lds_dwordx4 (no register staging), with its 64 flag bytes, in
+// kAttnStages buffers (the tile in use and the ones in flight).  With 128
+// pairs, two workgroups share a CU in two stages each, so one computes while
+// the other waits at its barrier; 256 pairs per workgroup (half the staging
+// bytes per MFMA, three stages, one workgroup per CU) measured slower.
+// K and V are both in their
 // natural [key][d] layout with the 16-byte chunks of each key row
 // XOR-swizzled, plus one 16-byte score slice per key written by 64 threads
 // (see below).
@@ -101,7 +106,13 @@ typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQRows = KVR_ATTN_QROWS;     // 128 pairs per workgroup
 constexpr int kKvTile = KVR_ATTN_KV_TILE;  // 64 keys per tile
-constexpr int kAttnThreads = 256;
+constexpr int kAttnThreads = 256;          // merge and decode kernels
+constexpr int kAttnWaves = kQRows / 32;    // packed kernel: 32 pairs per wave
+constexpr int kAttnMfmaThreads = 64 * kAttnWaves;
+constexpr int kAttnWgPerCu = 8 / kAttnWaves;   // 8 waves per CU (2 per SIMD)
+// KV tiles in LDS: the current one plus kAttnStages - 1 in flight (three
+// stages fit one 256-pair workgroup per CU, two stages two 128-pair ones)
+constexpr int kAttnStages = kAttnWgPerCu == 1 ? 3 : 2;
 
 #define KVR_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 #define KVR_GLB(p) ((const __attribute__((address_space(1))) void*)(p))
@@ -115,10 +126,17 @@ template <int D>
 struct AttnLds {
   static constexpr int kBytes = kKvTile * D * 2;   // K tile
   static constexpr int vBytes = kKvTile * D * 2;   // V tile
-  static constexpr int bBytes = kKvTile * 16;      // score slice per key: [b_hi, b_lo, 1, 1, 0 x 4]
-  static constexpr int stage = kBytes + vBytes + bBytes;
-  static constexpr int total = 2 * stage;
-  static constexpr int slices = (kBytes + vBytes) / 1024 / 4;   // 1 KB DMA slices per wave
+  static constexpr int fBytes = kKvTile;           // the tile's metadata flag bytes
+  static constexpr int stage = kBytes + vBytes + fBytes;
+  static constexpr int total = kAttnStages * stage;
+  // Regions by operand (K of every stage, then V, then the flags), so that
+  // every address within a region is a lane register plus an immediate
+  // offset below 64 KB.
+  static constexpr int kOff(int b) { return b * kBytes; }
+  static constexpr int vOff(int b) { return kAttnStages * kBytes + b * vBytes; }
+  static constexpr int fOff(int b) { return kAttnStages * (kBytes + vBytes) + b * fBytes; }
+  static constexpr int slices = (kBytes + vBytes) / 1024 / kAttnWaves;   // 1 KB DMA slices per wave
+  static_assert((kBytes + vBytes) % (1024 * kAttnWaves) == 0, "DMA slices per wave");
 };
 
 // Physical 16-byte chunk of logical chunk c in key row k.  K rows: c ^ (k & 15)
@@ -138,8 +156,76 @@ __device__ __forceinline__ int vchunk(int key, int c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
+}
+
+// ds_read_b64_tr_b16 at LDS byte address addr + OFF.  Written as inline
+// assembly because the compiler places a wait for every outstanding LDS DMA
+// in front of the builtin form (it cannot tell that the DMA in flight
+// targets another buffer), which would stall each tile on the prefetch of
+// the next.  The caller waits for the result with lds_wait().
+template <int OFF>
+__device__ __forceinline__ u32x2_t ds_read_tr16(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x2_t r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+__device__ __forceinline__ void lds_wait() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+}
+template <int N> __device__ __forceinline__ void lds_wait_n() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));   // at most N LDS operations outstanding
+}
+// The compiler does not know that an assembly LDS read's result is valid
+// only after the lgkmcnt wait: after waiting, pass every such result through
+// reg_fence, which the compiler must order after the wait (both are volatile)
+// and which every use of the value then depends on.
+template <typename T> __device__ __forceinline__ void reg_fence(T& r) { asm volatile("" : "+v"(r)); }
+
+// ds_read_b128 / ds_read_u8 at addr + OFF (see ds_read_tr16 for why assembly).
+template <int OFF>
+__device__ __forceinline__ u32x4_t ds_read_b128(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t ds_read_u8(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  uint32_t r;
+  asm volatile("ds_read_u8 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+
+// Workgroup barrier for the KV pipeline.  __syncthreads() (and any
+// workgroup release fence, since LDS DMA writes count as LDS stores) waits
+// for every outstanding global load, which would drain the KV tiles still in
+// flight.  Here each wave waits for its own LDS reads and writes
+// (lgkmcnt 0) and for the DMA of the next tile (attn_wait_vmcnt, before the
+// call); the empty asm statements keep the compiler from moving LDS
+// accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  lds_wait();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int D>
-__global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
+__global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     const uint8_t* __restrict__ flags, const int32_t* __restrict__ Tpos,
     const int32_t* __restrict__ n_full, const int32_t* __restrict__ n_total, int B, int n_tokens,
@@ -174,6 +260,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
   }
+  // the query fragments have arrived before the loop (otherwise the wait for
+  // them would sit inside it, in front of every tile's first product)
+  attn_wait_vmcnt<0>();
   // The score MFMA takes one more 16-wide K slice: key j supplies
   // [b_hi, b_lo, 1, 1, 0...] (b_hi + b_lo = bf16 split of the key's bias),
   // the query supplies [1, 1, -m_hi, -m_lo, 0...] (lanes of the upper half
@@ -204,67 +293,111 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   // this lane's loop-invariant 32-bit byte offset.
   constexpr int KSL = kKvTile / ROWS;   // slices per operand per tile (16 or 8)
   const size_t row_bytes = kv_row * 2;
-  int s_row[L::slices], s_col[L::slices], s_dst[L::slices];
+  // slice j of this wave: operand (wave-uniform), key row within the tile
+  // and logical 16-byte chunk of this lane
+  auto slice_isv = [&](int j) { return wave * L::slices + j >= KSL; };
+  auto slice_row = [&](int j) {
+    const int sl = wave * L::slices + j;
+    return (sl >= KSL ? sl - KSL : sl) * ROWS + lane / KCH;
+  };
+  auto slice_chunk = [&](int j) {
+    const int row = slice_row(j), phys = lane % KCH;
+    return slice_isv(j) ? vchunk<D>(row, phys) : kchunk<D>(row, phys);   // involutions
+  };
   uint32_t s_off[L::slices];
-  bool s_isv[L::slices];
+  int s_dst[L::slices];
 #pragma unroll
   for (int j = 0; j < L::slices; ++j) {
-    const int sl = wave * L::slices + j;         // 0 .. 2*KSL-1, wave-uniform
-    const bool isv = sl >= KSL;
-    const int row = (isv ? sl - KSL : sl) * ROWS + lane / KCH;
-    const int phys = lane % KCH;
-    const int logical = isv ? vchunk<D>(row, phys) : kchunk<D>(row, phys);   // involutions
-    s_isv[j] = isv;
-    s_row[j] = row;
-    s_col[j] = logical * 16;
-    s_off[j] = static_cast<uint32_t>(row * row_bytes) + logical * 16;
-    s_dst[j] = (isv ? L::kBytes : 0) + (isv ? sl - KSL : sl) * 1024;
+    const int sl = wave * L::slices + j;         // wave-uniform
+    s_off[j] = static_cast<uint32_t>(slice_row(j) * row_bytes) + slice_chunk(j) * 16;
+    s_dst[j] = (slice_isv(j) ? L::vOff(0) : L::kOff(0)) + (sl >= KSL ? sl - KSL : sl) * 1024;
   }
   const uint8_t* kg8 = reinterpret_cast<const uint8_t*>(kg);
   const uint8_t* vg8 = reinterpret_cast<const uint8_t*>(vg);
+  static_assert(L::kBytes == L::vBytes, "K and V stages advance by the same stride");
+  // Tile c into buffer BUF: this wave's K / V slices, and (wave 0) the 64
+  // flag bytes, 4 per lane.  A wave issues kIssued vector-memory operations
+  // per full tile; the last, partial tile stages its flags through registers
+  // (a compiler wait drains everything issued before) and clamps its rows.
   auto issue = [&](int c, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
+    uint8_t* dst = lds + BUF * L::kBytes;
     const int kv0 = c * kKvTile;
     const uint8_t* kt = kg8 + static_cast<size_t>(kv0) * row_bytes;
     const uint8_t* vt = vg8 + static_cast<size_t>(kv0) * row_bytes;
     if (kv0 + kKvTile <= n_tokens) {
+      if (wave == 0 && lane < kKvTile / 4)
+        __builtin_amdgcn_global_load_lds(KVR_GLB(flags + kv0 + 4 * lane),
+                                         KVR_LDS(lds + L::fOff(BUF)), 4, 0, 0);
 #pragma unroll
       for (int j = 0; j < L::slices; ++j)
-        __builtin_amdgcn_global_load_lds(KVR_GLB((s_isv[j] ? vt : kt) + s_off[j]),
-                                         KVR_LDS(lds + BUF * L::stage + s_dst[j]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(KVR_GLB((slice_isv(j) ? vt : kt) + s_off[j]),
+                                         KVR_LDS(dst + s_dst[j]), 16, 0, 0);
     } else {
-      // last, partial tile: rows past the cache repeat its last row (masked)
+      // rows and flags past the cache repeat its last row (those keys are masked)
+      if (wave == 0) lds[L::fOff(BUF) + lane] = flags[min(kv0 + lane, n_tokens - 1)];
 #pragma unroll
       for (int j = 0; j < L::slices; ++j) {
-        const int key = min(kv0 + s_row[j], n_tokens - 1);
-        const uint32_t off = static_cast<uint32_t>((key - kv0) * row_bytes) + s_col[j];
-        __builtin_amdgcn_global_load_lds(KVR_GLB((s_isv[j] ? vt : kt) + off),
-                                         KVR_LDS(lds + BUF * L::stage + s_dst[j]), 16, 0, 0);
+        const int key = min(kv0 + slice_row(j), n_tokens - 1);
+        const uint32_t off = static_cast<uint32_t>((key - kv0) * row_bytes) + slice_chunk(j) * 16;
+        __builtin_amdgcn_global_load_lds(KVR_GLB((slice_isv(j) ? vt : kt) + off),
+                                         KVR_LDS(dst + s_dst[j]), 16, 0, 0);
       }
     }
   };
-  uint8_t rf = 0;
-  auto fload = [&](int c) {
-    if (tid < kKvTile) rf = flags[min(c * kKvTile + tid, n_tokens - 1)];
+  // this wave's part of tile c + 1 has landed, at the end of tile c, with
+  // the tiles after it (kAttnStages - 2 of them) still in flight
+  auto wait_next = [&]() {
+    if (wave == 0)
+      attn_wait_vmcnt<(kAttnStages - 2) * (L::slices + 1)>();
+    else
+      attn_wait_vmcnt<(kAttnStages - 2) * L::slices>();
   };
-  auto fstore = [&](auto bufc) {
-    constexpr int BUF = decltype(bufc)::value;
-    if (tid < kKvTile) {
-      const float b = ((rf & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((rf & KVR_FLAG_SINK) ? bias_sink : 0.f);
-      const bf16_t bh = f32_to_bf16(b);
-      const bf16_t bl = f32_to_bf16(b - bf16_to_f32(bh));
-      u32x4_t ch;
-      ch[0] = static_cast<uint32_t>(bh) | (static_cast<uint32_t>(bl) << 16);
-      ch[1] = 0x3F803F80u;   // bf16 1.0, 1.0: multiply the query's -m_hi, -m_lo
-      ch[2] = 0u;
-      ch[3] = 0u;
-      *reinterpret_cast<u32x4_t*>(lds + BUF * L::stage + L::kBytes + L::vBytes + tid * 16) = ch;
-    }
+
+  // Score-MFMA operands.  K rows: key sb*32 + (lane % 32), 16-byte chunk
+  // 2 ks + half; its swizzle depends on key % 16 only, so klane[ks] plus an
+  // immediate (buffer, sb) addresses it.  Bias slice: key j supplies
+  // [b_hi, b_lo, 1, 1, 0 x 4] (lanes of the upper half supply zeros), picked
+  // from the four flag combinations by the key's flag byte.
+  uint32_t klane[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    klane[ks] = lds_addr(lds) + L::kOff(0) + (lane & 31) * (D * 2) +
+                (kchunk<D>(lane & 31, ks * 2 + half) << 4);
+  const uint32_t flane = lds_addr(lds) + L::fOff(0) + (lane & 31);
+  auto bias_word = [&](float b) {
+    const bf16_t bh = f32_to_bf16(b);
+    const bf16_t bl = f32_to_bf16(b - bf16_to_f32(bh));
+    return half == 0 ? (static_cast<uint32_t>(bh) | (static_cast<uint32_t>(bl) << 16)) : 0u;
+  };
+  const uint32_t bw_l = bias_word(bias_local), bw_s = bias_word(bias_sink);
+  const uint32_t bw_ls = bias_word(bias_local + bias_sink);
+  const uint32_t bones = half == 0 ? 0x3F803F80u : 0u;   // bf16 1.0, 1.0 times -m_hi, -m_lo
+  auto bias_operand = [&](uint32_t f) {
+    const uint32_t wl = (f & KVR_FLAG_SINK) ? bw_ls : bw_l;
+    const uint32_t wn = (f & KVR_FLAG_SINK) ? bw_s : 0u;
+    const uint32_t w = (f & KVR_FLAG_LOCAL) ? wl : wn;
+    const u32x4_t v = {w, bones, 0u, 0u};
+    return __builtin_bit_cast(bf16x8_t, v);
   };
 
   // transposing-read address pattern of this lane (see header comment)
   const int tr_key = (lane & 15) >> 2;                          // key within the 4-key group
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);    // d offset within a 32-row block
+  // Transposing-read address of key (16-key step base) + key_l, column block
+  // db: the V swizzle depends only on key % 4 = tr_key, so it is this lane's
+  // loop-invariant vlane[db] plus the step base times the row size (an
+  // immediate) plus the buffer's offset.
+  uint32_t vlane[D / 32];
+  {
+    const int key_l = 4 * half + tr_key;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = db * 32 + tr_d;
+      vlane[db] = lds_addr(lds) + L::vOff(0) + key_l * (D * 2) + (vchunk<D>(key_l, d >> 3) << 4) +
+                  (d & 7) * 2;
+    }
+  }
 
   f32x16_t o[D / 32];
 #pragma unroll
@@ -273,36 +406,39 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
     for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
   float l = 0.f;
 
-  // One key tile from buffer BUF (compile-time, so every LDS address is a
-  // loop-invariant register plus an immediate offset), prefetching tile c + 1
-  // into the other buffer.
+  // One key tile from buffer BUF, prefetching tile c + kAttnStages - 1 into
+  // the buffer tile c - 1 used.  All LDS reads of the loop are issued as
+  // inline assembly with explicit lgkmcnt waits: the compiler cannot tell
+  // them from the LDS DMA in flight (to another buffer) and would otherwise
+  // wait for that DMA before the first read.
   auto tile = [&](auto bufc, int c) {
     constexpr int BUF = decltype(bufc)::value;
-    const bool more = c + 1 < c1;
-    if (more) {
-      issue(c + 1, std::integral_constant<int, BUF ^ 1>{});
-      fload(c + 1);
-    }
-    const uint8_t* kb = lds + BUF * L::stage;
-    const uint8_t* vb = kb + L::kBytes;
-    const uint8_t* bb = vb + L::vBytes;
+    constexpr int NXT = (BUF + kAttnStages - 1) % kAttnStages;
+    const bool ahead = c + kAttnStages - 1 < c1;
+    if (ahead) issue(c + kAttnStages - 1, std::integral_constant<int, NXT>{});
 
     // S^T = K Q^T + (bias - m_eff) for the two 32-key halves of the tile
     f32x16_t s[2];
+    static_for<0, 2>([&](auto sbc) {
+      constexpr int sb = decltype(sbc)::value;
+      u32x4_t ka[D / 16];
+      static_for<0, D / 16>([&](auto ksc) {
+        constexpr int ks = decltype(ksc)::value;
+        ka[ks] = ds_read_b128<L::kOff(BUF) + sb * 32 * D * 2>(klane[ks]);
+      });
+      uint32_t fb = ds_read_u8<BUF * L::fBytes + sb * 32>(flane);
+      lds_wait();
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
+      for (int ks = 0; ks < D / 16; ++ks) reg_fence(ka[ks]);
+      reg_fence(fb);
 #pragma unroll
       for (int t = 0; t < 16; ++t) s[sb][t] = 0.f;
-      const int key = sb * 32 + (lane & 31);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            kb + key * (D * 2) + (kchunk<D>(key, ks * 2 + half) << 4));
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[sb], 0, 0, 0);
-      }
-      const bf16x8_t ab = *reinterpret_cast<const bf16x8_t*>(bb + key * 16);
-      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab, qx, s[sb], 0, 0, 0);
-    }
+      for (int ks = 0; ks < D / 16; ++ks)
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
+                                                         qf[ks], s[sb], 0, 0, 0);
+      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_operand(fb), qx, s[sb], 0, 0, 0);
+    });
     // causal test only on partially visible tiles (uniform branch)
     if (c >= nf) {
       const int lim = u - c * kKvTile;   // keys kl > lim lie in the future
@@ -355,46 +491,56 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
       }
 
     // O^T += V^T P^T, four 16-key steps
+    static_for<0, 4>([&](auto stc) {
+      constexpr int sb = decltype(stc)::value / 2, hs = decltype(stc)::value % 2;
+      constexpr int off = BUF * L::vBytes + (sb * 32 + hs * 16) * D * 2;
+      u32x2_t x[D / 32][2];
+      static_for<0, D / 32>([&](auto dbc) {
+        constexpr int db = decltype(dbc)::value;
+        x[db][0] = ds_read_tr16<off>(vlane[db]);
+        x[db][1] = ds_read_tr16<off + 8 * D * 2>(vlane[db]);
+      });
+      bf16x8_t pb;
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+      for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[sb][hs * 8 + i]);
+      lds_wait();
 #pragma unroll
-      for (int hs = 0; hs < 2; ++hs) {
-        bf16x8_t pb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[sb][hs * 8 + i]);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          s16x4_t x[2];
-#pragma unroll
-          for (int ins = 0; ins < 2; ++ins) {
-            const int key = sb * 32 + hs * 16 + 8 * ins + 4 * half + tr_key;
-            const int d = db * 32 + tr_d;
-            const uint8_t* addr = vb + key * (D * 2) + (vchunk<D>(key, d >> 3) << 4) + (d & 7) * 2;
-            x[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (__attribute__((address_space(3))) s16x4_t*)(addr));
-          }
-          const s16x4_t x0 = x[0], x1 = x[1];
-          const short av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-          bf16x8_t a;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(__bf16, av[i]);
-          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[db], 0, 0, 0);
-        }
+      for (int db = 0; db < D / 32; ++db) {
+        reg_fence(x[db][0]);
+        reg_fence(x[db][1]);
       }
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x4_t w = {x[db][0][0], x[db][0][1], x[db][1][0], x[db][1][1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb,
+                                                         o[db], 0, 0, 0);
+      }
+    });
 
-    if (more) fstore(std::integral_constant<int, BUF ^ 1>{});
-    attn_wait_vmcnt<0>();   // the next tile's DMA has landed (this wave's part)
-    __syncthreads();
+    if (ahead && kAttnStages > 2)
+      wait_next();   // tile c + 1 has landed (this wave's part)
+    else
+      attn_wait_vmcnt<0>();
+    lds_barrier();
   };
 
+  static_assert(kAttnStages == 2 || kAttnStages == 3, "pipeline depth");
   issue(c0, std::integral_constant<int, 0>{});
-  fload(c0);
-  fstore(std::integral_constant<int, 0>{});
-  attn_wait_vmcnt<0>();
-  __syncthreads();
-  for (int c = c0; c < c1; c += 2) {
-    tile(std::integral_constant<int, 0>{}, c);
-    if (c + 1 < c1) tile(std::integral_constant<int, 1>{}, c + 1);
+  if constexpr (kAttnStages == 3) {
+    if (c0 + 1 < c1) {
+      issue(c0 + 1, std::integral_constant<int, 1>{});
+      wait_next();   // tile c0 has landed
+    } else {
+      attn_wait_vmcnt<0>();
+    }
+  } else {
+    attn_wait_vmcnt<0>();
+  }
+  lds_barrier();
+  for (int c = c0; c < c1; c += kAttnStages) {
+    static_for<0, kAttnStages>([&](auto bc) {
+      if (c + decltype(bc)::value < c1) tile(bc, c + decltype(bc)::value);
+    });
   }
 
   // partial results: O^T columns (unnormalised), running max and sum
@@ -418,10 +564,13 @@ __global__ __launch_bounds__(kAttnThreads, 2) void k_attn_mfma(
   }
 }
 
-// Merge the split-KV partials: workgroup (query tile, KV group, 16-row slice
-// of d); thread (pair ql, 8 consecutive d).  Split weights 2^(m_s - max m),
+// Merge the split-KV partials: workgroup (query tile, KV group, kMergeD-row
+// slice of d); thread (pair ql, 8 consecutive d).  Split weights 2^(m_s - max m),
 // normalised by the weighted sums; each thread writes its pair's 8 outputs
 // (one 16-byte chunk of bf16, or two of float32).
+constexpr int kMergeD = 8 * (kAttnThreads / kQRows);   // d rows per merge workgroup
+static_assert(kAttnThreads % kQRows == 0, "merge threads cover whole query tiles");
+
 template <int D, typename OutT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
@@ -429,8 +578,8 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     int n_splits, OutT* __restrict__ o) {
   const int qt = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x;
-  const int ql = tid & (kQRows - 1);
-  const int d0 = blockIdx.z * 16 + (tid >> 7) * 8;
+  const int ql = tid % kQRows;
+  const int d0 = blockIdx.z * kMergeD + (tid / kQRows) * 8;
   const int p = qt * kQRows + ql;
   if (p >= B * G) return;
   const int ns = (n_total[qt] + split_tiles - 1) / split_tiles;
@@ -819,7 +968,7 @@ hipError_t launch_mfma(const void* q, const void* k_cache, const void* v_cache,
   float* part_ml = part_o + slots * sh.d * kQRows;
   const float log2e = 1.4426950408889634f;
   dim3 grid(nt, sh.hkv, ns);
-  hipLaunchKernelGGL(k_attn_mfma<D>, grid, dim3(kAttnThreads), AttnLds<D>::total, stream,
+  hipLaunchKernelGGL(k_attn_mfma<D>, grid, dim3(kAttnMfmaThreads), AttnLds<D>::total, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
                      static_cast<const bf16_t*>(v_cache), flags, T, n_full, n_total, B, n_tokens,
                      sh.hq, sh.hkv, sh.group, alpha * log2e, beta * log2e, st, ns, part_o,
@@ -836,7 +985,7 @@ hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_t
   const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
   const float* part_o = static_cast<const float*>(ws);
   const float* part_ml = part_o + slots * sh.d * kQRows;
-  hipLaunchKernelGGL((k_attn_merge<D, OutT>), dim3(nt, sh.hkv, D / 16), dim3(kAttnThreads), 0,
+  hipLaunchKernelGGL((k_attn_merge<D, OutT>), dim3(nt, sh.hkv, D / kMergeD), dim3(kAttnThreads), 0,
                      stream, part_o, part_ml, n_total, B, sh.hq, sh.hkv, sh.group, st, ns,
                      static_cast<OutT*>(o_out));
   return hipGetLastError();
