@@ -293,56 +293,59 @@ __global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
   // this lane's loop-invariant 32-bit byte offset.
   constexpr int KSL = kKvTile / ROWS;   // slices per operand per tile (16 or 8)
   const size_t row_bytes = kv_row * 2;
-  // slice j of this wave: operand (wave-uniform), key row within the tile
-  // and logical 16-byte chunk of this lane
+  // slice j of this wave: operand (wave-uniform) and this lane's byte offset
+  // within the tile (key row, logical 16-byte chunk)
   auto slice_isv = [&](int j) { return wave * L::slices + j >= KSL; };
-  auto slice_row = [&](int j) {
-    const int sl = wave * L::slices + j;
-    return (sl >= KSL ? sl - KSL : sl) * ROWS + lane / KCH;
-  };
-  auto slice_chunk = [&](int j) {
-    const int row = slice_row(j), phys = lane % KCH;
-    return slice_isv(j) ? vchunk<D>(row, phys) : kchunk<D>(row, phys);   // involutions
-  };
   uint32_t s_off[L::slices];
   int s_dst[L::slices];
 #pragma unroll
   for (int j = 0; j < L::slices; ++j) {
     const int sl = wave * L::slices + j;         // wave-uniform
-    s_off[j] = static_cast<uint32_t>(slice_row(j) * row_bytes) + slice_chunk(j) * 16;
+    const int row = (sl >= KSL ? sl - KSL : sl) * ROWS + lane / KCH, phys = lane % KCH;
+    const int logical = slice_isv(j) ? vchunk<D>(row, phys) : kchunk<D>(row, phys);   // involutions
+    s_off[j] = static_cast<uint32_t>(row * row_bytes) + logical * 16;
     s_dst[j] = (slice_isv(j) ? L::vOff(0) : L::kOff(0)) + (sl >= KSL ? sl - KSL : sl) * 1024;
   }
   const uint8_t* kg8 = reinterpret_cast<const uint8_t*>(kg);
   const uint8_t* vg8 = reinterpret_cast<const uint8_t*>(vg);
   static_assert(L::kBytes == L::vBytes, "K and V stages advance by the same stride");
-  // Tile c into buffer BUF: this wave's K / V slices, and (wave 0) the 64
-  // flag bytes, 4 per lane.  A wave issues kIssued vector-memory operations
-  // per full tile; the last, partial tile stages its flags through registers
-  // (a compiler wait drains everything issued before) and clamps its rows.
+  // Tile c into buffer BUF by buffer loads into LDS: per tile a wave-uniform
+  // descriptor whose range is the tile's rows inside the cache (rows past
+  // the cache read as zero; those keys are always masked), each lane a 32-bit
+  // offset.  Wave 0 also brings the 64 flag bytes, 4 per lane, issued first;
+  // the last, partial tile stages its flags through registers instead (a
+  // range-checked dword straddling the end would read as zero), and a
+  // compiler wait then drains everything issued before.  A wave issues
+  // L::slices (+1 on wave 0) vector-memory operations per full tile.
+  constexpr int kRsrcWord3 = 0x00020000;   // raw (untyped) buffer access
   auto issue = [&](int c, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    uint8_t* dst = lds + BUF * L::kBytes;
     const int kv0 = c * kKvTile;
-    const uint8_t* kt = kg8 + static_cast<size_t>(kv0) * row_bytes;
-    const uint8_t* vt = vg8 + static_cast<size_t>(kv0) * row_bytes;
-    if (kv0 + kKvTile <= n_tokens) {
-      if (wave == 0 && lane < kKvTile / 4)
-        __builtin_amdgcn_global_load_lds(KVR_GLB(flags + kv0 + 4 * lane),
-                                         KVR_LDS(lds + L::fOff(BUF)), 4, 0, 0);
-#pragma unroll
-      for (int j = 0; j < L::slices; ++j)
-        __builtin_amdgcn_global_load_lds(KVR_GLB((slice_isv(j) ? vt : kt) + s_off[j]),
-                                         KVR_LDS(dst + s_dst[j]), 16, 0, 0);
-    } else {
-      // rows and flags past the cache repeat its last row (those keys are masked)
-      if (wave == 0) lds[L::fOff(BUF) + lane] = flags[min(kv0 + lane, n_tokens - 1)];
-#pragma unroll
-      for (int j = 0; j < L::slices; ++j) {
-        const int key = min(kv0 + slice_row(j), n_tokens - 1);
-        const uint32_t off = static_cast<uint32_t>((key - kv0) * row_bytes) + slice_chunk(j) * 16;
-        __builtin_amdgcn_global_load_lds(KVR_GLB((slice_isv(j) ? vt : kt) + off),
-                                         KVR_LDS(dst + s_dst[j]), 16, 0, 0);
+    const int rows = min(kKvTile, n_tokens - kv0);
+    const int nbytes = rows * static_cast<int>(row_bytes);
+    if (wave == 0) {
+      if (rows == kKvTile) {
+        if (lane < kKvTile / 4) {
+          const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<uint8_t*>(flags + kv0), 0, kKvTile, kRsrcWord3);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, KVR_LDS(lds + L::fOff(BUF)), 4, 4 * lane, 0,
+                                                   0, 0);
+        }
+      } else {
+        lds[L::fOff(BUF) + lane] = flags[min(kv0 + lane, n_tokens - 1)];
       }
+    }
+    // (descriptors are built per slice from the chosen base, and the lane
+    // offset goes in as int: a conditional between descriptors, or an
+    // unsigned offset argument, makes the host compilation pass silently
+    // drop the kernel)
+#pragma unroll
+    for (int j = 0; j < L::slices; ++j) {
+      const uint8_t* base = (slice_isv(j) ? vg8 : kg8) + static_cast<size_t>(kv0) * row_bytes;
+      const __amdgpu_buffer_rsrc_t r =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, nbytes, kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, KVR_LDS(lds + BUF * L::kBytes + s_dst[j]), 16,
+                                               static_cast<int>(s_off[j]), 0, 0, 0);
     }
   };
   // this wave's part of tile c + 1 has landed, at the end of tile c, with
@@ -455,7 +458,7 @@ __global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
       for (int t = 0; t < 16; ++t) mt = fmaxf(mt, s[sb][t]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = xor32_max(mt);
     // Lazy maximum: m_eff moves only when the tile exceeds it by more than 8
     // (log2 units) or is the query's first visible tile, so probabilities
     // stay below 2^8 and most tiles skip rescaling.  After a move the tile's
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
         po[d * kQRows + ql] = o[db][t];
       }
   }
-  l += __shfl_xor(l, 32, 64);
+  l = xor32_add(l);
   if (half == 0 && p < P) {
     float* pm = part_ml + slot * 2 * kQRows;
     pm[ql] = m_set ? m_eff : -INFINITY;
@@ -769,7 +772,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int t = 0; t < 16; ++t) mt = fmaxf(mt, s[sb][t]);
-      mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+      mt = xor32_max(mt);
       m[cb] = mt;
       float ls = 0.f;
 #pragma unroll
@@ -780,7 +783,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
           s[sb][t] = e;
           ls += e;
         }
-      l[cb] = ls + __shfl_xor(ls, 32, 64);
+      l[cb] = xor32_add(ls);
       if (cb == 0) attn_wait_vmcnt<0>();   // V tile landed
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)

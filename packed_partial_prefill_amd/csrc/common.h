@@ -40,6 +40,19 @@ __device__ __forceinline__ int xcd_linear(int b, int total) {
   return xcd * q + min(xcd, rem) + b / kXcds;
 }
 
+// Combine x with the value of lane ^ 32: v_permlane32_swap exchanges the
+// wave's two 32-lane halves in one VALU instruction, leaving each lane its
+// own value and its partner's (in either order), where __shfl_xor would take
+// an LDS round trip.
+__device__ __forceinline__ float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xor32_add(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);

@@ -110,7 +110,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_sur_scores_mfma(
     __syncthreads();
   }
   if (wave != 0) return;
-  const float tn = sqrtf(tss + __shfl_xor(tss, 32, 64));
+  const float tn = sqrtf(xor32_add(tss));
   float best = -INFINITY;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kScoreThreads) void k_sur_scores_mfma(
       if (qb * 32 + row < Q) best = fmaxf(best, c);
     }
   }
-  best = fmaxf(best, __shfl_xor(best, 32, 64));
+  best = xor32_max(best);
   if (half == 0 && tok < S) {
     bool in_q = false;
     for (int j = 0; j < Q; ++j) in_q |= (qids[j] == id);
@@ -284,7 +284,7 @@ __global__ __launch_bounds__(kStatThreads) void k_sur_scores_stat(
     for (int i = 0; i < 4; ++i) acc[qb][i] += xr[(qb * 4 + i) * 64 + lane];
   tss += xr[4 * QB16 * 64 + lane];
   tss += __shfl_xor(tss, 16, 64);
-  tss += __shfl_xor(tss, 32, 64);
+  tss = xor32_add(tss);
   const float tn = sqrtf(tss);
   // D layout: lane holds token lane % 16, query rows 4 (lane / 16) + i
   float best = -INFINITY;
@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kStatThreads) void k_sur_scores_stat(
       if (row < Q) best = fmaxf(best, cv);
     }
   best = fmaxf(best, __shfl_xor(best, 16, 64));
-  best = fmaxf(best, __shfl_xor(best, 32, 64));
+  best = xor32_max(best);
   if (lane < 16 && tok < S) {
     bool in_q = false;
     for (int j = 0; j < Q; ++j) in_q |= (qids[j] == id);
