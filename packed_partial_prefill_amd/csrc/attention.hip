@@ -588,10 +588,13 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
   const int ns = (n_total[qt] + split_tiles - 1) / split_tiles;
   const size_t slot0 = (static_cast<size_t>(qt) * Hkv + g) * n_splits;
   float mmax = -INFINITY;
+  // unrolled so that several splits' loads are in flight per thread
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, part_ml[(slot0 + s) * 2 * kQRows + ql]);
   float denom = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 8
   for (int s = 0; s < ns; ++s) {
     const float* pm = part_ml + (slot0 + s) * 2 * kQRows;
     const float w = fast_exp2(pm[ql] - mmax);
@@ -919,14 +922,16 @@ __global__ __launch_bounds__(kMergeThreads) void k_decode_merge(
 }
 
 // KV tiles per split: 32 (2048 keys) when the launch has plenty of
-// workgroups; halved (down to 4) while the grid has fewer than 1024, so that
+// workgroups; halved (down to 8) while the grid has fewer than 1024, so that
 // small packed sets (few query tiles) still spread over every CU.  Roughly
-// half of a causal grid exits at once (splits past a tile's last key).
+// half of a causal grid exits at once (splits past a tile's last key).  Below
+// 8 tiles a split's partial (66 KB per workgroup) costs more to write and
+// merge than its share of the keys costs to attend.
 int attn_split_tiles(int B, int n_tokens, const Shape& sh) {
   const long qk = static_cast<long>(plan_tiles(B, sh.group)) * sh.hkv;
   const int kv_tiles = (n_tokens + kKvTile - 1) / kKvTile;
   int st = 32;
-  while (st > 4 && qk * ((kv_tiles + st - 1) / st) < 1024) st /= 2;
+  while (st > 8 && qk * ((kv_tiles + st - 1) / st) < 1024) st /= 2;
   return st;
 }
 
