@@ -453,11 +453,15 @@ __global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
           if (kl > lim) s[sb][t] = -INFINITY;
         }
     }
-    float mt = -INFINITY;   // tile maximum of s + bias - m_eff
+    // tile maximum of s + bias - m_eff, as a tree (a chain of 16 dependent
+    // max3 instructions sat on the critical path)
+    float mx[8];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-      for (int t = 0; t < 16; ++t) mt = fmaxf(mt, s[sb][t]);
+    for (int i = 0; i < 8; ++i)
+      mx[i] = fmaxf(fmaxf(s[i >> 2][4 * (i & 3)], s[i >> 2][4 * (i & 3) + 1]),
+                    fmaxf(s[i >> 2][4 * (i & 3) + 2], s[i >> 2][4 * (i & 3) + 3]));
+    float mt = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
+                     fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
     mt = xor32_max(mt);
     // Lazy maximum: m_eff moves only when the tile exceeds it by more than 8
     // (log2 units) or is the query's first visible tile, so probabilities
@@ -487,11 +491,18 @@ __global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const float e = fast_exp2(s[sb][t]);
-        s[sb][t] = e;
-        l += e;
-      }
+      for (int t = 0; t < 16; ++t) s[sb][t] = fast_exp2(s[sb][t]);
+    // the tile's sum of P as a pairwise tree (not a chain of 32 dependent adds)
+    {
+      float ps[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ps[i] = s[i >> 3][2 * (i & 7)] + s[i >> 3][2 * (i & 7) + 1];
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) ps[i] = ps[i] + ps[i + w];
+      l += ps[0];
+    }
 
     // O^T += V^T P^T, four 16-key steps
     static_for<0, 4>([&](auto stc) {
