@@ -402,20 +402,67 @@ __device__ __forceinline__ uint32_t order_desc(float x) {
   return ~asc;
 }
 
-// inclusive block scan of one value per thread (kSelThreads threads)
-__device__ __forceinline__ int block_scan_incl(int v, int* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int off = 1; off < kSelThreads; off <<= 1) {
-    const int x = tid >= off ? sh[tid - off] : 0;
-    __syncthreads();
-    sh[tid] += x;
-    __syncthreads();
+// Block-wide primitives for the 1024-thread selection workgroup: a wave-level
+// pass (shuffles), 16 per-wave partials in LDS, one more wave-level pass.
+// Each costs two barriers, where a tree over 1024 LDS slots costs twenty.
+constexpr int kSelWaves = kSelThreads / 64;
+
+// inclusive block scan of one value per thread; *total receives the sum
+__device__ __forceinline__ int block_scan_incl(int v, int* sh, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(v, off, 64);
+    if (lane >= off) v += y;
   }
-  const int res = sh[tid];
+  if (lane == 63) sh[wave] = v;
+  __syncthreads();
+  if (wave == 0) {
+    int t = lane < kSelWaves ? sh[lane] : 0;
+#pragma unroll
+    for (int off = 1; off < kSelWaves; off <<= 1) {
+      const int y = __shfl_up(t, off, 64);
+      if (lane >= off) t += y;
+    }
+    if (lane < kSelWaves) sh[kSelWaves + lane] = t;   // inclusive wave totals
+  }
+  __syncthreads();
+  const int res = v + (wave > 0 ? sh[kSelWaves + wave - 1] : 0);
+  *total = sh[2 * kSelWaves - 1];
   __syncthreads();
   return res;
+}
+
+__device__ __forceinline__ float block_max(float v, float* sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  v = wave_max(v);
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  float m = sh[0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) m = fmaxf(m, sh[w]);
+  __syncthreads();
+  return m;
+}
+
+// the largest v, the lowest i among equal largest values
+__device__ __forceinline__ int block_argmax_first(float v, int i, float* shv, int* shi) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(v, off, 64);
+    const int oi = __shfl_xor(i, off, 64);
+    if (ov > v || (ov == v && oi < i)) { v = ov; i = oi; }
+  }
+  if (lane == 0) { shv[wave] = v; shi[wave] = i; }
+  __syncthreads();
+  float bv = shv[0];
+  int bi = shi[0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w)
+    if (shv[w] > bv || (shv[w] == bv && shi[w] < bi)) { bv = shv[w]; bi = shi[w]; }
+  __syncthreads();
+  return bi;
 }
 
 __global__ __launch_bounds__(kSelThreads) void k_sur_select(
@@ -426,6 +473,7 @@ __global__ __launch_bounds__(kSelThreads) void k_sur_select(
   __shared__ unsigned long long key[kSurMaxUnits];   // (order_desc(score), unit)
   __shared__ int rank[kSurMaxUnits];
   __shared__ int scan[kSelThreads];
+  __shared__ int s_incl[kSelThreads], s_st[kSelThreads];   // T layout when U <= kSelThreads
   __shared__ int s_k, s_w, s_ws, s_err, s_bad;
   __shared__ float s_best[kSelThreads];
   const int tid = threadIdx.x;
@@ -442,27 +490,55 @@ __global__ __launch_bounds__(kSelThreads) void k_sur_select(
     if (tid == 0) { counts[0] = 0; counts[1] = 0; counts[2] = KVR_ERR_BAD_BLOCKS; }
     return;
   }
-  // rank the units: bitonic sort of (score descending, unit ascending)
-  int P2 = 1;
-  while (P2 < U) P2 <<= 1;
-  for (int i = tid; i < P2; i += kSelThreads)
-    key[i] = i < U ? (static_cast<unsigned long long>(order_desc(uscore[i])) << 32) | static_cast<unsigned>(i)
-                   : ~0ull;
-  __syncthreads();
-  for (int k = 2; k <= P2; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P2; i += kSelThreads) {
-        const int l = i ^ j;
-        if (l > i) {
-          const unsigned long long x = key[i], y = key[l];
-          const bool up = (i & k) == 0;
-          if ((x > y) == up) { key[i] = y; key[l] = x; }
-        }
-      }
-      __syncthreads();
+  // rank the units by (score descending, unit ascending); key[i] becomes the
+  // i-th unit in that order.  Up to kSelThreads units: each unit counts the
+  // keys below its own (keys are distinct); beyond: bitonic sort.
+  if (U <= kSelThreads) {
+    unsigned long long mine = 0;
+    if (tid < U) {
+      mine = (static_cast<unsigned long long>(order_desc(uscore[tid])) << 32) | static_cast<unsigned>(tid);
+      key[tid] = mine;
     }
-  for (int i = tid; i < U; i += kSelThreads) rank[static_cast<int>(key[i] & 0xffffffffu)] = i;
-  __syncthreads();
+    __syncthreads();
+    // tpu threads per unit (a power of two up to 64) share the counting
+    int tpu = 1;
+    while (tpu < 64 && 2 * tpu * U <= kSelThreads) tpu *= 2;
+    const int cu = tid / tpu, cq = tid % tpu;
+    const unsigned long long ck = cu < U ? key[cu] : 0ull;
+    int below = 0;
+    if (cu < U) {
+#pragma unroll 8
+      for (int v = cq; v < U; v += tpu) below += key[v] < ck ? 1 : 0;
+    }
+    for (int off = 1; off < tpu; off <<= 1) below += __shfl_xor(below, off, 64);
+    __syncthreads();
+    if (cu < U && cq == 0) {
+      key[below] = ck;
+      rank[cu] = below;
+    }
+    __syncthreads();
+  } else {
+    int P2 = 1;
+    while (P2 < U) P2 <<= 1;
+    for (int i = tid; i < P2; i += kSelThreads)
+      key[i] = i < U ? (static_cast<unsigned long long>(order_desc(uscore[i])) << 32) | static_cast<unsigned>(i)
+                     : ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= P2; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P2; i += kSelThreads) {
+          const int l = i ^ j;
+          if (l > i) {
+            const unsigned long long x = key[i], y = key[l];
+            const bool up = (i & k) == 0;
+            if ((x > y) == up) { key[i] = y; key[l] = x; }
+          }
+        }
+        __syncthreads();
+      }
+    for (int i = tid; i < U; i += kSelThreads) rank[static_cast<int>(key[i] & 0xffffffffu)] = i;
+    __syncthreads();
+  }
   // fill: the first ranked unit whose length exceeds the remaining allowance
   if (tid == 0) { s_k = U; s_w = 0; }
   __syncthreads();
@@ -474,13 +550,13 @@ __global__ __launch_bounds__(kSelThreads) void k_sur_select(
       const int u = static_cast<int>(key[i] & 0xffffffffu);
       len = ((u + 1 < U) ? ustart[u + 1] : S) - ustart[u];
     }
-    const int incl = block_scan_incl(len, scan) + carry;
+    int chunk;
+    const int incl = block_scan_incl(len, scan, &chunk) + carry;
     if (i < U && incl > budget && incl - len <= budget) {   // exactly one such i
       s_k = i;
       s_w = budget - (incl - len);
     }
-    carry += scan[kSelThreads - 1];   // this chunk's total
-    __syncthreads();
+    carry += chunk;
   }
   __syncthreads();
   const int k = s_k, w = s_w;   // units of rank < k are whole; rank k gets a width-w window
@@ -497,22 +573,25 @@ __global__ __launch_bounds__(kSelThreads) void k_sur_select(
     // max(e_t, e^(-1/16) u_{t-1}) in order by one thread
     float m = -INFINITY;
     for (int t = tid; t < wlen; t += kSelThreads) m = fmaxf(m, r[wa + t]);
-    s_best[tid] = m;
-    __syncthreads();
-    for (int off = kSelThreads / 2; off > 0; off >>= 1) {
-      if (tid < off) s_best[tid] = fmaxf(s_best[tid], s_best[tid + off]);
-      __syncthreads();
-    }
-    const float rmax = s_best[0];
-    __syncthreads();
+    const float rmax = block_max(m, s_best);
     for (int t = tid; t < wlen; t += kSelThreads) e[t] = expf(r[wa + t] - rmax);
     __syncthreads();
     if (tid == 0) {
+      // batches of 16: the loads issued together, the recurrence in registers
       const float c = 0.939413062813475786f;   // e^(-1/16) rounded to float32
       float prev = 0.f;
-      for (int t = 0; t < wlen; ++t) {
-        prev = fmaxf(e[t], c * prev);
-        e[t] = prev;
+      for (int base = 0; base < wlen; base += 16) {
+        float x[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) x[j] = base + j < wlen ? e[base + j] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          prev = fmaxf(x[j], c * prev);
+          x[j] = prev;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (base + j < wlen) e[base + j] = x[j];
       }
     }
     __syncthreads();
@@ -529,46 +608,60 @@ __global__ __launch_bounds__(kSelThreads) void k_sur_select(
     int bi = 0x7fffffff;
     for (int a = tid; a <= wlen - w; a += kSelThreads)
       if (sums[a] > bs) { bs = sums[a]; bi = a; }
-    __syncthreads();
-    s_best[tid] = bs;
-    scan[tid] = bi;
-    __syncthreads();
-    for (int off = kSelThreads / 2; off > 0; off >>= 1) {
-      if (tid < off) {
-        const float v = s_best[tid + off];
-        const int j = scan[tid + off];
-        if (v > s_best[tid] || (v == s_best[tid] && j < scan[tid])) {
-          s_best[tid] = v;
-          scan[tid] = j;
-        }
-      }
-      __syncthreads();
-    }
-    if (tid == 0) s_ws = scan[0];
+    const int best = block_argmax_first(bs, bi, s_best, scan);
+    if (tid == 0) s_ws = best;
     __syncthreads();
   }
   const int ws = (wu >= 0) ? s_ws : 0;
   // chosen ranges in position order -> T
-  carry = 0;
-  for (int base = 0; base < U; base += kSelThreads) {
-    const int u = base + tid;
+  int total = 0;
+  if (U <= kSelThreads) {
+    // offsets of every unit's range, then each output slot finds its unit
     int len = 0, st = 0;
-    if (u < U) {
-      const int a = ustart[u];
-      const int n = ((u + 1 < U) ? ustart[u + 1] : S) - a;
-      if (rank[u] < k) { len = n; st = a; }
-      else if (u == wu) { len = w; st = a + ws; }
+    if (tid < U) {
+      const int a = ustart[tid];
+      const int n = ((tid + 1 < U) ? ustart[tid + 1] : S) - a;
+      if (rank[tid] < k) { len = n; st = a; }
+      else if (tid == wu) { len = w; st = a + ws; }
     }
-    const int incl = block_scan_incl(len, scan) + carry;
-    const int off = incl - len;
-    if (off + len > cap) atomicOr(&s_bad, 1);
-    else
-      for (int j = 0; j < len; ++j) T[off + j] = pos0 + st + j;
-    carry = scan[kSelThreads - 1] + carry;
+    const int incl = block_scan_incl(len, scan, &total);
+    s_incl[tid] = incl;
+    s_st[tid] = st - (incl - len);   // position of slot i in this unit: s_st + i
     __syncthreads();
+    if (total > cap) {
+      if (tid == 0) s_bad = 1;
+    } else {
+      for (int i = tid; i < total; i += kSelThreads) {
+        int lo = 0, hi = U - 1;   // first unit with incl > i
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (s_incl[mid] > i) hi = mid; else lo = mid + 1;
+        }
+        T[i] = pos0 + s_st[lo] + i;
+      }
+    }
+  } else {
+    carry = 0;
+    for (int base = 0; base < U; base += kSelThreads) {
+      const int u = base + tid;
+      int len = 0, st = 0;
+      if (u < U) {
+        const int a = ustart[u];
+        const int n = ((u + 1 < U) ? ustart[u + 1] : S) - a;
+        if (rank[u] < k) { len = n; st = a; }
+        else if (u == wu) { len = w; st = a + ws; }
+      }
+      int chunk;
+      const int incl = block_scan_incl(len, scan, &chunk) + carry;
+      const int off = incl - len;
+      if (off + len > cap) atomicOr(&s_bad, 1);
+      else
+        for (int j = 0; j < len; ++j) T[off + j] = pos0 + st + j;
+      carry += chunk;
+    }
+    total = carry;
   }
   __syncthreads();
-  const int total = carry;
   if (s_bad || total != budget) {
     if (tid == 0) { counts[0] = total; counts[1] = 0; counts[2] = KVR_ERR_CAPACITY; }
     return;
@@ -581,13 +674,13 @@ __global__ __launch_bounds__(kSelThreads) void k_sur_select(
   for (int base = 0; base < total; base += kSelThreads) {
     const int i = base + tid;
     const int is_start = (i < total && (i == 0 || T[i] != T[i - 1] + 1)) ? 1 : 0;
-    const int incl = block_scan_incl(is_start, scan) + carry;
+    int chunk;
+    const int incl = block_scan_incl(is_start, scan, &chunk) + carry;
     if (is_start) {
       run_start[incl - 1] = T[i];
       run_len[incl - 1] = i;
     }
-    carry += scan[kSelThreads - 1];
-    __syncthreads();
+    carry += chunk;
   }
   const int R = carry;
   __threadfence_block();

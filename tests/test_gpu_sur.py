@@ -148,6 +148,19 @@ def test_sur_select_random_partitions_and_ties():
         _check_select(r_np, starts, B, pos0, T, rs, rl, us)
 
 
+@pytest.mark.parametrize("S,n_units,B", [(20000, 1500, 900), (40000, 5000, 23457), (3000, 1024, 1500),
+                                         (3000, 1025, 1499)])
+def test_sur_select_many_units(S, n_units, B):
+    """Above 1024 units the ranking is a bitonic sort and T is written per
+    unit; at or below, ranking by counting and T by binary search."""
+    m = kvr()
+    rng = np.random.default_rng(S + n_units)
+    r_np = (np.round(rng.standard_normal(S) * 8) / 8).astype(np.float32)
+    starts = [0] + sorted(rng.choice(np.arange(1, S), size=n_units - 1, replace=False).tolist())
+    T, rs, rl, us = _gpu_select(m, torch.from_numpy(r_np).cuda(), starts, B, 11)
+    _check_select(r_np, starts, B, 11, T, rs, rl, us)
+
+
 def test_sur_select_rejects_bad_units():
     m = kvr()
     r = torch.zeros(50, dtype=torch.float32, device="cuda")
