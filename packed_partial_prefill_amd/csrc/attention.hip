@@ -100,8 +100,6 @@ __global__ __launch_bounds__(64) void k_attn_rowwise(const T* __restrict__ q,
 // ---------------------------------------------------------------------------
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
-typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
-typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kQRows = KVR_ATTN_QROWS;     // 128 pairs per workgroup
@@ -164,11 +162,6 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
-}
-
 // ds_read_b64_tr_b16 at LDS byte address addr + OFF.  Written as inline
 // assembly because the compiler places a wait for every outstanding LDS DMA
 // in front of the builtin form (it cannot tell that the DMA in flight
@@ -181,27 +174,7 @@ __device__ __forceinline__ u32x2_t ds_read_tr16(uint32_t addr) {
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
   return r;
 }
-__device__ __forceinline__ void lds_wait() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
-}
-template <int N> __device__ __forceinline__ void lds_wait_n() {
-  static_assert(N >= 0 && N < 16, "lgkmcnt");
-  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));   // at most N LDS operations outstanding
-}
-// The compiler does not know that an assembly LDS read's result is valid
-// only after the lgkmcnt wait: after waiting, pass every such result through
-// reg_fence, which the compiler must order after the wait (both are volatile)
-// and which every use of the value then depends on.
-template <typename T> __device__ __forceinline__ void reg_fence(T& r) { asm volatile("" : "+v"(r)); }
-
-// ds_read_b128 / ds_read_u8 at addr + OFF (see ds_read_tr16 for why assembly).
-template <int OFF>
-__device__ __forceinline__ u32x4_t ds_read_b128(uint32_t addr) {
-  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
-  u32x4_t r;
-  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
-  return r;
-}
+// ds_read_u8 at addr + OFF (see ds_read_tr16 for why assembly).
 template <int OFF>
 __device__ __forceinline__ uint32_t ds_read_u8(uint32_t addr) {
   static_assert(OFF >= 0 && OFF < 65536, "ds offset field");

@@ -40,6 +40,38 @@ __device__ __forceinline__ int xcd_linear(int b, int total) {
   return xcd * q + min(xcd, rem) + b / kXcds;
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+// LDS reads issued as inline assembly, for loops that keep LDS DMA in flight
+// into other buffers: the compiler cannot tell such reads from the DMA and
+// places a wait for all outstanding DMA (or for all LDS operations) in front
+// of its own forms.  The caller waits with lds_wait / lds_wait_n and then
+// passes each result through reg_fence.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)(p)));
+}
+__device__ __forceinline__ void lds_wait() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); vmcnt and expcnt not waited for
+}
+template <int N> __device__ __forceinline__ void lds_wait_n() {
+  static_assert(N >= 0 && N < 16, "lgkmcnt");
+  __builtin_amdgcn_s_waitcnt(0xC07F | (N << 8));   // at most N LDS operations outstanding
+}
+// An assembly LDS read's result is valid only after the lgkmcnt wait; the
+// compiler must order reg_fence after the wait (both are volatile) and every
+// use of the value then depends on it.
+template <typename T> __device__ __forceinline__ void reg_fence(T& r) { asm volatile("" : "+v"(r)); }
+// ds_read_b128 at LDS byte address addr + OFF
+template <int OFF = 0>
+__device__ __forceinline__ u32x4_t ds_read_b128(uint32_t addr) {
+  static_assert(OFF >= 0 && OFF < 65536, "ds offset field");
+  u32x4_t r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+
 // Combine x with the value of lane ^ 32: v_permlane32_swap exchanges the
 // wave's two 32-lane halves in one VALU instruction, leaving each lane its
 // own value and its partner's (in either order), where __shfl_xor would take

@@ -151,18 +151,18 @@ struct Tile {
   static_assert(TN % 2 == 0, "gate and up blocks pair up in the fused SwiGLU epilogue");
   static_assert(NS >= 3 && NS <= 6 && (NS - 2) * LS < 64, "pipeline depth and vmcnt range");
   static_assert(NS * (ABytes + WBytes) * OCC_ <= 160 * 1024, "LDS per CU");
+  // one dynamic LDS buffer: the NS A stages, then the NS W stages, so that a
+  // fragment address is a lane register plus a compile-time offset
+  static constexpr int aOff(int s) { return s * ABytes; }
+  static constexpr int wOff(int s) { return NS * ABytes + s * WBytes; }
+  static constexpr int smem = NS * (ABytes + WBytes);
+  static_assert((NS - 1) * ABytes < 65536 && (NS - 1) * WBytes < 65536, "ds offset field");
 };
 
 // The tile shapes the library launches.
 using TileL = Tile<256, 256, 4, 2, 4, 1>;
 using TileM = Tile<128, 128, 2, 2, 4, 2>;
 using TileS = Tile<64, 128, 1, 2, 6, 2>;
-
-template <class C>
-struct Stages {
-  uint8_t* a[C::NS];
-  uint8_t* w[C::NS];
-};
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * (KB * 2) + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -183,76 +183,116 @@ struct GemmThread {
   const bf16_t* asrc[C::LA];   // this lane's global source (A), at the split's first k
   const bf16_t* wsrc[C::LW];   // ... (W)
   int adst[C::LA], wdst[C::LW];  // wave-uniform LDS byte offset of each 1 KB slice
-  int arow[C::TM], wrow[C::TN];
-  int khalf;
+  uint32_t la[C::TM][2], lw[C::TN][2];   // fragment LDS addresses in stage 0, per K half
+  uint8_t* smem;
 };
 
 template <class C, int S>
-__device__ __forceinline__ void issue_stage(const GemmThread<C>& g, const Stages<C>& st, int kb) {
+__device__ __forceinline__ void issue_stage(const GemmThread<C>& g, int kb) {
 #pragma unroll
   for (int j = 0; j < C::LA; ++j)
-    __builtin_amdgcn_global_load_lds(KVR_GLB(g.asrc[j] + kb), KVR_LDS(st.a[S] + g.adst[j]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(KVR_GLB(g.asrc[j] + kb), KVR_LDS(g.smem + C::aOff(S) + g.adst[j]),
+                                     16, 0, 0);
 #pragma unroll
   for (int j = 0; j < C::LW; ++j)
-    __builtin_amdgcn_global_load_lds(KVR_GLB(g.wsrc[j] + kb), KVR_LDS(st.w[S] + g.wdst[j]), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(KVR_GLB(g.wsrc[j] + kb), KVR_LDS(g.smem + C::wOff(S) + g.wdst[j]),
+                                     16, 0, 0);
 }
 
-template <class C, int S>
-__device__ __forceinline__ void mma_half(const GemmThread<C>& g, const Stages<C>& st, int ks,
-                                         f32x16_t (&acc)[C::TM][C::TN]) {
-  const uint8_t* a = st.a[S];
-  const uint8_t* w = st.w[S];
-  const int chunk = ks * 2 + g.khalf;
-  bf16x8_t fa[C::TM], fw[C::TN];
+// Operand fragments of one 16-wide K half of a stage.
+template <class C>
+struct Frags {
+  bf16x8_t a[C::TM], w[C::TN];
+};
+
+// Reads of the main loop are inline assembly (the compiler's lgkmcnt
+// tracking across the stage pipeline waits for every outstanding LDS read
+// before the first product); a step waits for the older half with
+// lds_wait_n<TM + TN> while the newer half's reads stay in flight.
+template <class C, int S, int KS>
+__device__ __forceinline__ void load_frags(const GemmThread<C>& g, Frags<C>& f) {
 #pragma unroll
-  for (int mb = 0; mb < C::TM; ++mb) fa[mb] = *reinterpret_cast<const bf16x8_t*>(a + swz(g.arow[mb], chunk));
+  for (int mb = 0; mb < C::TM; ++mb)
+    f.a[mb] = __builtin_bit_cast(bf16x8_t, ds_read_b128<S * C::ABytes>(g.la[mb][KS]));
 #pragma unroll
-  for (int nb = 0; nb < C::TN; ++nb) fw[nb] = *reinterpret_cast<const bf16x8_t*>(w + swz(g.wrow[nb], chunk));
+  for (int nb = 0; nb < C::TN; ++nb)
+    f.w[nb] = __builtin_bit_cast(bf16x8_t, ds_read_b128<S * C::WBytes>(g.lw[nb][KS]));
+}
+
+// the fragments read before the last TM + TN reads have landed
+template <class C>
+__device__ __forceinline__ void frags_ready(Frags<C>& f) {
+  lds_wait_n<C::TM + C::TN>();
+#pragma unroll
+  for (int mb = 0; mb < C::TM; ++mb) reg_fence(f.a[mb]);
+#pragma unroll
+  for (int nb = 0; nb < C::TN; ++nb) reg_fence(f.w[nb]);
+}
+
+template <class C>
+__device__ __forceinline__ void mma(const Frags<C>& f, f32x16_t (&acc)[C::TM][C::TN]) {
 #pragma unroll
   for (int mb = 0; mb < C::TM; ++mb)
 #pragma unroll
     for (int nb = 0; nb < C::TN; ++nb)
-      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fw[nb], acc[mb][nb], 0, 0, 0);
+      acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[mb], f.w[nb], acc[mb][nb], 0, 0, 0);
 }
 
-// One K step on stage S (its data was certified by the previous barrier):
-// the first 16-wide half is read and its MFMAs issued; then, with those in
-// flight, wait until the next stage's DMA has landed (NS - 3 newer stages may
-// stay in flight), barrier (every wave is past the previous stage), refill
-// the previous stage's buffers with the step NS - 1 ahead (clamped to the last
-// step: a refill past the end is never read), and run the second half.
-template <class C, int S>
-__device__ __forceinline__ void k_step(const GemmThread<C>& g, const Stages<C>& st, int i,
-                                       int nsteps, f32x16_t (&acc)[C::TM][C::TN]) {
-  mma_half<C, S>(g, st, 0, acc);
-  wait_vmcnt<(C::NS - 3) * C::LS>();
+// Barrier between the stage waits and the stage reads/refills; the empty asm
+// statements keep the compiler from moving LDS reads or DMA across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
-  issue_stage<C, (S + C::NS - 1) % C::NS>(g, st, min(i + C::NS - 1, nsteps - 1) * KB);
-  mma_half<C, S>(g, st, 1, acc);
+  asm volatile("" ::: "memory");
+}
+
+// One K step on stage S, software-pipelined over the two 16-wide halves:
+// f0 arrives holding half 0 of stage S (read during the previous step).
+// Half 1's reads are issued, then half 0 multiplies while they land; then
+// wait until the next stage's DMA has landed (NS - 3 newer stages may stay
+// in flight) and barrier (every wave is past the previous stage), refill the
+// previous stage's buffers with the step NS - 1 ahead (clamped to the last
+// step: a refill past the end is never read), read half 0 of the next stage
+// into f0, and multiply half 1 while those land.
+template <class C, int S>
+__device__ __forceinline__ void k_step(const GemmThread<C>& g, int i,
+                                       int nsteps, f32x16_t (&acc)[C::TM][C::TN], Frags<C>& f0,
+                                       Frags<C>& f1) {
+  load_frags<C, S, 1>(g, f1);
+  frags_ready<C>(f0);
+  mma<C>(f0, acc);
+  wait_vmcnt<(C::NS - 3) * C::LS>();
+  stage_barrier();
+  issue_stage<C, (S + C::NS - 1) % C::NS>(g, min(i + C::NS - 1, nsteps - 1) * KB);
+  load_frags<C, (S + 1) % C::NS, 0>(g, f0);   // unused after the last step (in bounds)
+  frags_ready<C>(f1);
+  mma<C>(f1, acc);
 }
 
 // NS consecutive steps starting on stage S = 0.
 template <class C, int S>
-__device__ __forceinline__ void k_round(const GemmThread<C>& g, const Stages<C>& st, int i,
-                                        int nsteps, f32x16_t (&acc)[C::TM][C::TN]) {
-  k_step<C, S>(g, st, i + S, nsteps, acc);
-  if constexpr (S + 1 < C::NS) k_round<C, S + 1>(g, st, i, nsteps, acc);
+__device__ __forceinline__ void k_round(const GemmThread<C>& g, int i,
+                                        int nsteps, f32x16_t (&acc)[C::TM][C::TN], Frags<C>& f0,
+                                        Frags<C>& f1) {
+  k_step<C, S>(g, i + S, nsteps, acc, f0, f1);
+  if constexpr (S + 1 < C::NS) k_round<C, S + 1>(g, i, nsteps, acc, f0, f1);
 }
 
 // The last nsteps - i (< NS) steps.
 template <class C, int S>
-__device__ __forceinline__ void k_tail(const GemmThread<C>& g, const Stages<C>& st, int i,
-                                       int nsteps, f32x16_t (&acc)[C::TM][C::TN]) {
+__device__ __forceinline__ void k_tail(const GemmThread<C>& g, int i,
+                                       int nsteps, f32x16_t (&acc)[C::TM][C::TN], Frags<C>& f0,
+                                       Frags<C>& f1) {
   if (i + S < nsteps) {
-    k_step<C, S>(g, st, i + S, nsteps, acc);
-    if constexpr (S + 2 < C::NS) k_tail<C, S + 1>(g, st, i, nsteps, acc);
+    k_step<C, S>(g, i + S, nsteps, acc, f0, f1);
+    if constexpr (S + 2 < C::NS) k_tail<C, S + 1>(g, i, nsteps, acc, f0, f1);
   }
 }
 
 template <class C, int S>
-__device__ __forceinline__ void k_prologue(const GemmThread<C>& g, const Stages<C>& st, int nsteps) {
-  issue_stage<C, S>(g, st, min(S, nsteps - 1) * KB);
-  if constexpr (S + 2 < C::NS) k_prologue<C, S + 1>(g, st, nsteps);
+__device__ __forceinline__ void k_prologue(const GemmThread<C>& g, int nsteps) {
+  issue_stage<C, S>(g, min(S, nsteps - 1) * KB);
+  if constexpr (S + 2 < C::NS) k_prologue<C, S + 1>(g, nsteps);
 }
 
 // MODE 0: part[split][M][N] = A * W^T over this split's K range (W segmented).
@@ -265,17 +305,7 @@ __global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
     const bf16_t* __restrict__ A, WeightSegs W, int M, int N, int K, int k_per_split,
     int tiles_m, int tiles_n, int splits, float* __restrict__ part, bf16_t* __restrict__ out) {
   constexpr int TM = C::TM, TN = C::TN, BM = C::BM, BN = C::BN;
-  __shared__ __attribute__((aligned(16))) uint8_t a0[C::ABytes], a1[C::ABytes], a2[C::ABytes],
-      a3[C::ABytes], a4[C::NS > 4 ? C::ABytes : 16], a5[C::NS > 5 ? C::ABytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t w0[C::WBytes], w1[C::WBytes], w2[C::WBytes],
-      w3[C::WBytes], w4[C::NS > 4 ? C::WBytes : 16], w5[C::NS > 5 ? C::WBytes : 16];
-  Stages<C> st;
-  {
-    uint8_t* as[6] = {a0, a1, a2, a3, a4, a5};
-    uint8_t* ws[6] = {w0, w1, w2, w3, w4, w5};
-#pragma unroll
-    for (int s = 0; s < C::NS; ++s) { st.a[s] = as[s]; st.w[s] = ws[s]; }
-  }
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
 
   // XCD-aware order: t = ((split * tiles_n) + n) * tiles_m + m
   const int total = tiles_m * tiles_n * splits;
@@ -319,14 +349,21 @@ __global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
     }
     g.wsrc[j] = wr + k0 + chunk * 8;
   }
+  g.smem = smem;
+  const int khalf = lane >> 5;
 #pragma unroll
-  for (int mb = 0; mb < TM; ++mb) g.arow[mb] = (wm * TM + mb) * 32 + (lane & 31);
+  for (int mb = 0; mb < TM; ++mb) {
+    const int arow = (wm * TM + mb) * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) g.la[mb][ks] = lds_addr(smem) + C::aOff(0) + swz(arow, ks * 2 + khalf);
+  }
 #pragma unroll
   for (int nb = 0; nb < TN; ++nb) {
-    if (MODE == 0) g.wrow[nb] = (wn * TN + nb) * 32 + (lane & 31);
-    else g.wrow[nb] = (nb < TN / 2 ? 0 : BN / 2) + (wn * (TN / 2) + nb % (TN / 2)) * 32 + (lane & 31);
+    const int wrow = MODE == 0 ? (wn * TN + nb) * 32 + (lane & 31)
+                               : (nb < TN / 2 ? 0 : BN / 2) + (wn * (TN / 2) + nb % (TN / 2)) * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) g.lw[nb][ks] = lds_addr(smem) + C::wOff(0) + swz(wrow, ks * 2 + khalf);
   }
-  g.khalf = lane >> 5;
 
   f32x16_t acc[TM][TN];
 #pragma unroll
@@ -337,17 +374,19 @@ __global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
       for (int e = 0; e < 16; ++e) acc[mb][nb][e] = 0.f;
 
   if (nsteps > 0) {
-    k_prologue<C, 0>(g, st, nsteps);            // stages 0 .. NS-2
+    k_prologue<C, 0>(g, nsteps);                // stages 0 .. NS-2
     wait_vmcnt<(C::NS - 2) * C::LS>();          // stage 0 landed; the rest may be in flight
-    __builtin_amdgcn_s_barrier();
+    stage_barrier();
+    Frags<C> f0, f1;
+    load_frags<C, 0, 0>(g, f0);
     int i = 0;
-    for (; i + C::NS <= nsteps; i += C::NS) k_round<C, 0>(g, st, i, nsteps, acc);
-    k_tail<C, 0>(g, st, i, nsteps, acc);
+    for (; i + C::NS <= nsteps; i += C::NS) k_round<C, 0>(g, i, nsteps, acc, f0, f1);
+    k_tail<C, 0>(g, i, nsteps, acc, f0, f1);
     wait_vmcnt<0>();
+    lds_wait();   // the unused reads after the last step
   }
 
   // epilogue
-  const int khalf = g.khalf;
 #pragma unroll
   for (int mb = 0; mb < TM; ++mb) {
 #pragma unroll
@@ -407,8 +446,15 @@ void launch_mfma(const bf16_t* A, const WeightSegs& W, int M, int N, int K, int 
   const int kps = ((K / splits + KB - 1) / KB) * KB;
   const int tm = (M + C::BM - 1) / C::BM;
   const int tn = MODE == 1 ? (N + C::BN / 2 - 1) / (C::BN / 2) : (N + C::BN - 1) / C::BN;
-  hipLaunchKernelGGL((k_gemm_mfma<MODE, C>), dim3(tm * tn * splits), dim3(C::threads), 0, stream,
-                     A, W, M, N, K, kps, tm, tn, splits, part, out);
+  static bool attr = false;
+  if (!attr) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm_mfma<MODE, C>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, C::smem) != hipSuccess)
+      return;   // the launch below then reports the error
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_gemm_mfma<MODE, C>), dim3(tm * tn * splits), dim3(C::threads), C::smem,
+                     stream, A, W, M, N, K, kps, tm, tn, splits, part, out);
 }
 
 template <int MODE>
