@@ -393,28 +393,63 @@ __global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
     const bool ahead = c + kAttnStages - 1 < c1;
     if (ahead) issue(c + kAttnStages - 1, std::integral_constant<int, NXT>{});
 
-    // S^T = K Q^T + (bias - m_eff) for the two 32-key halves of the tile
+    // S^T = K Q^T + (bias - m_eff) for the two 32-key halves of the tile.
+    // The K fragments come in groups of KG 16-wide K slices, each group read
+    // while the previous group's products run (two register buffers).
+    constexpr int KG = 4, GPS = D / 16 / KG, NG = 2 * GPS;   // groups per half, in all
     f32x16_t s[2];
-    static_for<0, 2>([&](auto sbc) {
-      constexpr int sb = decltype(sbc)::value;
-      u32x4_t ka[D / 16];
-      static_for<0, D / 16>([&](auto ksc) {
-        constexpr int ks = decltype(ksc)::value;
-        ka[ks] = ds_read_b128<L::kOff(BUF) + sb * 32 * D * 2>(klane[ks]);
+    uint32_t fb[2];
+    fb[0] = ds_read_u8<BUF * L::fBytes>(flane);
+    fb[1] = ds_read_u8<BUF * L::fBytes + 32>(flane);
+    u32x4_t kb[2][KG];
+    auto kread = [&](auto gic, u32x4_t(&dst)[KG]) {
+      constexpr int gi = decltype(gic)::value, sb = gi / GPS, kq = gi % GPS;
+      static_for<0, KG>([&](auto jc) {
+        constexpr int j = decltype(jc)::value;
+        dst[j] = ds_read_b128<L::kOff(BUF) + sb * 32 * D * 2>(klane[kq * KG + j]);
       });
-      uint32_t fb = ds_read_u8<BUF * L::fBytes + sb * 32>(flane);
-      lds_wait();
+    };
+    kread(std::integral_constant<int, 0>{}, kb[0]);
+    static_for<0, NG>([&](auto gic) {
+      constexpr int gi = decltype(gic)::value, sb = gi / GPS, kq = gi % GPS;
+      if constexpr (gi + 1 < NG) {
+        kread(std::integral_constant<int, gi + 1>{}, kb[(gi + 1) & 1]);
+        lds_wait_n<KG>();   // this group (and the flag bytes) landed
+      } else {
+        lds_wait();
+      }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) reg_fence(ka[ks]);
-      reg_fence(fb);
+      for (int j = 0; j < KG; ++j) reg_fence(kb[gi & 1][j]);
+      if constexpr (gi == 0) {
+        reg_fence(fb[0]);
+        reg_fence(fb[1]);
+      }
+      if constexpr (kq == 0) {
 #pragma unroll
-      for (int t = 0; t < 16; ++t) s[sb][t] = 0.f;
+        for (int t = 0; t < 16; ++t) s[sb][t] = 0.f;
+      }
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks)
-        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, ka[ks]),
-                                                         qf[ks], s[sb], 0, 0, 0);
-      s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_operand(fb), qx, s[sb], 0, 0, 0);
+      for (int j = 0; j < KG; ++j)
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kb[gi & 1][j]),
+                                                         qf[kq * KG + j], s[sb], 0, 0, 0);
+      if constexpr (kq == GPS - 1)
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_operand(fb[sb]), qx, s[sb], 0, 0, 0);
+      // keep this group's products ahead of the next group's wait (the
+      // scheduler would otherwise sink them past it)
+      __builtin_amdgcn_sched_barrier(0);
     });
+    // V^T operands of the first 16-key step, read while the softmax runs
+    u32x2_t xv[2][D / 32][2];
+    auto vread = [&](auto stc, u32x2_t(&dst)[D / 32][2]) {
+      constexpr int st = decltype(stc)::value, sb = st / 2, hs = st % 2;
+      constexpr int off = BUF * L::vBytes + (sb * 32 + hs * 16) * D * 2;
+      static_for<0, D / 32>([&](auto dbc) {
+        constexpr int db = decltype(dbc)::value;
+        dst[db][0] = ds_read_tr16<off>(vlane[db]);
+        dst[db][1] = ds_read_tr16<off + 8 * D * 2>(vlane[db]);
+      });
+    };
+    vread(std::integral_constant<int, 0>{}, xv[0]);
     // causal test only on partially visible tiles (uniform branch)
     if (c >= nf) {
       const int lim = u - c * kKvTile;   // keys kl > lim lie in the future
@@ -477,31 +512,31 @@ __global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
       l += ps[0];
     }
 
-    // O^T += V^T P^T, four 16-key steps
+    // O^T += V^T P^T, four 16-key steps.  Step st + 1's operands are read
+    // once step st's first column block has landed (at most 14 LDS reads
+    // outstanding), and each block's product waits only for its own reads.
     static_for<0, 4>([&](auto stc) {
-      constexpr int sb = decltype(stc)::value / 2, hs = decltype(stc)::value % 2;
-      constexpr int off = BUF * L::vBytes + (sb * 32 + hs * 16) * D * 2;
-      u32x2_t x[D / 32][2];
-      static_for<0, D / 32>([&](auto dbc) {
-        constexpr int db = decltype(dbc)::value;
-        x[db][0] = ds_read_tr16<off>(vlane[db]);
-        x[db][1] = ds_read_tr16<off + 8 * D * 2>(vlane[db]);
-      });
+      constexpr int st = decltype(stc)::value, sb = st / 2, hs = st % 2;
+      constexpr int NB = D / 32, NEXT = st + 1 < 4 ? 2 * NB : 0;
+      auto& x = xv[st & 1];
+      lds_wait_n<2 * (NB - 1)>();
+      reg_fence(x[0][0]);
+      reg_fence(x[0][1]);
+      if constexpr (st + 1 < 4) vread(std::integral_constant<int, st + 1>{}, xv[(st + 1) & 1]);
       bf16x8_t pb;
 #pragma unroll
       for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[sb][hs * 8 + i]);
-      lds_wait();
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        reg_fence(x[db][0]);
-        reg_fence(x[db][1]);
-      }
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
+      static_for<0, NB>([&](auto dbc) {
+        constexpr int db = decltype(dbc)::value;
+        if constexpr (db > 0) {
+          lds_wait_n<2 * (NB - 1 - db) + NEXT>();
+          reg_fence(x[db][0]);
+          reg_fence(x[db][1]);
+        }
         const u32x4_t w = {x[db][0][0], x[db][0][1], x[db][1][0], x[db][1][1]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb,
                                                          o[db], 0, 0, 0);
-      }
+      });
     });
 
     if (ahead && kAttnStages > 2)
@@ -551,6 +586,449 @@ __global__ __launch_bounds__(kAttnMfmaThreads, kAttnWgPerCu) void k_attn_mfma(
   }
 }
 
+// ---------------------------------------------------------------------------
+// Ping-pong form of the packed kernel (d = 128).  One workgroup of 8 waves
+// takes two neighbouring 128-pair query tiles of one KV group, so every KV
+// tile is staged in LDS once for 256 pairs.  Waves 0-3 (group A, the first
+// query tile) and 4-7 (group B, the second) share SIMDs pairwise and run the
+// same per-tile program one phase apart: a product phase (PV of the previous
+// tile, then the scores of this one) and a softmax phase.  Phases end at
+// workgroup barriers, so on every SIMD one wave's matrix products overlap the
+// other wave's softmax.  Per wave the arithmetic, and its order, is that of
+// k_attn_mfma.  Four LDS stages: tile i is read in phases 2i .. 2i+3 (scores,
+// then PV, each by both groups), and tile i + 2 is issued at phase 2i, four
+// phases before its first read.
+constexpr int kPPWaves = 8;
+constexpr int kPPThreads = 64 * kPPWaves;
+constexpr int kPPStages = 4;
+// stream-K ranges in XCD-contiguous runs (neighbouring pieces share KV tiles)
+constexpr bool kAttnXcdOrder = true;
+
+template <int D>
+struct PPLds {
+  static constexpr int kBytes = kKvTile * D * 2;
+  static constexpr int vBytes = kKvTile * D * 2;
+  static constexpr int fBytes = kKvTile;
+  static constexpr int total = kPPStages * (kBytes + vBytes + fBytes);
+  static constexpr int kOff(int b) { return b * kBytes; }
+  static constexpr int vOff(int b) { return kPPStages * kBytes + b * vBytes; }
+  static constexpr int fOff(int b) { return kPPStages * (kBytes + vBytes) + b * fBytes; }
+  static constexpr int slices = (kBytes + vBytes) / 1024 / kPPWaves;
+  static_assert((kBytes + vBytes) % (1024 * kPPWaves) == 0, "DMA slices per wave");
+  // immediate offsets: K reads up to kOff(3) + 32 rows, V reads (relative to
+  // vOff(0)) up to 3 stages + 64 rows
+  static_assert(kOff(kPPStages - 1) + kBytes <= 65536 && (kPPStages - 1) * vBytes + vBytes <= 65536,
+                "ds offset field");
+};
+
+template <int D>
+__global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
+    const uint8_t* __restrict__ flags, const int32_t* __restrict__ Tpos,
+    const int32_t* __restrict__ n_full, const int32_t* __restrict__ n_total, int n_qt, int B,
+    int n_tokens, int Hq, int Hkv, int G, float bias_local, float bias_sink, bool xcd_order,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  using L = PPLds<D>;
+  constexpr int KCH = D / 8;
+  constexpr int ROWS = 1024 / (D * 2);
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wave >> 2;   // 0: group A, 1: group B
+  const int P = B * G;
+
+  // This workgroup's share of the work (see attn_sk_range).
+  const int npairs = (n_qt + 1) / 2;
+  auto pair_len = [&](int j) __attribute__((always_inline)) {
+    const int a = n_total[2 * j];
+    return 2 * j + 1 < n_qt ? max(a, n_total[2 * j + 1]) : a;
+  };
+  int lsum = 0;
+  for (int j = 0; j < npairs; ++j) lsum += pair_len(j);
+  const long long T = static_cast<long long>(lsum) * Hkv;
+  // at most one workgroup per tile, so that every range is non-empty (the
+  // merge reads one piece from each workgroup between a segment's owners)
+  const int W = static_cast<int>(min(static_cast<long long>(gridDim.x), T));
+  const int w = xcd_order ? xcd_linear(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
+  if (w >= W) return;
+  const long long r0 = w * T / W, r1 = (w + 1) * T / W;
+
+  float m_eff = 0.f;
+  bool m_set = false;
+  bf16x8_t qx;
+  auto set_qx = [&](float mref) __attribute__((always_inline)) {
+    const bf16_t mh = f32_to_bf16(-mref);
+    const bf16_t ml = f32_to_bf16(-mref - bf16_to_f32(mh));
+    m_eff = -(bf16_to_f32(mh) + bf16_to_f32(ml));
+    const bf16_t one = 0x3F80;
+    const bf16_t v[8] = {one, one, mh, ml, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qx[i] = __builtin_bit_cast(__bf16, half == 0 ? v[i] : static_cast<bf16_t>(0));
+  };
+
+  const size_t kv_row = static_cast<size_t>(Hkv) * D;
+  const uint8_t* kg8 = nullptr;   // this piece's KV group
+  const uint8_t* vg8 = nullptr;
+  constexpr int KSL = kKvTile / ROWS;
+  const size_t row_bytes = kv_row * 2;
+  // DMA slices of this wave (waves 0-3 stage K, 4-7 stage V)
+  auto slice_isv = [&](int j) __attribute__((always_inline)) { return wave * L::slices + j >= KSL; };
+  uint32_t s_off[L::slices];
+  int s_dst[L::slices];
+#pragma unroll
+  for (int j = 0; j < L::slices; ++j) {
+    const int sl = wave * L::slices + j;
+    const int row = (sl >= KSL ? sl - KSL : sl) * ROWS + lane / KCH, phys = lane % KCH;
+    const int logical = slice_isv(j) ? vchunk<D>(row, phys) : kchunk<D>(row, phys);
+    s_off[j] = static_cast<uint32_t>(row * row_bytes) + logical * 16;
+    s_dst[j] = (slice_isv(j) ? L::vOff(0) : L::kOff(0)) + (sl >= KSL ? sl - KSL : sl) * 1024;
+  }
+  static_assert(L::kBytes == L::vBytes, "K and V stages advance by the same stride");
+  constexpr int kRsrcWord3 = 0x00020000;
+  // tile c into stage BUF (as k_attn_mfma: wave 0 also brings the flag bytes)
+  auto issue = [&](int c, auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    const int kv0 = c * kKvTile;
+    const int rows = min(kKvTile, n_tokens - kv0);
+    const int nbytes = rows * static_cast<int>(row_bytes);
+    if (wave == 0) {
+      if (rows == kKvTile) {
+        if (lane < kKvTile / 4) {
+          const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
+              const_cast<uint8_t*>(flags + kv0), 0, kKvTile, kRsrcWord3);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, KVR_LDS(lds + L::fOff(BUF)), 4, 4 * lane, 0,
+                                                   0, 0);
+        }
+      } else {
+        lds[L::fOff(BUF) + lane] = flags[min(kv0 + lane, n_tokens - 1)];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < L::slices; ++j) {
+      const uint8_t* base = (slice_isv(j) ? vg8 : kg8) + static_cast<size_t>(kv0) * row_bytes;
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, nbytes, kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, KVR_LDS(lds + BUF * L::kBytes + s_dst[j]), 16,
+                                               static_cast<int>(s_off[j]), 0, 0, 0);
+    }
+  };
+  // this wave's part of the oldest tile in flight has landed; with `newer`,
+  // the tile issued after it may still be in flight
+  auto wait_tile = [&](bool newer) __attribute__((always_inline)) {
+    if (newer) {
+      if (wave == 0)
+        attn_wait_vmcnt<L::slices + 1>();
+      else
+        attn_wait_vmcnt<L::slices>();
+    } else {
+      attn_wait_vmcnt<0>();
+    }
+  };
+
+  uint32_t klane[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    klane[ks] = lds_addr(lds) + L::kOff(0) + (lane & 31) * (D * 2) +
+                (kchunk<D>(lane & 31, ks * 2 + half) << 4);
+  const uint32_t flane = lds_addr(lds) + L::fOff(0) + (lane & 31);
+  auto bias_word = [&](float b) __attribute__((always_inline)) {
+    const bf16_t bh = f32_to_bf16(b);
+    const bf16_t bl = f32_to_bf16(b - bf16_to_f32(bh));
+    return half == 0 ? (static_cast<uint32_t>(bh) | (static_cast<uint32_t>(bl) << 16)) : 0u;
+  };
+  const uint32_t bw_l = bias_word(bias_local), bw_s = bias_word(bias_sink);
+  const uint32_t bw_ls = bias_word(bias_local + bias_sink);
+  const uint32_t bones = half == 0 ? 0x3F803F80u : 0u;
+  auto bias_operand = [&](uint32_t f) __attribute__((always_inline)) {
+    const uint32_t wl = (f & KVR_FLAG_SINK) ? bw_ls : bw_l;
+    const uint32_t wn = (f & KVR_FLAG_SINK) ? bw_s : 0u;
+    const uint32_t w = (f & KVR_FLAG_LOCAL) ? wl : wn;
+    const u32x4_t v = {w, bones, 0u, 0u};
+    return __builtin_bit_cast(bf16x8_t, v);
+  };
+  const int tr_key = (lane & 15) >> 2;
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  uint32_t vlane[D / 32];
+  {
+    const int key_l = 4 * half + tr_key;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db) {
+      const int d = db * 32 + tr_d;
+      vlane[db] = lds_addr(lds) + L::vOff(0) + key_l * (D * 2) + (vchunk<D>(key_l, d >> 3) << 4) +
+                  (d & 7) * 2;
+    }
+  }
+
+  bf16x8_t qf[D / 16];
+  f32x16_t o[D / 32];
+  float l = 0.f;
+  f32x16_t s[2];          // scores of the tile between its product and softmax phases
+  bf16x8_t pb[4];         // P of the tile between its softmax and PV phases
+  int nf = 0, u = 0;
+
+  // scores S^T = K Q^T + (bias - m_eff) of the tile in stage BUF
+  auto qk = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int KG = 4, GPS = D / 16 / KG, NG = 2 * GPS;
+    uint32_t fb[2];
+    fb[0] = ds_read_u8<BUF * L::fBytes>(flane);
+    fb[1] = ds_read_u8<BUF * L::fBytes + 32>(flane);
+    u32x4_t kb[2][KG];
+    auto kread = [&](auto gic, u32x4_t(&dst)[KG]) {
+      constexpr int gi = decltype(gic)::value, sb = gi / GPS, kq = gi % GPS;
+      static_for<0, KG>([&](auto jc) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value;
+        dst[j] = ds_read_b128<L::kOff(BUF) + sb * 32 * D * 2>(klane[kq * KG + j]);
+      });
+    };
+    kread(std::integral_constant<int, 0>{}, kb[0]);
+    static_for<0, NG>([&](auto gic) __attribute__((always_inline)) {
+      constexpr int gi = decltype(gic)::value, sb = gi / GPS, kq = gi % GPS;
+      if constexpr (gi + 1 < NG) {
+        kread(std::integral_constant<int, gi + 1>{}, kb[(gi + 1) & 1]);
+        lds_wait_n<KG>();
+      } else {
+        lds_wait();
+      }
+#pragma unroll
+      for (int j = 0; j < KG; ++j) reg_fence(kb[gi & 1][j]);
+      if constexpr (gi == 0) {
+        reg_fence(fb[0]);
+        reg_fence(fb[1]);
+      }
+      if constexpr (kq == 0) {
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s[sb][t] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < KG; ++j)
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kb[gi & 1][j]),
+                                                         qf[kq * KG + j], s[sb], 0, 0, 0);
+      if constexpr (kq == GPS - 1)
+        s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bias_operand(fb[sb]), qx, s[sb], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  // O^T += V^T P^T for the tile in stage BUF
+  auto pv = [&](auto bufc) __attribute__((always_inline)) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int NB = D / 32;
+    u32x2_t xv[2][NB][2];
+    auto vread = [&](auto stc, u32x2_t(&dst)[NB][2]) {
+      constexpr int st = decltype(stc)::value, sb = st / 2, hs = st % 2;
+      constexpr int off = BUF * L::vBytes + (sb * 32 + hs * 16) * D * 2;
+      static_for<0, NB>([&](auto dbc) __attribute__((always_inline)) {
+        constexpr int db = decltype(dbc)::value;
+        dst[db][0] = ds_read_tr16<off>(vlane[db]);
+        dst[db][1] = ds_read_tr16<off + 8 * D * 2>(vlane[db]);
+      });
+    };
+    vread(std::integral_constant<int, 0>{}, xv[0]);
+    static_for<0, 4>([&](auto stc) __attribute__((always_inline)) {
+      constexpr int st = decltype(stc)::value;
+      constexpr int NEXT = st + 1 < 4 ? 2 * NB : 0;
+      auto& x = xv[st & 1];
+      lds_wait_n<2 * (NB - 1)>();
+      reg_fence(x[0][0]);
+      reg_fence(x[0][1]);
+      if constexpr (st + 1 < 4) vread(std::integral_constant<int, st + 1>{}, xv[(st + 1) & 1]);
+      static_for<0, NB>([&](auto dbc) __attribute__((always_inline)) {
+        constexpr int db = decltype(dbc)::value;
+        if constexpr (db > 0) {
+          lds_wait_n<2 * (NB - 1 - db) + NEXT>();
+          reg_fence(x[db][0]);
+          reg_fence(x[db][1]);
+        }
+        const u32x4_t w = {x[db][0][0], x[db][0][1], x[db][1][0], x[db][1][1]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb[st],
+                                                         o[db], 0, 0, 0);
+      });
+    });
+  };
+  auto pv_at = [&](int buf) __attribute__((always_inline)) {
+    static_for<0, kPPStages>([&](auto bc) __attribute__((always_inline)) {
+      if (buf == decltype(bc)::value) pv(bc);
+    });
+  };
+
+  // softmax of tile c: causal mask, lazy maximum, P and its row sum
+  auto softmax = [&](int c) __attribute__((always_inline)) {
+    if (c >= nf) {
+      const int lim = u - c * kKvTile;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int kl = sb * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
+          if (kl > lim) s[sb][t] = -INFINITY;
+        }
+    }
+    float mx[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      mx[i] = fmaxf(fmaxf(s[i >> 2][4 * (i & 3)], s[i >> 2][4 * (i & 3) + 1]),
+                    fmaxf(s[i >> 2][4 * (i & 3) + 2], s[i >> 2][4 * (i & 3) + 3]));
+    float mt = fmaxf(fmaxf(fmaxf(mx[0], mx[1]), fmaxf(mx[2], mx[3])),
+                     fmaxf(fmaxf(mx[4], mx[5]), fmaxf(mx[6], mx[7])));
+    mt = xor32_max(mt);
+    const bool bump = (mt > 8.f) || (!m_set && mt != -INFINITY);
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+      float shift = 0.f;
+      if (bump) {
+        const float old = m_eff;
+        set_qx(m_eff + mt);
+        shift = m_eff - old;
+        const float corr = m_set ? fast_exp2(-shift) : 0.f;
+        l *= corr;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int t = 0; t < 16; ++t) o[db][t] *= corr;
+        m_set = true;
+      }
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) s[sb][t] -= shift;
+    }
+#pragma unroll
+    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) s[sb][t] = fast_exp2(s[sb][t]);
+    {
+      float ps[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) ps[i] = s[i >> 3][2 * (i & 7)] + s[i >> 3][2 * (i & 7) + 1];
+#pragma unroll
+      for (int w = 8; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) ps[i] = ps[i] + ps[i + w];
+      l += ps[0];
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pb[st][i] = static_cast<__bf16>(s[st / 2][(st % 2) * 8 + i]);
+  };
+
+  // Pieces: the parts of this workgroup's range that fall in one segment
+  // (query-tile pair j, KV group g; segments in order g-major).
+  int g = static_cast<int>(r0 / lsum), j = 0;
+  long long start = static_cast<long long>(g) * lsum;
+  while (start + pair_len(j) <= r0) start += pair_len(j++);
+  for (;;) {
+    // (the piece's scalars are wave-uniform; readfirstlane tells the compiler)
+    j = __builtin_amdgcn_readfirstlane(j);
+    g = __builtin_amdgcn_readfirstlane(g);
+    const int len = __builtin_amdgcn_readfirstlane(pair_len(j));
+    const int c0 = __builtin_amdgcn_readfirstlane(static_cast<int>(max(r0, start) - start));
+    const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(min(r1, start + len) - start) - c0);
+    const int qt0 = 2 * j;
+    const bool two = qt0 + 1 < n_qt;
+    // causal test from the first tile either query tile sees only partly
+    nf = __builtin_amdgcn_readfirstlane(two ? min(n_full[qt0], n_full[qt0 + 1]) : n_full[qt0]);
+    const int qt = qt0 + grp;
+    kg8 = reinterpret_cast<const uint8_t*>(kc + static_cast<size_t>(g) * D);
+    vg8 = reinterpret_cast<const uint8_t*>(vc + static_cast<size_t>(g) * D);
+    // the query column this lane owns (past the last pair: a duplicate of
+    // the last pair, computed and never written)
+    const int p = qt * kQRows + (wave & 3) * 32 + (lane & 31);
+    const int pc = min(p, P - 1);
+    const int r = pc / G;
+    const int h = g * G + (pc - r * G);
+    u = Tpos[r];
+    {
+      const bf16_t* qrow = q + (static_cast<size_t>(r) * Hq + h) * D + 8 * half;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
+    }
+    // the query fragments (and the previous piece's partial stores) are
+    // complete before the piece's first DMA
+    attn_wait_vmcnt<0>();
+    m_set = false;
+    set_qx(0.f);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) o[db][t] = 0.f;
+    l = 0.f;
+
+    // Each wave runs the same program, tile by tile: a product phase (PV of
+    // the previous tile, scores of this one) and a softmax phase, each ended by
+    // a workgroup barrier.  Group B starts one barrier late (in phase 2i group
+    // A takes the products of tile i while group B takes the softmax of tile
+    // i - 1) and skips the barrier after its last softmax, so both pass 2n.
+    // The stages are managed per phase for all waves alike: in phase 2i the
+    // waves issue tile i + 2 (into the stage tile i - 2 left, whose last PV was
+    // in phase 2i - 1), and at the end of phase 2i + 1 each waits for its part
+    // of tile i + 1.
+    issue(c0, std::integral_constant<int, 0>{});
+    if (n > 1) issue(c0 + 1, std::integral_constant<int, 1>{});
+    wait_tile(n > 1);
+    lds_barrier();
+    if (grp == 1) {
+      if (n > 2) issue(c0 + 2, std::integral_constant<int, 2>{});
+      lds_barrier();
+    }
+    auto unit = [&](auto bc, int i) __attribute__((always_inline)) {
+      constexpr int BUF = decltype(bc)::value;
+      constexpr int PREV = (BUF + kPPStages - 1) % kPPStages;
+      constexpr int NEXT2 = (BUF + 2) % kPPStages, NEXT3 = (BUF + 3) % kPPStages;
+      // products (phase 2i for group A, 2i + 1 for group B)
+      if (grp == 0 && i + 2 < n) issue(c0 + i + 2, std::integral_constant<int, NEXT2>{});
+      if (i > 0) pv(std::integral_constant<int, PREV>{});
+      qk(bc);
+      if (grp == 1 && i + 1 < n) wait_tile(i + 2 < n);
+      lds_barrier();
+      // softmax (phase 2i + 1 for group A, 2i + 2 for group B)
+      if (grp == 1 && i + 3 < n) issue(c0 + i + 3, std::integral_constant<int, NEXT3>{});
+      softmax(c0 + i);
+      if (grp == 0 && i + 1 < n) wait_tile(i + 2 < n);
+      if (grp == 0 || i + 1 < n) lds_barrier();
+    };
+    for (int i = 0; i < n; i += kPPStages) {
+      static_for<0, kPPStages>([&](auto bc) __attribute__((always_inline)) {
+        if (i + decltype(bc)::value < n) unit(bc, i + decltype(bc)::value);
+      });
+    }
+    pv_at((n - 1) % kPPStages);   // PV of the last tile
+
+    // partial of this piece: slot (segment + workgroup) * 2 + query tile of the pair
+    const size_t slot = static_cast<size_t>(g * npairs + j + w) * 2 + grp;
+    const int ql = (wave & 3) * 32 + (lane & 31);
+    if (p < P) {
+      // buffer stores: a lane offset plus a constant per element (no 64-bit
+      // address per element, which the compiler would hoist and spill)
+      const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+          part_o + slot * D * kQRows, 0, D * kQRows * 4, kRsrcWord3);
+      const int vo = (4 * half * kQRows + ql) * 4;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const float v = o[db][t];   // (bit_cast of a vector element reads element 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), ro, vo,
+                                                (db * 32 + 8 * (t >> 2) + (t & 3)) * kQRows * 4, 0);
+        }
+    }
+    l = xor32_add(l);
+    if (half == 0 && p < P) {
+      float* pm = part_ml + slot * 2 * kQRows;
+      pm[ql] = m_set ? m_eff : -INFINITY;
+      pm[kQRows + ql] = l;
+    }
+    // the other group may still be reading the last stage
+    lds_barrier();
+    start += len;
+    if (start >= r1) break;
+    if (++j == npairs) {
+      j = 0;
+      ++g;
+    }
+  }
+}
+
 // Merge the split-KV partials: workgroup (query tile, KV group, kMergeD-row
 // slice of d); thread (pair ql, 8 consecutive d).  Split weights 2^(m_s - max m),
 // normalised by the weighted sums; each thread writes its pair's 8 outputs
@@ -561,29 +1039,56 @@ static_assert(kAttnThreads % kQRows == 0, "merge threads cover whole query tiles
 template <int D, typename OutT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ n_total, int B, int Hq, int Hkv, int G, int split_tiles,
-    int n_splits, OutT* __restrict__ o) {
+    const int32_t* __restrict__ n_total, int n_qt, int B, int Hq, int Hkv, int G,
+    int split_tiles, int n_splits, int sk_groups, OutT* __restrict__ o) {
   const int qt = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x;
   const int ql = tid % kQRows;
   const int d0 = blockIdx.z * kMergeD + (tid / kQRows) * 8;
   const int p = qt * kQRows + ql;
   if (p >= B * G) return;
-  const int ns = (n_total[qt] + split_tiles - 1) / split_tiles;
-  const size_t slot0 = (static_cast<size_t>(qt) * Hkv + g) * n_splits;
+  // partials of this (query tile, KV group): slots slot0 + s * stride, s < ns
+  int ns;
+  size_t slot0, stride;
+  if (sk_groups > 0) {
+    // stream-K pieces of segment (pair qt / 2, group g): one per workgroup
+    // w in [owner(first tile), owner(last tile)], in slot (segment + w) * 2 + qt % 2
+    const int npairs = (n_qt + 1) / 2;
+    long long before = 0, lsum = 0;
+    for (int j = 0; j < npairs; ++j) {
+      const int a = n_total[2 * j];
+      const int len = 2 * j + 1 < n_qt ? max(a, n_total[2 * j + 1]) : a;
+      lsum += len;
+      if (j < qt / 2) before += len;
+    }
+    const int jq = qt / 2;
+    const int len = 2 * jq + 1 < n_qt ? max(n_total[2 * jq], n_total[2 * jq + 1]) : n_total[2 * jq];
+    const long long T = lsum * Hkv, first = g * lsum + before, last = first + len - 1;
+    const long long W = min(static_cast<long long>(sk_groups), T);   // as the attention kernel
+    const int w0 = static_cast<int>(((first + 1) * W - 1) / T);
+    const int w1 = static_cast<int>(((last + 1) * W - 1) / T);
+    ns = w1 - w0 + 1;
+    slot0 = static_cast<size_t>(g * npairs + jq + w0) * 2 + (qt & 1);
+    stride = 2;
+  } else {
+    ns = (n_total[qt] + split_tiles - 1) / split_tiles;
+    slot0 = (static_cast<size_t>(qt) * Hkv + g) * n_splits;
+    stride = 1;
+  }
   float mmax = -INFINITY;
   // unrolled so that several splits' loads are in flight per thread
 #pragma unroll 8
-  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, part_ml[(slot0 + s) * 2 * kQRows + ql]);
+  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, part_ml[(slot0 + s * stride) * 2 * kQRows + ql]);
   float denom = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll 8
   for (int s = 0; s < ns; ++s) {
-    const float* pm = part_ml + (slot0 + s) * 2 * kQRows;
+    const size_t sl = slot0 + s * stride;
+    const float* pm = part_ml + sl * 2 * kQRows;
     const float w = fast_exp2(pm[ql] - mmax);
     denom += w * pm[kQRows + ql];
-    const float* po = part_o + (slot0 + s) * D * kQRows + static_cast<size_t>(d0) * kQRows + ql;
+    const float* po = part_o + sl * D * kQRows + static_cast<size_t>(d0) * kQRows + ql;
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] += w * po[i * kQRows];
   }
@@ -919,6 +1424,29 @@ int attn_split_tiles(int B, int n_tokens, const Shape& sh) {
   return st;
 }
 
+// Workgroups of the stream-K pair kernel (d = 128): one per CU, each taking an
+// equal share of all (query-tile pair, KV group, KV tile) work; 0 for the
+// split kernel (d = 64).
+int attn_sk_groups(const Shape& sh) {
+  if (sh.d != 128) return 0;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  return cus;
+}
+
+// Partial slots of one launch: stream-K pieces are numbered (segment +
+// workgroup) per query tile of a pair; splits (query tile, KV group, split).
+size_t attn_slots(int B, int n_tokens, const Shape& sh) {
+  const int nt = plan_tiles(B, sh.group);
+  const int W = attn_sk_groups(sh);
+  if (W > 0) return static_cast<size_t>(sh.hkv * ((nt + 1) / 2) + W) * 2;
+  const int st = attn_split_tiles(B, n_tokens, sh);
+  const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
+  return static_cast<size_t>(nt) * sh.hkv * ns;
+}
+
 }  // namespace
 
 bool decode_supported(kvr_dtype dt, int B, const Shape& sh) {
@@ -932,10 +1460,7 @@ size_t decode_workspace_bytes(int B, int n_tokens, const Shape& sh) {
 
 size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh) {
   if (dt != KVR_BF16) return 0;
-  const int nt = plan_tiles(B, sh.group);
-  const int st = attn_split_tiles(B, n_tokens, sh);
-  const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
-  return static_cast<size_t>(nt) * sh.hkv * ns * (sh.d + 2) * kQRows * sizeof(float);
+  return attn_slots(B, n_tokens, sh) * (sh.d + 2) * kQRows * sizeof(float);
 }
 
 namespace {
@@ -955,10 +1480,26 @@ hipError_t launch_mfma(const void* q, const void* k_cache, const void* v_cache,
   const int nt = plan_tiles(B, sh.group);
   const int st = attn_split_tiles(B, n_tokens, sh);
   const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
-  const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
+  const size_t slots = attn_slots(B, n_tokens, sh);
   float* part_o = static_cast<float*>(ws);
   float* part_ml = part_o + slots * sh.d * kQRows;
   const float log2e = 1.4426950408889634f;
+  if constexpr (D == 128) {
+    static bool pp_attr = false;
+    if (!pp_attr) {
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_pp<D>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         PPLds<D>::total);
+      if (e != hipSuccess) return e;
+      pp_attr = true;
+    }
+    hipLaunchKernelGGL(k_attn_pp<D>, dim3(attn_sk_groups(sh)), dim3(kPPThreads), PPLds<D>::total,
+                       stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
+                       static_cast<const bf16_t*>(v_cache), flags, T, n_full, n_total, nt, B,
+                       n_tokens, sh.hq, sh.hkv, sh.group, alpha * log2e, beta * log2e,
+                       kAttnXcdOrder, part_o, part_ml);
+    return hipGetLastError();
+  }
   dim3 grid(nt, sh.hkv, ns);
   hipLaunchKernelGGL(k_attn_mfma<D>, grid, dim3(kAttnMfmaThreads), AttnLds<D>::total, stream,
                      static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
@@ -974,12 +1515,12 @@ hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_t
   const int nt = plan_tiles(B, sh.group);
   const int st = attn_split_tiles(B, n_tokens, sh);
   const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
-  const size_t slots = static_cast<size_t>(nt) * sh.hkv * ns;
+  const size_t slots = attn_slots(B, n_tokens, sh);
   const float* part_o = static_cast<const float*>(ws);
   const float* part_ml = part_o + slots * sh.d * kQRows;
   hipLaunchKernelGGL((k_attn_merge<D, OutT>), dim3(nt, sh.hkv, D / kMergeD), dim3(kAttnThreads), 0,
-                     stream, part_o, part_ml, n_total, B, sh.hq, sh.hkv, sh.group, st, ns,
-                     static_cast<OutT*>(o_out));
+                     stream, part_o, part_ml, n_total, nt, B, sh.hq, sh.hkv, sh.group, st, ns,
+                     attn_sk_groups(sh), static_cast<OutT*>(o_out));
   return hipGetLastError();
 }
 }  // namespace

@@ -60,7 +60,9 @@ def dev_cache(w: wl.Workload, K: np.ndarray, V: np.ndarray) -> Tuple[torch.Tenso
 
 def workspace(cfg, B: int, n_tokens: int) -> torch.Tensor:
     n = kvr().kvr_workspace_bytes(cfg, B, n_tokens)
-    return torch.empty(n, dtype=torch.uint8, device="cuda")
+    # all bytes 0xFF (float32 NaN): a kernel that reads workspace it has not
+    # written in the same call shows up as NaN, not as a stale value
+    return torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
 
 
 def build_seams_gpu(w: wl.Workload, tau: Optional[int] = None, asym: bool = True,
