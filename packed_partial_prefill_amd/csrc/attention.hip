@@ -627,7 +627,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     const uint8_t* __restrict__ flags, const int32_t* __restrict__ Tpos,
     const int32_t* __restrict__ n_full, const int32_t* __restrict__ n_total, int n_qt, int B,
     int n_tokens, int Hq, int Hkv, int G, float bias_local, float bias_sink, bool xcd_order,
-    float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float* __restrict__ part_o, float* __restrict__ part_ml, int2* __restrict__ seg_tab) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   using L = PPLds<D>;
   constexpr int KCH = D / 8;
@@ -685,9 +685,8 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
   }
   static_assert(L::kBytes == L::vBytes, "K and V stages advance by the same stride");
   constexpr int kRsrcWord3 = 0x00020000;
-  // tile c into stage BUF (as k_attn_mfma: wave 0 also brings the flag bytes)
-  auto issue = [&](int c, auto bufc) __attribute__((always_inline)) {
-    constexpr int BUF = decltype(bufc)::value;
+  // tile c into stage buf (as k_attn_mfma: wave 0 also brings the flag bytes)
+  auto issue = [&](int c, int buf) __attribute__((always_inline)) {
     const int kv0 = c * kKvTile;
     const int rows = min(kKvTile, n_tokens - kv0);
     const int nbytes = rows * static_cast<int>(row_bytes);
@@ -696,11 +695,11 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
         if (lane < kKvTile / 4) {
           const __amdgpu_buffer_rsrc_t rf = __builtin_amdgcn_make_buffer_rsrc(
               const_cast<uint8_t*>(flags + kv0), 0, kKvTile, kRsrcWord3);
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, KVR_LDS(lds + L::fOff(BUF)), 4, 4 * lane, 0,
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rf, KVR_LDS(lds + L::fOff(0) + buf * L::fBytes), 4, 4 * lane, 0,
                                                    0, 0);
         }
       } else {
-        lds[L::fOff(BUF) + lane] = flags[min(kv0 + lane, n_tokens - 1)];
+        lds[L::fOff(0) + buf * L::fBytes + lane] = flags[min(kv0 + lane, n_tokens - 1)];
       }
     }
 #pragma unroll
@@ -708,7 +707,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
       const uint8_t* base = (slice_isv(j) ? vg8 : kg8) + static_cast<size_t>(kv0) * row_bytes;
       const __amdgpu_buffer_rsrc_t rs =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), 0, nbytes, kRsrcWord3);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, KVR_LDS(lds + BUF * L::kBytes + s_dst[j]), 16,
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, KVR_LDS(lds + buf * L::kBytes + s_dst[j]), 16,
                                                static_cast<int>(s_off[j]), 0, 0, 0);
     }
   };
@@ -916,6 +915,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
   // (query-tile pair j, KV group g; segments in order g-major).
   int g = static_cast<int>(r0 / lsum), j = 0;
   long long start = static_cast<long long>(g) * lsum;
+  int b0 = 0;   // stage of the piece's first tile: the ring continues across pieces
   while (start + pair_len(j) <= r0) start += pair_len(j++);
   for (;;) {
     // (the piece's scalars are wave-uniform; readfirstlane tells the compiler)
@@ -943,9 +943,12 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
     }
-    // the query fragments (and the previous piece's partial stores) are
-    // complete before the piece's first DMA
-    attn_wait_vmcnt<0>();
+    // (the query loads complete with the first tile's wait below)
+    if (c0 == 0 && wave == 0 && lane == 0) {
+      // the merge's view of this segment: its first workgroup and piece count
+      const long long last = start + len - 1;
+      seg_tab[g * npairs + j] = make_int2(w, static_cast<int>(((last + 1) * W - 1) / T) - w + 1);
+    }
     m_set = false;
     set_qx(0.f);
 #pragma unroll
@@ -963,12 +966,12 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     // waves issue tile i + 2 (into the stage tile i - 2 left, whose last PV was
     // in phase 2i - 1), and at the end of phase 2i + 1 each waits for its part
     // of tile i + 1.
-    issue(c0, std::integral_constant<int, 0>{});
-    if (n > 1) issue(c0 + 1, std::integral_constant<int, 1>{});
+    issue(c0, b0);
+    if (n > 1) issue(c0 + 1, (b0 + 1) % kPPStages);
     wait_tile(n > 1);
     lds_barrier();
     if (grp == 1) {
-      if (n > 2) issue(c0 + 2, std::integral_constant<int, 2>{});
+      if (n > 2) issue(c0 + 2, (b0 + 2) % kPPStages);
       lds_barrier();
     }
     auto unit = [&](auto bc, int i) __attribute__((always_inline)) {
@@ -976,23 +979,25 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
       constexpr int PREV = (BUF + kPPStages - 1) % kPPStages;
       constexpr int NEXT2 = (BUF + 2) % kPPStages, NEXT3 = (BUF + 3) % kPPStages;
       // products (phase 2i for group A, 2i + 1 for group B)
-      if (grp == 0 && i + 2 < n) issue(c0 + i + 2, std::integral_constant<int, NEXT2>{});
+      if (grp == 0 && i + 2 < n) issue(c0 + i + 2, NEXT2);
       if (i > 0) pv(std::integral_constant<int, PREV>{});
       qk(bc);
       if (grp == 1 && i + 1 < n) wait_tile(i + 2 < n);
       lds_barrier();
       // softmax (phase 2i + 1 for group A, 2i + 2 for group B)
-      if (grp == 1 && i + 3 < n) issue(c0 + i + 3, std::integral_constant<int, NEXT3>{});
+      if (grp == 1 && i + 3 < n) issue(c0 + i + 3, NEXT3);
       softmax(c0 + i);
       if (grp == 0 && i + 1 < n) wait_tile(i + 2 < n);
       if (grp == 0 || i + 1 < n) lds_barrier();
     };
-    for (int i = 0; i < n; i += kPPStages) {
+    // tile i sits in stage (b0 + i) % kPPStages
+    for (int k0 = 0; k0 < b0 + n; k0 += kPPStages) {
       static_for<0, kPPStages>([&](auto bc) __attribute__((always_inline)) {
-        if (i + decltype(bc)::value < n) unit(bc, i + decltype(bc)::value);
+        const int i = k0 + decltype(bc)::value - b0;
+        if (i >= 0 && i < n) unit(bc, i);
       });
     }
-    pv_at((n - 1) % kPPStages);   // PV of the last tile
+    pv_at((b0 + n - 1) % kPPStages);   // PV of the last tile
 
     // partial of this piece: slot (segment + workgroup) * 2 + query tile of the pair
     const size_t slot = static_cast<size_t>(g * npairs + j + w) * 2 + grp;
@@ -1018,8 +1023,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
       pm[ql] = m_set ? m_eff : -INFINITY;
       pm[kQRows + ql] = l;
     }
-    // the other group may still be reading the last stage
-    lds_barrier();
+    // No barrier here: the next piece's first three tiles go to the stages
+    // after this piece's last one, which the other group may still be reading.
+    b0 = (b0 + n) % kPPStages;
     start += len;
     if (start >= r1) break;
     if (++j == npairs) {
@@ -1040,7 +1046,7 @@ template <int D, typename OutT>
 __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
     const int32_t* __restrict__ n_total, int n_qt, int B, int Hq, int Hkv, int G,
-    int split_tiles, int n_splits, int sk_groups, OutT* __restrict__ o) {
+    int split_tiles, int n_splits, const int2* __restrict__ seg_tab, OutT* __restrict__ o) {
   const int qt = blockIdx.x, g = blockIdx.y;
   const int tid = threadIdx.x;
   const int ql = tid % kQRows;
@@ -1050,25 +1056,14 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
   // partials of this (query tile, KV group): slots slot0 + s * stride, s < ns
   int ns;
   size_t slot0, stride;
-  if (sk_groups > 0) {
-    // stream-K pieces of segment (pair qt / 2, group g): one per workgroup
-    // w in [owner(first tile), owner(last tile)], in slot (segment + w) * 2 + qt % 2
-    const int npairs = (n_qt + 1) / 2;
-    long long before = 0, lsum = 0;
-    for (int j = 0; j < npairs; ++j) {
-      const int a = n_total[2 * j];
-      const int len = 2 * j + 1 < n_qt ? max(a, n_total[2 * j + 1]) : a;
-      lsum += len;
-      if (j < qt / 2) before += len;
-    }
-    const int jq = qt / 2;
-    const int len = 2 * jq + 1 < n_qt ? max(n_total[2 * jq], n_total[2 * jq + 1]) : n_total[2 * jq];
-    const long long T = lsum * Hkv, first = g * lsum + before, last = first + len - 1;
-    const long long W = min(static_cast<long long>(sk_groups), T);   // as the attention kernel
-    const int w0 = static_cast<int>(((first + 1) * W - 1) / T);
-    const int w1 = static_cast<int>(((last + 1) * W - 1) / T);
-    ns = w1 - w0 + 1;
-    slot0 = static_cast<size_t>(g * npairs + jq + w0) * 2 + (qt & 1);
+  if (seg_tab) {
+    // stream-K pieces of segment s = (pair qt / 2, group g): one per workgroup
+    // w0 .. w0 + ns - 1 (recorded by the attention kernel), in slot
+    // (s + w) * 2 + qt % 2
+    const int seg = g * ((n_qt + 1) / 2) + qt / 2;
+    const int2 e = seg_tab[seg];
+    ns = e.y;
+    slot0 = static_cast<size_t>(seg + e.x) * 2 + (qt & 1);
     stride = 2;
   } else {
     ns = (n_total[qt] + split_tiles - 1) / split_tiles;
@@ -1436,6 +1431,11 @@ int attn_sk_groups(const Shape& sh) {
   return cus;
 }
 
+// Stream-K segments (query-tile pair, KV group); 0 for the split kernel.
+size_t attn_segments(int B, const Shape& sh) {
+  return attn_sk_groups(sh) > 0 ? static_cast<size_t>(sh.hkv) * ((plan_tiles(B, sh.group) + 1) / 2) : 0;
+}
+
 // Partial slots of one launch: stream-K pieces are numbered (segment +
 // workgroup) per query tile of a pair; splits (query tile, KV group, split).
 size_t attn_slots(int B, int n_tokens, const Shape& sh) {
@@ -1460,7 +1460,9 @@ size_t decode_workspace_bytes(int B, int n_tokens, const Shape& sh) {
 
 size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh) {
   if (dt != KVR_BF16) return 0;
-  return attn_slots(B, n_tokens, sh) * (sh.d + 2) * kQRows * sizeof(float);
+  // partials (O, then max and sum), then the stream-K segment table
+  return attn_slots(B, n_tokens, sh) * (sh.d + 2) * kQRows * sizeof(float) +
+         attn_segments(B, sh) * sizeof(int2);
 }
 
 namespace {
@@ -1497,7 +1499,8 @@ hipError_t launch_mfma(const void* q, const void* k_cache, const void* v_cache,
                        stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
                        static_cast<const bf16_t*>(v_cache), flags, T, n_full, n_total, nt, B,
                        n_tokens, sh.hq, sh.hkv, sh.group, alpha * log2e, beta * log2e,
-                       kAttnXcdOrder, part_o, part_ml);
+                       kAttnXcdOrder, part_o, part_ml,
+                       reinterpret_cast<int2*>(part_ml + slots * 2 * kQRows));
     return hipGetLastError();
   }
   dim3 grid(nt, sh.hkv, ns);
@@ -1520,7 +1523,9 @@ hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_t
   const float* part_ml = part_o + slots * sh.d * kQRows;
   hipLaunchKernelGGL((k_attn_merge<D, OutT>), dim3(nt, sh.hkv, D / kMergeD), dim3(kAttnThreads), 0,
                      stream, part_o, part_ml, n_total, nt, B, sh.hq, sh.hkv, sh.group, st, ns,
-                     attn_sk_groups(sh), static_cast<OutT*>(o_out));
+                     attn_sk_groups(sh) > 0 ? reinterpret_cast<const int2*>(part_ml + slots * 2 * kQRows)
+                                            : nullptr,
+                     static_cast<OutT*>(o_out));
   return hipGetLastError();
 }
 }  // namespace
