@@ -603,6 +603,9 @@ constexpr int kPPThreads = 64 * kPPWaves;
 constexpr int kPPStages = 4;
 // stream-K ranges in XCD-contiguous runs (neighbouring pieces share KV tiles)
 constexpr bool kAttnXcdOrder = true;
+// fewest KV tiles per stream-K workgroup (small problems use fewer CUs
+// rather than paying a piece's prologue and epilogue for one or two tiles)
+constexpr int kSkMinTiles = 4;
 
 template <int D>
 struct PPLds {
@@ -637,18 +640,48 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
   const int grp = wave >> 2;   // 0: group A, 1: group B
   const int P = B * G;
 
-  // This workgroup's share of the work (see attn_sk_range).
+  // This workgroup's share of the work.  Segment (pair j, KV group g) has
+  // len(j) = max(n_total) of the pair's query tiles; with up to 64 pairs
+  // each lane holds one pair's length, prefix and n_full (one round of
+  // loads at the start instead of a chain of dependent scalar loads).
   const int npairs = (n_qt + 1) / 2;
   auto pair_len = [&](int j) __attribute__((always_inline)) {
     const int a = n_total[2 * j];
     return 2 * j + 1 < n_qt ? max(a, n_total[2 * j + 1]) : a;
   };
+  auto pair_nf = [&](int j) __attribute__((always_inline)) {
+    const int a = n_full[2 * j];
+    return 2 * j + 1 < n_qt ? min(a, n_full[2 * j + 1]) : a;
+  };
+  const bool lane_pairs = npairs <= 64;
+  int len_l = 0, nf_l = 0, incl_l = 0;   // this lane's pair (lane < npairs)
   int lsum = 0;
-  for (int j = 0; j < npairs; ++j) lsum += pair_len(j);
+  if (lane_pairs) {
+    if (lane < npairs) {
+      len_l = pair_len(lane);
+      nf_l = pair_nf(lane);
+    }
+    incl_l = len_l;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl_l, o);
+      if (lane >= o) incl_l += v;
+    }
+    lsum = __builtin_amdgcn_readlane(incl_l, 63);
+  } else {
+    for (int j = 0; j < npairs; ++j) lsum += pair_len(j);
+  }
+  auto seg_len = [&](int j) __attribute__((always_inline)) {
+    return lane_pairs ? __builtin_amdgcn_readlane(len_l, j) : pair_len(j);
+  };
+  auto seg_nf = [&](int j) __attribute__((always_inline)) {
+    return lane_pairs ? __builtin_amdgcn_readlane(nf_l, j) : pair_nf(j);
+  };
   const long long T = static_cast<long long>(lsum) * Hkv;
-  // at most one workgroup per tile, so that every range is non-empty (the
+  // at least kSkMinTiles tiles per workgroup (every range non-empty: the
   // merge reads one piece from each workgroup between a segment's owners)
-  const int W = static_cast<int>(min(static_cast<long long>(gridDim.x), T));
+  const int W = static_cast<int>(
+      min(static_cast<long long>(gridDim.x), (T + kSkMinTiles - 1) / kSkMinTiles));
   const int w = xcd_order ? xcd_linear(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
   if (w >= W) return;
   const long long r0 = w * T / W, r1 = (w + 1) * T / W;
@@ -916,18 +949,24 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
   int g = static_cast<int>(r0 / lsum), j = 0;
   long long start = static_cast<long long>(g) * lsum;
   int b0 = 0;   // stage of the piece's first tile: the ring continues across pieces
-  while (start + pair_len(j) <= r0) start += pair_len(j++);
+  if (lane_pairs) {
+    // first pair whose inclusive prefix passes r0's offset in segment row g
+    const unsigned long long past = __builtin_amdgcn_ballot_w64(lane < npairs && incl_l > r0 - start);
+    j = __builtin_ctzll(past);
+    start += __builtin_amdgcn_readlane(incl_l, j) - __builtin_amdgcn_readlane(len_l, j);
+  } else {
+    while (start + pair_len(j) <= r0) start += pair_len(j++);
+  }
   for (;;) {
     // (the piece's scalars are wave-uniform; readfirstlane tells the compiler)
     j = __builtin_amdgcn_readfirstlane(j);
     g = __builtin_amdgcn_readfirstlane(g);
-    const int len = __builtin_amdgcn_readfirstlane(pair_len(j));
+    const int len = __builtin_amdgcn_readfirstlane(seg_len(j));
     const int c0 = __builtin_amdgcn_readfirstlane(static_cast<int>(max(r0, start) - start));
     const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(min(r1, start + len) - start) - c0);
     const int qt0 = 2 * j;
-    const bool two = qt0 + 1 < n_qt;
     // causal test from the first tile either query tile sees only partly
-    nf = __builtin_amdgcn_readfirstlane(two ? min(n_full[qt0], n_full[qt0 + 1]) : n_full[qt0]);
+    nf = __builtin_amdgcn_readfirstlane(seg_nf(j));
     const int qt = qt0 + grp;
     kg8 = reinterpret_cast<const uint8_t*>(kc + static_cast<size_t>(g) * D);
     vg8 = reinterpret_cast<const uint8_t*>(vc + static_cast<size_t>(g) * D);
@@ -1419,28 +1458,35 @@ int attn_split_tiles(int B, int n_tokens, const Shape& sh) {
   return st;
 }
 
-// Workgroups of the stream-K pair kernel (d = 128): one per CU, each taking an
-// equal share of all (query-tile pair, KV group, KV tile) work; 0 for the
-// split kernel (d = 64).
-int attn_sk_groups(const Shape& sh) {
+// Workgroups of the stream-K pair kernel: one per CU, each taking an equal
+// share of all (query-tile pair, KV group, KV tile) work; 0 for the split
+// kernel.  The pair kernel is for d = 128 and launches with at least 16 KV
+// tiles per CU at the cache's full length (below that the split kernel's
+// 128-pair workgroups, two per CU, spread the work over more waves and a
+// stream-K piece's prologue and epilogue weigh too much: 1.5B layer at 4K,
+// 36.7 against 27 us).
+int attn_sk_groups(int B, int n_tokens, const Shape& sh) {
   if (sh.d != 128) return 0;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  return cus;
+  const long long tiles = static_cast<long long>(sh.hkv) * ((plan_tiles(B, sh.group) + 1) / 2) *
+                          ((n_tokens + kKvTile - 1) / kKvTile);
+  return tiles >= 16LL * cus ? cus : 0;
 }
 
 // Stream-K segments (query-tile pair, KV group); 0 for the split kernel.
-size_t attn_segments(int B, const Shape& sh) {
-  return attn_sk_groups(sh) > 0 ? static_cast<size_t>(sh.hkv) * ((plan_tiles(B, sh.group) + 1) / 2) : 0;
+size_t attn_segments(int B, int n_tokens, const Shape& sh) {
+  return attn_sk_groups(B, n_tokens, sh) > 0
+             ? static_cast<size_t>(sh.hkv) * ((plan_tiles(B, sh.group) + 1) / 2) : 0;
 }
 
 // Partial slots of one launch: stream-K pieces are numbered (segment +
 // workgroup) per query tile of a pair; splits (query tile, KV group, split).
 size_t attn_slots(int B, int n_tokens, const Shape& sh) {
   const int nt = plan_tiles(B, sh.group);
-  const int W = attn_sk_groups(sh);
+  const int W = attn_sk_groups(B, n_tokens, sh);
   if (W > 0) return static_cast<size_t>(sh.hkv * ((nt + 1) / 2) + W) * 2;
   const int st = attn_split_tiles(B, n_tokens, sh);
   const int ns = ((n_tokens + kKvTile - 1) / kKvTile + st - 1) / st;
@@ -1462,7 +1508,7 @@ size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape&
   if (dt != KVR_BF16) return 0;
   // partials (O, then max and sum), then the stream-K segment table
   return attn_slots(B, n_tokens, sh) * (sh.d + 2) * kQRows * sizeof(float) +
-         attn_segments(B, sh) * sizeof(int2);
+         attn_segments(B, n_tokens, sh) * sizeof(int2);
 }
 
 namespace {
@@ -1487,21 +1533,24 @@ hipError_t launch_mfma(const void* q, const void* k_cache, const void* v_cache,
   float* part_ml = part_o + slots * sh.d * kQRows;
   const float log2e = 1.4426950408889634f;
   if constexpr (D == 128) {
-    static bool pp_attr = false;
-    if (!pp_attr) {
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_pp<D>),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize,
-                                         PPLds<D>::total);
-      if (e != hipSuccess) return e;
-      pp_attr = true;
+    const int sk = attn_sk_groups(B, n_tokens, sh);
+    if (sk > 0) {
+      static bool pp_attr = false;
+      if (!pp_attr) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_pp<D>),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize,
+                                           PPLds<D>::total);
+        if (e != hipSuccess) return e;
+        pp_attr = true;
+      }
+      hipLaunchKernelGGL(k_attn_pp<D>, dim3(sk), dim3(kPPThreads), PPLds<D>::total,
+                         stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
+                         static_cast<const bf16_t*>(v_cache), flags, T, n_full, n_total, nt, B,
+                         n_tokens, sh.hq, sh.hkv, sh.group, alpha * log2e, beta * log2e,
+                         kAttnXcdOrder, part_o, part_ml,
+                         reinterpret_cast<int2*>(part_ml + slots * 2 * kQRows));
+      return hipGetLastError();
     }
-    hipLaunchKernelGGL(k_attn_pp<D>, dim3(attn_sk_groups(sh)), dim3(kPPThreads), PPLds<D>::total,
-                       stream, static_cast<const bf16_t*>(q), static_cast<const bf16_t*>(k_cache),
-                       static_cast<const bf16_t*>(v_cache), flags, T, n_full, n_total, nt, B,
-                       n_tokens, sh.hq, sh.hkv, sh.group, alpha * log2e, beta * log2e,
-                       kAttnXcdOrder, part_o, part_ml,
-                       reinterpret_cast<int2*>(part_ml + slots * 2 * kQRows));
-    return hipGetLastError();
   }
   dim3 grid(nt, sh.hkv, ns);
   hipLaunchKernelGGL(k_attn_mfma<D>, grid, dim3(kAttnMfmaThreads), AttnLds<D>::total, stream,
@@ -1523,7 +1572,8 @@ hipError_t launch_merge(int B, int n_tokens, const Shape& sh, const int32_t* n_t
   const float* part_ml = part_o + slots * sh.d * kQRows;
   hipLaunchKernelGGL((k_attn_merge<D, OutT>), dim3(nt, sh.hkv, D / kMergeD), dim3(kAttnThreads), 0,
                      stream, part_o, part_ml, n_total, nt, B, sh.hq, sh.hkv, sh.group, st, ns,
-                     attn_sk_groups(sh) > 0 ? reinterpret_cast<const int2*>(part_ml + slots * 2 * kQRows)
+                     attn_sk_groups(B, n_tokens, sh) > 0
+                         ? reinterpret_cast<const int2*>(part_ml + slots * 2 * kQRows)
                                             : nullptr,
                      static_cast<OutT*>(o_out));
   return hipGetLastError();

@@ -37,8 +37,9 @@ def run_inference(w: wl.Workload, pos: np.ndarray, check_rows=None):
     dq = torch.from_numpy(q).cuda()
     dpos = torch.from_numpy(pos).cuda()
     o = torch.full((B, w.n_q_heads, w.head_dim), float("nan"), dtype=torch.float32, device="cuda")
-    ws = torch.empty(m.kvr_attention_workspace_bytes(cfg, B, w.n_tokens), dtype=torch.uint8,
-                     device="cuda")
+    # 0xFF bytes (float32 NaN): a read of workspace not written in this call shows
+    ws = torch.full((m.kvr_attention_workspace_bytes(cfg, B, w.n_tokens),), 0xFF,
+                    dtype=torch.uint8, device="cuda")
     m.kvr_biased_attention(cfg, kc, vc, flags, dq, dpos, o, ws)
     torch.cuda.synchronize()
     assert torch.equal(kc, kc0) and torch.equal(vc, vc0)
@@ -83,6 +84,24 @@ def test_inference_alpha_beta_zero_without_metadata_is_plain_attention():
 def test_inference_decode_path_shapes(hq, hkv, d, n, pos):
     w = _small(f"inf-decode-{hq}-{hkv}-{d}-{n}", 205, "bf16", hq, hkv, d, n, 128)
     run_inference(w, np.asarray(pos))
+
+
+def test_inference_stream_k_short_ranges_odd_tile_count():
+    # 7B heads over a 16K cache, queries at positions 0..299: the launch takes
+    # the stream-K pair kernel (sized by the cache length) although every
+    # query sees at most 5 KV tiles, so workgroups get 4-tile pieces; 2100
+    # pairs make 17 query tiles, the last pair holding one.
+    w = _small("inf-sk-short", 206, "bf16", 28, 4, 128, 16384, 256)
+    run_inference(w, np.arange(300))
+
+
+def test_inference_stream_k_group6_scattered():
+    # 1.5B heads (G = 6) over a 16K cache, 600 scattered queries (29 query
+    # tiles): segments of very different lengths split over workgroups.
+    w = _small("inf-sk-g6", 207, "bf16", 12, 2, 128, 16384, 512, alpha=-0.7, beta=-3.0)
+    rng = np.random.default_rng(7)
+    pos = np.sort(rng.choice(16384, size=600, replace=False))
+    run_inference(w, pos, check_rows=np.r_[0:8, 290:300, 590:600])
 
 
 @pytest.mark.parametrize("B", [1, 8])
