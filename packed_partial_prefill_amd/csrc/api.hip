@@ -229,10 +229,9 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
   const int qkv_n = sh.qkv_cols();
 
   // once per call: plan (Eq. 23-24) and RoPE table for the fixed positions
-  KVR_RUN(KVR_KERNEL_PLAN, stream, "plan",
-          kvr::launch_build_plan(d_T, B, sh.group, n_full, n_total, stream));
-  KVR_RUN(KVR_KERNEL_PLAN, stream, "rope table",
-          kvr::launch_rope_table(d_T, B, sh.d, cfg->rope_theta, tab, stream));
+  KVR_RUN(KVR_KERNEL_PLAN, stream, "plan and rope table",
+          kvr::launch_layer_tables(d_T, B, sh.group, n_full, n_total, sh.d, cfg->rope_theta, tab,
+                                   stream));
   // gather the selected rows once; RMSNorm for layer 0
   KVR_RUN(KVR_KERNEL_NORM, stream, "gather+norm",
           kvr::launch_gather_norm(dt, x_in, gather ? d_T : nullptr, x_out,

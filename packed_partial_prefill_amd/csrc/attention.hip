@@ -606,6 +606,9 @@ constexpr bool kAttnXcdOrder = true;
 // fewest KV tiles per stream-K workgroup (small problems use fewer CUs
 // rather than paying a piece's prologue and epilogue for one or two tiles)
 constexpr int kSkMinTiles = 4;
+// cost of a piece's prologue and epilogue in KV tiles, charged per segment in
+// the stream-K split (a workgroup with an extra piece takes fewer tiles)
+constexpr int kSkPieceCost = 2;
 
 template <int D>
 struct PPLds {
@@ -654,14 +657,17 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     return 2 * j + 1 < n_qt ? min(a, n_full[2 * j + 1]) : a;
   };
   const bool lane_pairs = npairs <= 64;
-  int len_l = 0, nf_l = 0, incl_l = 0;   // this lane's pair (lane < npairs)
-  int lsum = 0;
+  // Costs: a segment of len tiles costs len + kSkPieceCost units (its
+  // piece's prologue and epilogue), the leading kSkPieceCost units being
+  // virtual; workgroups split the units evenly.
+  int len_l = 0, nf_l = 0, incl_l = 0;   // this lane's pair (lane < npairs); incl_l in units
+  int lsum = 0;                          // units of one KV group's segments
   if (lane_pairs) {
     if (lane < npairs) {
       len_l = pair_len(lane);
       nf_l = pair_nf(lane);
     }
-    incl_l = len_l;
+    incl_l = lane < npairs ? len_l + kSkPieceCost : 0;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl_l, o);
@@ -669,7 +675,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     }
     lsum = __builtin_amdgcn_readlane(incl_l, 63);
   } else {
-    for (int j = 0; j < npairs; ++j) lsum += pair_len(j);
+    for (int j = 0; j < npairs; ++j) lsum += pair_len(j) + kSkPieceCost;
   }
   auto seg_len = [&](int j) __attribute__((always_inline)) {
     return lane_pairs ? __builtin_amdgcn_readlane(len_l, j) : pair_len(j);
@@ -678,10 +684,12 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     return lane_pairs ? __builtin_amdgcn_readlane(nf_l, j) : pair_nf(j);
   };
   const long long T = static_cast<long long>(lsum) * Hkv;
-  // at least kSkMinTiles tiles per workgroup (every range non-empty: the
-  // merge reads one piece from each workgroup between a segment's owners)
+  // At least kSkMinTiles units per workgroup, more than kSkPieceCost: every
+  // range then holds a tile (the merge reads one piece from each workgroup
+  // between the owners of a segment's first and last tile).
+  static_assert(kSkMinTiles > kSkPieceCost, "ranges must reach past a segment's virtual units");
   const int W = static_cast<int>(
-      min(static_cast<long long>(gridDim.x), (T + kSkMinTiles - 1) / kSkMinTiles));
+      max(1LL, min(static_cast<long long>(gridDim.x), T / kSkMinTiles)));
   const int w = xcd_order ? xcd_linear(blockIdx.x, gridDim.x) : static_cast<int>(blockIdx.x);
   if (w >= W) return;
   const long long r0 = w * T / W, r1 = (w + 1) * T / W;
@@ -953,17 +961,19 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     // first pair whose inclusive prefix passes r0's offset in segment row g
     const unsigned long long past = __builtin_amdgcn_ballot_w64(lane < npairs && incl_l > r0 - start);
     j = __builtin_ctzll(past);
-    start += __builtin_amdgcn_readlane(incl_l, j) - __builtin_amdgcn_readlane(len_l, j);
+    start += __builtin_amdgcn_readlane(incl_l, j) - (__builtin_amdgcn_readlane(len_l, j) + kSkPieceCost);
   } else {
-    while (start + pair_len(j) <= r0) start += pair_len(j++);
+    while (start + pair_len(j) + kSkPieceCost <= r0) start += pair_len(j++) + kSkPieceCost;
   }
   for (;;) {
     // (the piece's scalars are wave-uniform; readfirstlane tells the compiler)
     j = __builtin_amdgcn_readfirstlane(j);
     g = __builtin_amdgcn_readfirstlane(g);
     const int len = __builtin_amdgcn_readfirstlane(seg_len(j));
-    const int c0 = __builtin_amdgcn_readfirstlane(static_cast<int>(max(r0, start) - start));
-    const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(min(r1, start + len) - start) - c0);
+    const long long tile0 = start + kSkPieceCost;   // unit of the segment's first tile
+    const int c0 = __builtin_amdgcn_readfirstlane(static_cast<int>(max(r0, tile0) - tile0));
+    const int n = __builtin_amdgcn_readfirstlane(static_cast<int>(min(r1, tile0 + len) - tile0) - c0);
+    if (n <= 0) break;   // the range ends inside this segment's virtual units
     const int qt0 = 2 * j;
     // causal test from the first tile either query tile sees only partly
     nf = __builtin_amdgcn_readfirstlane(seg_nf(j));
@@ -985,7 +995,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     // (the query loads complete with the first tile's wait below)
     if (c0 == 0 && wave == 0 && lane == 0) {
       // the merge's view of this segment: its first workgroup and piece count
-      const long long last = start + len - 1;
+      const long long last = tile0 + len - 1;
       seg_tab[g * npairs + j] = make_int2(w, static_cast<int>(((last + 1) * W - 1) / T) - w + 1);
     }
     m_set = false;
@@ -1065,7 +1075,7 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     // No barrier here: the next piece's first three tiles go to the stages
     // after this piece's last one, which the other group may still be reading.
     b0 = (b0 + n) % kPPStages;
-    start += len;
+    start = tile0 + len;
     if (start >= r1) break;
     if (++j == npairs) {
       j = 0;

@@ -170,10 +170,11 @@ __global__ __launch_bounds__(kBuildThreads) void k_check_support(const int32_t* 
   if (threadIdx.x == 0) result[0] = s_bad ? KVR_ERR_BAD_SUPPORT : KVR_OK;
 }
 
-__global__ void k_build_plan(const int32_t* __restrict__ T, int B, int group, int n_tiles,
-                             int32_t* __restrict__ n_full, int32_t* __restrict__ n_total) {
-  const int t = blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= n_tiles) return;
+// Attention plan entry t: first KV tile only partly visible to query tile t
+// (n_full) and tiles it needs (n_total).
+__device__ __forceinline__ void plan_entry(const int32_t* __restrict__ T, int B, int group, int t,
+                                           int32_t* __restrict__ n_full,
+                                           int32_t* __restrict__ n_total) {
   const int P = B * group;
   const int p0 = t * KVR_ATTN_QROWS;
   const int p1 = min(P, p0 + KVR_ATTN_QROWS) - 1;
@@ -182,18 +183,34 @@ __global__ void k_build_plan(const int32_t* __restrict__ T, int B, int group, in
   n_total[t] = (u_max + KVR_ATTN_KV_TILE) / KVR_ATTN_KV_TILE;
 }
 
-// cos / sin of g * theta^(-2i/d) for every packed row and frequency, built in
-// float64 once per call and stored as float32 pairs [B][d/2].
-__global__ void k_rope_table(const int32_t* __restrict__ T, int B, int half, double theta,
-                             float2* __restrict__ tab) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * half) return;
+// cos / sin of g * theta^(-2i/d) for packed row r and frequency i, built in
+// float64 and stored as a float32 pair of the table [B][d/2].
+__device__ __forceinline__ void rope_entry(const int32_t* __restrict__ T, int half, double theta,
+                                           int idx, float2* __restrict__ tab) {
   const int r = idx / half, i = idx - r * half;
   const double inv = pow(theta, -(2.0 * i) / (2.0 * half));
   const double ang = static_cast<double>(T[r]) * inv;
   double sn, cs;
   sincos(ang, &sn, &cs);
   tab[idx] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
+}
+
+__global__ void k_build_plan(const int32_t* __restrict__ T, int B, int group, int n_tiles,
+                             int32_t* __restrict__ n_full, int32_t* __restrict__ n_total) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t < n_tiles) plan_entry(T, B, group, t, n_full, n_total);
+}
+
+// Both tables of a layer call in one launch: plan entries first, then the
+// rope table.
+__global__ void k_layer_tables(const int32_t* __restrict__ T, int B, int group, int n_tiles,
+                               int32_t* __restrict__ n_full, int32_t* __restrict__ n_total,
+                               int half, double theta, float2* __restrict__ tab) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx < n_tiles)
+    plan_entry(T, B, group, idx, n_full, n_total);
+  else if (idx - n_tiles < B * half)
+    rope_entry(T, half, theta, idx - n_tiles, tab);
 }
 
 }  // namespace
@@ -234,12 +251,13 @@ hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full
   return hipGetLastError();
 }
 
-hipError_t launch_rope_table(const int32_t* T, int B, int head_dim, double theta, float2* tab,
-                             hipStream_t stream) {
-  const int n = B * (head_dim / 2);
+hipError_t launch_layer_tables(const int32_t* T, int B, int group, int32_t* n_full,
+                              int32_t* n_total, int head_dim, double theta, float2* tab,
+                              hipStream_t stream) {
+  const int n = plan_tiles(B, group) + B * (head_dim / 2);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_rope_table, dim3((n + 255) / 256), dim3(256), 0, stream, T, B,
-                     head_dim / 2, theta, tab);
+  hipLaunchKernelGGL(k_layer_tables, dim3((n + 255) / 256), dim3(256), 0, stream, T, B, group,
+                     plan_tiles(B, group), n_full, n_total, head_dim / 2, theta, tab);
   return hipGetLastError();
 }
 

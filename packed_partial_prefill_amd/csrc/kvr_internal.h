@@ -27,8 +27,11 @@ hipError_t launch_check_support(const int32_t* T, int B, int n_tokens, int first
 int plan_tiles(int B, int group);
 hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full,
                              int32_t* n_total, hipStream_t stream);
-hipError_t launch_rope_table(const int32_t* T, int B, int head_dim, double theta, float2* tab,
-                             hipStream_t stream);
+// launch_build_plan plus the RoPE table (cos, sin of T[r] * theta^(-2i/d) as
+// float32 pairs [B][d/2], computed in float64) in one launch
+hipError_t launch_layer_tables(const int32_t* T, int B, int group, int32_t* n_full,
+                              int32_t* n_total, int head_dim, double theta, float2* tab,
+                              hipStream_t stream);
 
 // ---- norm.hip ---------------------------------------------------------------
 // x_res[r] = x_in[gather ? T[r] : r]; n_out[r] = RMSNorm(x_res[r]) * gamma.
