@@ -5,10 +5,13 @@
 // Eq. 22) with logits <q, k_j>/sqrt(d) + alpha*[local_j] + beta*[sink_j]
 // (cross-attention reuse page, 6.4) and an online softmax.
 //
-// bf16 storage runs on the MFMA kernel below (split-KV plus a merge kernel);
-// float32 storage runs on a VALU kernel: one wave per (row, head), each
-// 64-key step scores one key per lane, then accumulates P*V with every lane
-// owning d/64 output columns.
+// bf16 storage runs on MFMA kernels followed by a merge kernel: k_attn_pp
+// (d = 128, launches with many KV tiles per CU: two query tiles per
+// workgroup in ping-pong phases, stream-K schedule) or k_attn_mfma (d = 64
+// and small launches: one query tile per workgroup, split-KV); float32
+// storage runs on a VALU kernel: one wave per (row, head), each 64-key step
+// scores one key per lane, then accumulates P*V with every lane owning d/64
+// output columns.
 #include <type_traits>
 
 #include "common.h"
@@ -79,12 +82,12 @@ __global__ __launch_bounds__(64) void k_attn_rowwise(const T* __restrict__ q,
 // global_load_lds_dwordx4 (no register staging), with its 64 flag bytes, in
 // kAttnStages buffers (the tile in use and the ones in flight).  With 128
 // pairs, two workgroups share a CU in two stages each, so one computes while
-// the other waits at its barrier; 256 pairs per workgroup (half the staging
-// bytes per MFMA, three stages, one workgroup per CU) measured slower.
-// K and V are both in their
+// the other waits at its barrier; 256 pairs per workgroup without phase
+// offsets (half the staging bytes per MFMA, three stages, one workgroup per
+// CU) measured slower: both waves of a SIMD then compute and exponentiate at
+// the same time (k_attn_pp below offsets them).  K and V are both in their
 // natural [key][d] layout with the 16-byte chunks of each key row
-// XOR-swizzled, plus one 16-byte score slice per key written by 64 threads
-// (see below).
+// XOR-swizzled, and the tile's flag bytes give each key's bias slice.
 // Scores are formed transposed, S^T = K Q^T, so each lane owns one query
 // column and 16 of the tile's keys: the softmax reduction is in-lane plus one
 // exchange with lane ^ 32.  O^T += V^T P^T takes the lane's own P values as
@@ -1085,9 +1088,9 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
 }
 
 // Merge the split-KV partials: workgroup (query tile, KV group, kMergeD-row
-// slice of d); thread (pair ql, 8 consecutive d).  Split weights 2^(m_s - max m),
-// normalised by the weighted sums; each thread writes its pair's 8 outputs
-// (one 16-byte chunk of bf16, or two of float32).
+// slice of d); thread (pair ql, 8 consecutive d).  Partial weights
+// 2^(m_s - max m), normalised by the weighted sums; each thread writes its
+// pair's 8 outputs (one 16-byte chunk of bf16, or two of float32).
 constexpr int kMergeD = 8 * (kAttnThreads / kQRows);   // d rows per merge workgroup
 static_assert(kAttnThreads % kQRows == 0, "merge threads cover whole query tiles");
 
@@ -1119,22 +1122,30 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     slot0 = (static_cast<size_t>(qt) * Hkv + g) * n_splits;
     stride = 1;
   }
-  float mmax = -INFINITY;
-  // unrolled so that several splits' loads are in flight per thread
-#pragma unroll 8
-  for (int s = 0; s < ns; ++s) mmax = fmaxf(mmax, part_ml[(slot0 + s * stride) * 2 * kQRows + ql]);
-  float denom = 0.f, acc[8];
+  // One pass with a running maximum (the sums so far are rescaled when it
+  // grows), so that a partial's maximum, sum and O values are loaded
+  // together; unrolled so that several partials' loads are in flight.
+  // Partials that saw no key (maximum -inf) add nothing.
+  float mmax = -INFINITY, denom = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll 8
   for (int s = 0; s < ns; ++s) {
     const size_t sl = slot0 + s * stride;
     const float* pm = part_ml + sl * 2 * kQRows;
-    const float w = fast_exp2(pm[ql] - mmax);
-    denom += w * pm[kQRows + ql];
     const float* po = part_o + sl * D * kQRows + static_cast<size_t>(d0) * kQRows + ql;
+    const float ms = pm[ql], ls = pm[kQRows + ql];
+    float ov[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] += w * po[i * kQRows];
+    for (int i = 0; i < 8; ++i) ov[i] = po[i * kQRows];
+    const float mn = fmaxf(mmax, ms);
+    const bool none = mn == -INFINITY;
+    const float a = none ? 0.f : fast_exp2(mmax - mn);   // rescale of the sums so far
+    const float w = none ? 0.f : fast_exp2(ms - mn);
+    denom = denom * a + w * ls;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = acc[i] * a + w * ov[i];
+    mmax = mn;
   }
   const float inv = 1.f / denom;
   const int r = p / G, h = g * G + (p - r * G);
