@@ -72,34 +72,41 @@ template <typename T>
 __global__ __launch_bounds__(kThreads) void k_rope_writeback(
     const float* __restrict__ part, int splits, size_t split_stride, const float* __restrict__ bq,
     const float* __restrict__ bk, const float* __restrict__ bv, const float2* __restrict__ tab,
-    const int32_t* __restrict__ Tpos, Shape sh, float q_scale, T* __restrict__ q_out,
+    const int32_t* __restrict__ Tpos, int B, Shape sh, float q_scale, T* __restrict__ q_out,
     T* __restrict__ kc, T* __restrict__ vc, uint8_t* __restrict__ flags) {
-  const int r = blockIdx.x;
-  const int u = Tpos[r];
+  // One thread per item of a row: 4 rotated pairs of a query head, 4 rotated
+  // pairs of a key head, or 4 value columns (every load of the launch is
+  // then in flight at once; a workgroup per row looped over its items).
   const int d = sh.d, half = d >> 1, q4 = half >> 2, ncols = sh.qkv_cols();
+  const int n_q = sh.hq * q4, n_k = sh.hkv * q4, n_v = sh.hkv * (d >> 2);
+  const int per_row = n_q + n_k + n_v;
+  const size_t t = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (t >= static_cast<size_t>(B) * per_row) return;
+  const int r = static_cast<int>(t / per_row);
+  int idx = static_cast<int>(t - static_cast<size_t>(r) * per_row);
+  const int u = Tpos[r];
   const float* pr = part + static_cast<size_t>(r) * ncols;
   const float2* tr = tab + static_cast<size_t>(r) * half;
-  // query heads (times the attention kernel's score factor)
-  for (int idx = threadIdx.x; idx < sh.hq * q4; idx += kThreads) {
+  if (idx < n_q) {   // query heads (times the attention kernel's score factor)
     const int h = idx / q4, i = (idx - h * q4) * 4;
     rotate4<T>(pr, splits, split_stride, bq, h * d + i, half, tr + i, q_scale,
                q_out + (static_cast<size_t>(r) * sh.hq + h) * d + i);
+    return;
   }
-  // key heads: rotated, written to cache row u
-  const int kbase = sh.hq * d;
-  for (int idx = threadIdx.x; idx < sh.hkv * q4; idx += kThreads) {
+  idx -= n_q;
+  if (idx < n_k) {   // key heads: rotated, written to cache row u
     const int g = idx / q4, i = (idx - g * q4) * 4;
-    rotate4<T>(pr + kbase, splits, split_stride, bk, g * d + i, half, tr + i, 1.f,
+    rotate4<T>(pr + sh.hq * d, splits, split_stride, bk, g * d + i, half, tr + i, 1.f,
                kc + (static_cast<size_t>(u) * sh.hkv + g) * d + i);
+    if (idx == 0)
+      flags[u] = static_cast<uint8_t>(flags[u] & ~(KVR_FLAG_LOCAL | KVR_FLAG_SINK));
+    return;
   }
-  // values: copied to cache row u
+  idx -= n_k;        // values: copied to cache row u
   const int vbase = (sh.hq + sh.hkv) * d;
-  for (int idx = threadIdx.x; idx < sh.hkv * (d >> 2); idx += kThreads) {
-    float4 a = cols4(pr, splits, split_stride, vbase + idx * 4);
-    if (bv) a = add4(a, *reinterpret_cast<const float4*>(bv + idx * 4));
-    put4<T>(vc + static_cast<size_t>(u) * sh.hkv * d + idx * 4, a);
-  }
-  if (threadIdx.x == 0) flags[u] = static_cast<uint8_t>(flags[u] & ~(KVR_FLAG_LOCAL | KVR_FLAG_SINK));
+  float4 a = cols4(pr, splits, split_stride, vbase + idx * 4);
+  if (bv) a = add4(a, *reinterpret_cast<const float4*>(bv + idx * 4));
+  put4<T>(vc + static_cast<size_t>(u) * sh.hkv * d + idx * 4, a);
 }
 
 // Queries handed in from outside the repair (inference mode): scaled by the
@@ -136,14 +143,19 @@ hipError_t launch_rope_writeback(kvr_dtype dt, const float* qkv_part, int splits
                                  const Shape& sh, float q_scale, void* q_out, void* k_cache,
                                  void* v_cache, uint8_t* flags, hipStream_t stream) {
   if (B == 0) return hipSuccess;
+  const int q4 = sh.d / 8;
+  const size_t items = static_cast<size_t>(B) * ((sh.hq + sh.hkv) * q4 + sh.hkv * (sh.d / 4));
+  const dim3 grid(static_cast<unsigned>((items + kThreads - 1) / kThreads));
   if (dt == KVR_BF16)
-    hipLaunchKernelGGL(k_rope_writeback<bf16_t>, dim3(B), dim3(kThreads), 0, stream, qkv_part,
-                       splits, split_stride, bq, bk, bv, tab, T, sh, q_scale, static_cast<bf16_t*>(q_out),
-                       static_cast<bf16_t*>(k_cache), static_cast<bf16_t*>(v_cache), flags);
+    hipLaunchKernelGGL(k_rope_writeback<bf16_t>, grid, dim3(kThreads), 0, stream, qkv_part,
+                       splits, split_stride, bq, bk, bv, tab, T, B, sh, q_scale,
+                       static_cast<bf16_t*>(q_out), static_cast<bf16_t*>(k_cache),
+                       static_cast<bf16_t*>(v_cache), flags);
   else
-    hipLaunchKernelGGL(k_rope_writeback<float>, dim3(B), dim3(kThreads), 0, stream, qkv_part,
-                       splits, split_stride, bq, bk, bv, tab, T, sh, q_scale, static_cast<float*>(q_out),
-                       static_cast<float*>(k_cache), static_cast<float*>(v_cache), flags);
+    hipLaunchKernelGGL(k_rope_writeback<float>, grid, dim3(kThreads), 0, stream, qkv_part,
+                       splits, split_stride, bq, bk, bv, tab, T, B, sh, q_scale,
+                       static_cast<float*>(q_out), static_cast<float*>(k_cache),
+                       static_cast<float*>(v_cache), flags);
   return hipGetLastError();
 }
 
