@@ -83,6 +83,8 @@ __global__ __launch_bounds__(kRowThreads) void k_residual_norm(
     const int j4 = threadIdx.x + c * kRowThreads;
     if (j4 < h4) {
       float4 a = xr[j4];
+      // unrolled so that several partials' loads are in flight together
+#pragma unroll 8
       for (int s = 0; s < splits; ++s) {
         const float4 p = pr[s * ps4 + j4];
         a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;

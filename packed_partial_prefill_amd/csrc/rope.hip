@@ -38,6 +38,7 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 // Sum of the split-K partials of 4 consecutive columns starting at c.
 __device__ __forceinline__ float4 cols4(const float* pr, int splits, size_t split_stride, int c) {
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
   for (int s = 0; s < splits; ++s)
     a = add4(a, *reinterpret_cast<const float4*>(pr + s * split_stride + c));
   return a;
