@@ -427,6 +427,8 @@ __global__ __launch_bounds__(kRedThreads) void k_swiglu_reduce(const float* __re
   const size_t stride4 = static_cast<size_t>(M) * 2 * n4;
   const float4* g4 = reinterpret_cast<const float4*>(part) + m * 2 * n4 + j;
   float4 g = g4[0], u = g4[n4];
+  // unrolled so that several partials' loads are in flight together
+#pragma unroll 8
   for (int s = 1; s < splits; ++s) {
     const float4 a = g4[s * stride4], c = g4[s * stride4 + n4];
     g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
