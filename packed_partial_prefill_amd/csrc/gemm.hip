@@ -387,28 +387,56 @@ __global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
   }
 
   // epilogue
+  if constexpr (MODE == 0) {
 #pragma unroll
-  for (int mb = 0; mb < TM; ++mb) {
+    for (int mb = 0; mb < TM; ++mb) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int m = m0 + (wm * TM + mb) * 32 + 8 * (e >> 2) + 4 * khalf + (e & 3);
-      if (m >= M) continue;
-      if (MODE == 0) {
+      for (int e = 0; e < 16; ++e) {
+        const int m = m0 + (wm * TM + mb) * 32 + 8 * (e >> 2) + 4 * khalf + (e & 3);
+        if (m >= M) continue;
         float* crow = part + (static_cast<size_t>(split) * M + m) * N;
 #pragma unroll
         for (int nb = 0; nb < TN; ++nb) {
           const int n = n0 + (wn * TN + nb) * 32 + (lane & 31);
           if (n < N) crow[n] = acc[mb][nb][e];
         }
-      } else {
+      }
+    }
+  } else {
+    // SiLU(gate) * up in bf16, staged through LDS (free once every wave is
+    // past its last stage read) so that the tile leaves in 16-byte row
+    // chunks rather than 2-byte stores.  SiLU uses the hardware exp2 and
+    // reciprocal (each within an ulp or two of float32; the result is
+    // rounded to bf16).
+    constexpr int OC = BN / 2;                 // output columns of the tile
+    constexpr int RS = OC * 2 + 16;            // LDS row stride in bytes (padded)
+    static_assert(BM * RS <= C::smem, "output tile fits the stage buffers");
+    stage_barrier();
+#pragma unroll
+    for (int mb = 0; mb < TM; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rl = (wm * TM + mb) * 32 + 8 * (e >> 2) + 4 * khalf + (e & 3);
 #pragma unroll
         for (int nb = 0; nb < TN / 2; ++nb) {
-          const int n = n0 + (wn * (TN / 2) + nb) * 32 + (lane & 31);
-          if (n < N) {
-            const float gt = acc[mb][nb][e], up = acc[mb][nb + TN / 2][e];
-            out[static_cast<size_t>(m) * N + n] = f32_to_bf16(gt / (1.f + expf(-gt)) * up);
-          }
+          const int cl = (wn * (TN / 2) + nb) * 32 + (lane & 31);
+          const float gt = acc[mb][nb][e], up = acc[mb][nb + TN / 2][e];
+          const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-gt * 1.4426950408889634f));
+          *reinterpret_cast<bf16_t*>(smem + rl * RS + cl * 2) = f32_to_bf16(gt * sg * up);
         }
+      }
+    __syncthreads();
+    constexpr int CH = OC / 8;                 // 16-byte chunks per output row
+    for (int i = tid; i < BM * CH; i += C::threads) {
+      const int rl = i / CH, ch = i - rl * CH;
+      const int m = m0 + rl, n = n0 + ch * 8;
+      if (m >= M || n >= N) continue;
+      const uint8_t* src = smem + rl * RS + ch * 16;
+      bf16_t* dst = out + static_cast<size_t>(m) * N + n;
+      if (n + 8 <= N && (N & 7) == 0) {
+        *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(src);
+      } else {
+        for (int k = 0; k < 8 && n + k < N; ++k) dst[k] = reinterpret_cast<const bf16_t*>(src)[k];
       }
     }
   }
