@@ -388,17 +388,40 @@ __global__ __launch_bounds__(C::threads, C::waves_per_simd) void k_gemm_mfma(
 
   // epilogue
   if constexpr (MODE == 0) {
+    // float32 partials, staged through LDS one band of TM * 32 rows (one
+    // wave row) at a time so that they leave in 16-byte row chunks
+    constexpr int RB = TM * 32;                // rows per band
+    constexpr int RS = BN * 4 + 16;            // LDS row stride in bytes (padded)
+    constexpr int CH = BN / 4;                 // 16-byte chunks per row
+    static_assert(RB * RS <= C::smem, "band fits the stage buffers");
+    float* pbase = part + static_cast<size_t>(split) * M * N;
+#pragma unroll 1
+    for (int band = 0; band < C::WM; ++band) {
+      stage_barrier();   // the previous band (or the last stage) has been read
+      if (wm == band) {
 #pragma unroll
-    for (int mb = 0; mb < TM; ++mb) {
+        for (int mb = 0; mb < TM; ++mb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int m = m0 + (wm * TM + mb) * 32 + 8 * (e >> 2) + 4 * khalf + (e & 3);
-        if (m >= M) continue;
-        float* crow = part + (static_cast<size_t>(split) * M + m) * N;
+          for (int e = 0; e < 16; ++e) {
+            const int rl = mb * 32 + 8 * (e >> 2) + 4 * khalf + (e & 3);
 #pragma unroll
-        for (int nb = 0; nb < TN; ++nb) {
-          const int n = n0 + (wn * TN + nb) * 32 + (lane & 31);
-          if (n < N) crow[n] = acc[mb][nb][e];
+            for (int nb = 0; nb < TN; ++nb) {
+              const int cl = (wn * TN + nb) * 32 + (lane & 31);
+              *reinterpret_cast<float*>(smem + rl * RS + cl * 4) = acc[mb][nb][e];
+            }
+          }
+      }
+      __syncthreads();
+      for (int i = tid; i < RB * CH; i += C::threads) {
+        const int rl = i / CH, ch = i - rl * CH;
+        const int m = m0 + band * RB + rl, n = n0 + ch * 4;
+        if (m >= M || n >= N) continue;
+        const uint8_t* src = smem + rl * RS + ch * 16;
+        float* dst = pbase + static_cast<size_t>(m) * N + n;
+        if (n + 4 <= N && (N & 3) == 0) {
+          *reinterpret_cast<float4*>(dst) = *reinterpret_cast<const float4*>(src);
+        } else {
+          for (int k = 0; k < 4 && n + k < N; ++k) dst[k] = reinterpret_cast<const float*>(src)[k];
         }
       }
     }
