@@ -13,6 +13,9 @@ namespace kvr {
 namespace {
 
 constexpr int kBuildThreads = 1024;
+// T and the run openings are also kept in LDS up to this many entries, so
+// the run pass reads them back without a round trip to memory.
+constexpr int kBuildLds = 4096;
 
 // Exclusive prefix sum over a 1024-thread workgroup; *total gets the sum.
 __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
@@ -64,6 +67,8 @@ __global__ __launch_bounds__(kBuildThreads) void k_build_repair_set(
     int32_t* __restrict__ run_len, int32_t* __restrict__ counts, int cap) {
   __shared__ int wsum[16];
   __shared__ int s_bad;
+  __shared__ int sT[kBuildLds];      // T, when it fits
+  __shared__ int sOpen[kBuildLds];   // index in T of each run's first position, when they fit
   const int tid = threadIdx.x;
   if (tid == 0) s_bad = 0;
   __syncthreads();
@@ -96,6 +101,7 @@ __global__ __launch_bounds__(kBuildThreads) void k_build_repair_set(
   }
 
   // 3. fill T: block i writes its ranges at its exclusive offset
+  const bool lds_t = total <= kBuildLds;
   int off0 = 0;
   for (int base = 0; base < m; base += blockDim.x) {
     const int i = base + tid;
@@ -103,34 +109,50 @@ __global__ __launch_bounds__(kBuildThreads) void k_build_repair_set(
     if (i < m) r = block_ranges(i, m, s[i], e[i], tau, asym != 0);
     int chunk;
     int off = off0 + block_exclusive_scan(i < m ? r.count() : 0, wsum, &chunk);
-    for (int t = r.a0; t < r.a1; ++t) T[off++] = t;
-    for (int t = r.b0; t < r.b1; ++t) T[off++] = t;
+    for (int t = r.a0; t < r.a1; ++t) {
+      if (lds_t) sT[off] = t;
+      T[off++] = t;
+    }
+    for (int t = r.b0; t < r.b1; ++t) {
+      if (lds_t) sT[off] = t;
+      T[off++] = t;
+    }
     off0 += chunk;
   }
   __threadfence_block();
   __syncthreads();
+  auto t_at = [&](int k) { return lds_t ? sT[k] : T[k]; };
 
   // 4. maximal runs: T[k] opens a run unless T[k] == T[k-1] + 1.  run_len
   //    first holds the opening index, then the length.
   int nruns = 0;
   for (int base = 0; base < total; base += blockDim.x) {
     const int k = base + tid;
-    const int open = (k < total) && (k == 0 || T[k] != T[k - 1] + 1);
+    const int open = (k < total) && (k == 0 || t_at(k) != t_at(k - 1) + 1);
     int chunk;
     const int id = nruns + block_exclusive_scan(open, wsum, &chunk);
-    if (open) { run_start[id] = T[k]; run_len[id] = k; }
+    if (open) {
+      run_start[id] = t_at(k);
+      if (id < kBuildLds) sOpen[id] = k;
+      run_len[id] = k;
+    }
     nruns += chunk;
   }
   __threadfence_block();
   __syncthreads();
-  for (int base = 0; base < nruns; base += blockDim.x) {
-    const int j = base + tid;
-    int len = 0;
-    if (j < nruns) len = ((j + 1 < nruns) ? run_len[j + 1] : total) - run_len[j];
-    __syncthreads();
-    if (j < nruns) run_len[j] = len;
-    __threadfence_block();
-    __syncthreads();
+  if (nruns <= kBuildLds) {
+    for (int j = tid; j < nruns; j += blockDim.x)
+      run_len[j] = ((j + 1 < nruns) ? sOpen[j + 1] : total) - sOpen[j];
+  } else {
+    for (int base = 0; base < nruns; base += blockDim.x) {
+      const int j = base + tid;
+      int len = 0;
+      if (j < nruns) len = ((j + 1 < nruns) ? run_len[j + 1] : total) - run_len[j];
+      __syncthreads();
+      if (j < nruns) run_len[j] = len;
+      __threadfence_block();
+      __syncthreads();
+    }
   }
   if (tid == 0) { counts[0] = total; counts[1] = nruns; counts[2] = KVR_OK; }
 }
