@@ -66,8 +66,12 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_norm(
 }
 
 // x_res[r] += sum_s part[s][r]; when gamma is given, n_out[r] = RMSNorm(x_res[r]) * gamma.
-template <typename T>
-__global__ __launch_bounds__(kRowThreads) void k_residual_norm(
+// NC = float4 chunks per thread, ceil(hidden / 4 / kRowThreads).
+// (at most 4 waves per SIMD: room for every chunk's loads in flight; the
+// default occupancy target made the scheduler reuse one register set and
+// wait for each load)
+template <typename T, int NC>
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_residual_norm(
     float* __restrict__ x_res, const float* __restrict__ part, int splits, size_t split_stride,
     const float* __restrict__ gamma, float eps, T* __restrict__ n_out, int hidden) {
   __shared__ float red[16];
@@ -76,20 +80,31 @@ __global__ __launch_bounds__(kRowThreads) void k_residual_norm(
   float4* xr = reinterpret_cast<float4*>(x_res + static_cast<size_t>(r) * hidden);
   const float4* pr = reinterpret_cast<const float4*>(part + static_cast<size_t>(r) * hidden);
   const size_t ps4 = split_stride >> 2;
-  float4 v[kMaxChunks];
+  // Chunks past the row's end read its last chunk (discarded), so that the
+  // loads need no branch and every chunk's loads (residual, then the
+  // partials in split order) can be in flight together.
+  int jc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) jc[c] = min(static_cast<int>(threadIdx.x) + c * kRowThreads, h4 - 1);
+  float4 v[NC];
   float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < NC; ++c) v[c] = xr[jc[c]];
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    float4 p[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) p[c] = pr[s * ps4 + jc[c]];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      v[c].x += p[c].x; v[c].y += p[c].y; v[c].z += p[c].z; v[c].w += p[c].w;
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
     const int j4 = threadIdx.x + c * kRowThreads;
     if (j4 < h4) {
-      float4 a = xr[j4];
-      // unrolled so that several partials' loads are in flight together
-#pragma unroll 8
-      for (int s = 0; s < splits; ++s) {
-        const float4 p = pr[s * ps4 + j4];
-        a.x += p.x; a.y += p.y; a.z += p.z; a.w += p.w;
-      }
-      v[c] = a;
+      const float4 a = v[c];
       xr[j4] = a;
       ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
     }
@@ -100,10 +115,25 @@ __global__ __launch_bounds__(kRowThreads) void k_residual_norm(
   T* no = n_out + static_cast<size_t>(r) * hidden;
   const float4* g4 = reinterpret_cast<const float4*>(gamma);
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int j4 = threadIdx.x + c * kRowThreads;
     if (j4 < h4) store4<T>(no, j4, scale4(v[c], rs, g4[j4]));
   }
+}
+
+template <typename T, int NC>
+void launch_residual_norm_t(float* x_res, const float* part, int splits, size_t split_stride,
+                            const float* gamma, float eps, T* n_out, int B, int hidden,
+                            hipStream_t stream) {
+  if constexpr (NC < kMaxChunks) {
+    if (hidden > 4 * kRowThreads * NC) {
+      launch_residual_norm_t<T, NC + 1>(x_res, part, splits, split_stride, gamma, eps, n_out, B,
+                                        hidden, stream);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_residual_norm<T, NC>), dim3(B), dim3(kRowThreads), 0, stream, x_res, part,
+                     splits, split_stride, gamma, eps, n_out, hidden);
 }
 
 }  // namespace
@@ -126,13 +156,11 @@ hipError_t launch_residual_norm(kvr_dtype dt, float* x_res, const float* part, i
                                 int B, int hidden, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   if (dt == KVR_BF16)
-    hipLaunchKernelGGL(k_residual_norm<bf16_t>, dim3(B), dim3(kRowThreads), 0, stream, x_res,
-                       part, splits, split_stride, gamma, eps, static_cast<bf16_t*>(n_out),
-                       hidden);
+    launch_residual_norm_t<bf16_t, 1>(x_res, part, splits, split_stride, gamma, eps,
+                                      static_cast<bf16_t*>(n_out), B, hidden, stream);
   else
-    hipLaunchKernelGGL(k_residual_norm<float>, dim3(B), dim3(kRowThreads), 0, stream, x_res,
-                       part, splits, split_stride, gamma, eps, static_cast<float*>(n_out),
-                       hidden);
+    launch_residual_norm_t<float, 1>(x_res, part, splits, split_stride, gamma, eps,
+                                     static_cast<float*>(n_out), B, hidden, stream);
   return hipGetLastError();
 }
 
