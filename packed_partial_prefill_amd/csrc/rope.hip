@@ -35,13 +35,28 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
 }
 
-// Sum of the split-K partials of 4 consecutive columns starting at c.
+// Sum of the split-K partials of 4 consecutive columns starting at c (in
+// split order; unrolled by 4 so that those loads are in flight together).
 __device__ __forceinline__ float4 cols4(const float* pr, int splits, size_t split_stride, int c) {
   float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
+#pragma unroll 4
   for (int s = 0; s < splits; ++s)
     a = add4(a, *reinterpret_cast<const float4*>(pr + s * split_stride + c));
   return a;
+}
+
+// The same for the columns c and c + half of a rotated pair, in one loop.
+__device__ __forceinline__ void cols4x2(const float* pr, int splits, size_t split_stride, int c,
+                                        int half, float4& a, float4& b) {
+  a = make_float4(0.f, 0.f, 0.f, 0.f);
+  b = a;
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    const float4 pa = *reinterpret_cast<const float4*>(pr + s * split_stride + c);
+    const float4 pb = *reinterpret_cast<const float4*>(pr + s * split_stride + c + half);
+    a = add4(a, pa);
+    b = add4(b, pb);
+  }
 }
 
 // Rotate 4 consecutive pairs (i .. i+3, i+half .. i+half+3) of one head.
@@ -49,8 +64,8 @@ template <typename T>
 __device__ __forceinline__ void rotate4(const float* pr, int splits, size_t split_stride,
                                         const float* bias, int c0, int half,
                                         const float2* tr, float scale, T* dst) {
-  float4 a = cols4(pr, splits, split_stride, c0);
-  float4 b = cols4(pr, splits, split_stride, c0 + half);
+  float4 a, b;
+  cols4x2(pr, splits, split_stride, c0, half, a, b);
   if (bias) {
     a = add4(a, *reinterpret_cast<const float4*>(bias + c0));
     b = add4(b, *reinterpret_cast<const float4*>(bias + c0 + half));
@@ -69,8 +84,10 @@ __device__ __forceinline__ void rotate4(const float* pr, int splits, size_t spli
   put4<T>(dst + half, make_float4(hi[0], hi[1], hi[2], hi[3]));
 }
 
+// (at most 4 waves per SIMD, so that the scheduler keeps the partial loads of
+// an item in flight together rather than reusing one register set)
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_rope_writeback(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_rope_writeback(
     const float* __restrict__ part, int splits, size_t split_stride, const float* __restrict__ bq,
     const float* __restrict__ bk, const float* __restrict__ bv, const float2* __restrict__ tab,
     const int32_t* __restrict__ Tpos, int B, Shape sh, float q_scale, T* __restrict__ q_out,
