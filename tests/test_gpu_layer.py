@@ -100,6 +100,18 @@ def test_tiny_bf16_head_dim_128_group_6():
     run_layer_case(w)
 
 
+def test_bf16_large_m_ragged_projections():
+    """600 packed rows (the 256 x 256 projection tiles, split-K and the fused
+    gate/up with weights in 128-byte pairs) on shapes that leave partial
+    tiles everywhere: M = 600, hidden 320 (five K pairs, an odd count),
+    intermediate 576 (a half gate/up tile), QKV width 512."""
+    w = wl.Workload("ragged-proj-bf16", 103, hidden=320, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                    intermediate=576, n_layers=1, n_tokens=1024, block_size=128, dtype="bf16",
+                    alpha=-1.0, beta=-2.0, support="contiguous", support_start=300,
+                    support_len=600)
+    run_layer_case(w)
+
+
 def test_qwen15_layer_seams():
     run_layer_case(wl.QWEN15_LAYER)
 
