@@ -164,8 +164,9 @@ struct Tile {
   static_assert(LA * 16 * waves == BM && LW * 16 * waves == BN, "whole DMA slices per wave");
   static_assert(TN % 2 == 0, "gate and up blocks pair up in the fused SwiGLU epilogue");
   static_assert(NS >= 3 && NS <= 6 && (NS - 2) * LS < 64, "pipeline depth and vmcnt range");
-  static_assert(!WP || (NS % 2 == 0 && LWP * 8 * waves == BN && 2 * LA + LWP < 64),
-                "pair steps line up with the A stages; whole pieces; vmcnt range");
+  static_assert(!WP || (NS == 4 && LWP * 8 * waves == BN && 2 * LA + LWP < 64),
+                "the pair schedule (prologue and vmcnt counts) is laid out for 4 A stages; "
+                "whole pieces; vmcnt range");
   // one dynamic LDS buffer: the NS A stages, then the NS W stages, so that a
   // fragment address is a lane register plus a compile-time offset
   static constexpr int aOff(int s) { return s * ABytes; }
