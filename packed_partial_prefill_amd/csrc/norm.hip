@@ -31,8 +31,12 @@ __device__ __forceinline__ float4 scale4(float4 v, float s, float4 g) {
   return make_float4(v.x * s * g.x, v.y * s * g.y, v.z * s * g.z, v.w * s * g.w);
 }
 
-template <typename T>
-__global__ __launch_bounds__(kRowThreads) void k_gather_norm(
+// x_res[r] = x_in[gather_T[r]] (or x_in[r]); n_out[r] = RMSNorm(x_res[r]) * gamma.
+// NC = float4 chunks per thread; chunks past the row's end load its last
+// chunk (discarded) so that every load is unconditional and all of them,
+// gamma's included, are in flight together.
+template <typename T, int NC>
+__global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_gather_norm(
     const float* __restrict__ x_in, const int32_t* __restrict__ gather_T, float* x_res,
     const float* __restrict__ gamma, float eps, T* __restrict__ n_out, int hidden) {
   __shared__ float red[16];
@@ -40,27 +44,31 @@ __global__ __launch_bounds__(kRowThreads) void k_gather_norm(
   const int h4 = hidden >> 2;
   const size_t src = gather_T ? static_cast<size_t>(gather_T[r]) : static_cast<size_t>(r);
   const float4* xr = reinterpret_cast<const float4*>(x_in + src * hidden);
-  float4 v[kMaxChunks];
+  const float4* g4 = reinterpret_cast<const float4*>(gamma);
+  int jc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) jc[c] = min(static_cast<int>(threadIdx.x) + c * kRowThreads, h4 - 1);
+  float4 v[NC], g[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) v[c] = xr[jc[c]];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) g[c] = g4[jc[c]];
   float ss = 0.f;
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
-    const int j4 = threadIdx.x + c * kRowThreads;
-    if (j4 < h4) {
-      v[c] = xr[j4];
-      ss += v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
-    }
+  for (int c = 0; c < NC; ++c) {
+    const float q = v[c].x * v[c].x + v[c].y * v[c].y + v[c].z * v[c].z + v[c].w * v[c].w;
+    ss += static_cast<int>(threadIdx.x) + c * kRowThreads < h4 ? q : 0.f;
   }
   const float tot = block_sum(ss, red);  // all reads of x_in precede any write
   const float rs = rsqrtf(tot / hidden + eps);
   float4* xo = reinterpret_cast<float4*>(x_res + static_cast<size_t>(r) * hidden);
   T* no = n_out + static_cast<size_t>(r) * hidden;
-  const float4* g4 = reinterpret_cast<const float4*>(gamma);
 #pragma unroll
-  for (int c = 0; c < kMaxChunks; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const int j4 = threadIdx.x + c * kRowThreads;
     if (j4 < h4) {
       xo[j4] = v[c];
-      store4<T>(no, j4, scale4(v[c], rs, g4[j4]));
+      store4<T>(no, j4, scale4(v[c], rs, g[c]));
     }
   }
 }
@@ -136,6 +144,20 @@ void launch_residual_norm_t(float* x_res, const float* part, int splits, size_t 
                      splits, split_stride, gamma, eps, n_out, hidden);
 }
 
+template <typename T, int NC>
+void launch_gather_norm_t(const float* x_in, const int32_t* gather_T, float* x_res,
+                          const float* gamma, float eps, T* n_out, int B, int hidden,
+                          hipStream_t stream) {
+  if constexpr (NC < kMaxChunks) {
+    if (hidden > 4 * kRowThreads * NC) {
+      launch_gather_norm_t<T, NC + 1>(x_in, gather_T, x_res, gamma, eps, n_out, B, hidden, stream);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((k_gather_norm<T, NC>), dim3(B), dim3(kRowThreads), 0, stream, x_in, gather_T,
+                     x_res, gamma, eps, n_out, hidden);
+}
+
 }  // namespace
 
 hipError_t launch_gather_norm(kvr_dtype dt, const float* x_in, const int32_t* gather_T,
@@ -143,11 +165,11 @@ hipError_t launch_gather_norm(kvr_dtype dt, const float* x_in, const int32_t* ga
                               int hidden, hipStream_t stream) {
   if (B == 0) return hipSuccess;
   if (dt == KVR_BF16)
-    hipLaunchKernelGGL(k_gather_norm<bf16_t>, dim3(B), dim3(kRowThreads), 0, stream, x_in,
-                       gather_T, x_res, gamma, eps, static_cast<bf16_t*>(n_out), hidden);
+    launch_gather_norm_t<bf16_t, 1>(x_in, gather_T, x_res, gamma, eps, static_cast<bf16_t*>(n_out),
+                                    B, hidden, stream);
   else
-    hipLaunchKernelGGL(k_gather_norm<float>, dim3(B), dim3(kRowThreads), 0, stream, x_in,
-                       gather_T, x_res, gamma, eps, static_cast<float*>(n_out), hidden);
+    launch_gather_norm_t<float, 1>(x_in, gather_T, x_res, gamma, eps, static_cast<float*>(n_out),
+                                   B, hidden, stream);
   return hipGetLastError();
 }
 
