@@ -1122,29 +1122,43 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
     slot0 = (static_cast<size_t>(qt) * Hkv + g) * n_splits;
     stride = 1;
   }
-  // One pass with a running maximum (the sums so far are rescaled when it
-  // grows), so that a partial's maximum, sum and O values are loaded
-  // together; unrolled so that several partials' loads are in flight.
-  // Partials that saw no key (maximum -inf) add nothing.
+  // Partials four at a time with a running maximum (the sums so far are
+  // rescaled when it grows): the four partials' maxima, sums and O values
+  // are loaded together, indices past the last partial clamped to it and
+  // their weights zeroed, so that a segment of up to four pieces (the usual
+  // count) costs one round trip.  Partials that saw no key (maximum -inf)
+  // add nothing.
+  constexpr int kChunk = 4;
   float mmax = -INFINITY, denom = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-#pragma unroll 8
-  for (int s = 0; s < ns; ++s) {
-    const size_t sl = slot0 + s * stride;
-    const float* pm = part_ml + sl * 2 * kQRows;
-    const float* po = part_o + sl * D * kQRows + static_cast<size_t>(d0) * kQRows + ql;
-    const float ms = pm[ql], ls = pm[kQRows + ql];
-    float ov[8];
+  for (int s0 = 0; s0 < ns; s0 += kChunk) {
+    float ms[kChunk], ls[kChunk], ov[kChunk][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) ov[i] = po[i * kQRows];
-    const float mn = fmaxf(mmax, ms);
+    for (int k = 0; k < kChunk; ++k) {
+      const size_t sl = slot0 + static_cast<size_t>(min(s0 + k, ns - 1)) * stride;
+      const float* pm = part_ml + sl * 2 * kQRows;
+      const float* po = part_o + sl * D * kQRows + static_cast<size_t>(d0) * kQRows + ql;
+      ms[k] = s0 + k < ns ? pm[ql] : -INFINITY;
+      ls[k] = pm[kQRows + ql];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ov[k][i] = po[i * kQRows];
+    }
+    float mn = mmax;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) mn = fmaxf(mn, ms[k]);
     const bool none = mn == -INFINITY;
     const float a = none ? 0.f : fast_exp2(mmax - mn);   // rescale of the sums so far
-    const float w = none ? 0.f : fast_exp2(ms - mn);
-    denom = denom * a + w * ls;
+    denom *= a;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = acc[i] * a + w * ov[i];
+    for (int i = 0; i < 8; ++i) acc[i] *= a;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float w = none ? 0.f : fast_exp2(ms[k] - mn);   // 0 for ms = -inf
+      denom += w * ls[k];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += w * ov[k][i];
+    }
     mmax = mn;
   }
   const float inv = 1.f / denom;
