@@ -211,7 +211,9 @@ struct GemmThread {
   int adst[C::LA], wdst[NW];   // wave-uniform LDS byte offset of each 1 KB slice
   // fragment LDS addresses in stage (pair slot) 0, per K half (for W pairs
   // those of the pair's first step: the second step's chunk differs in bit
-  // 2, which is address bit 6 in a 128-byte row)
+  // 2, which is address bit 6 in a 128-byte row, the pair slots starting
+  // on 128-byte boundaries of an LDS buffer at address 0 -- the kernel has
+  // no static LDS)
   uint32_t la[C::TM][2], lw[C::TN][2];
   uint8_t* smem;
 };
