@@ -112,6 +112,17 @@ def test_bf16_large_m_ragged_projections():
     run_layer_case(w)
 
 
+def test_bf16_m513_one_row_past_the_small_tiles():
+    """513 packed rows: the first size on the 256 x 256 projection path, its
+    third M tile holding a single row (every other row of that tile clamped
+    on load and masked on store)."""
+    w = wl.Workload("m513-bf16", 104, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                    intermediate=384, n_layers=1, n_tokens=800, block_size=200, dtype="bf16",
+                    alpha=-0.5, beta=-1.5, support="contiguous", support_start=200,
+                    support_len=513)
+    run_layer_case(w)
+
+
 def test_qwen15_layer_seams():
     run_layer_case(wl.QWEN15_LAYER)
 
