@@ -1132,6 +1132,9 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
   float mmax = -INFINITY, denom = 0.f, acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  // (two chunks per iteration when there are more: the split kernel's
+  // segments can have a dozen partials or more)
+#pragma unroll 2
   for (int s0 = 0; s0 < ns; s0 += kChunk) {
     float ms[kChunk], ls[kChunk], ov[kChunk][8];
 #pragma unroll
