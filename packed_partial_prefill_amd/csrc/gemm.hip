@@ -125,8 +125,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_fma(const T* __restrict__ A, 
 // pieces).  With every CU streaming from L2, 128-byte pieces move about 1.5x
 // the bytes per clock of 64-byte ones (a 64-byte piece costs the L2 -> L1
 // path a whole line); the pair ring also gives W a step more of lead.
-// Measured 4% faster for gate/up at the 7B layer; slower for the split-K
-// projections, which keep 64-byte pieces.
+// Measured 4% faster for gate/up at the 7B layer (8% at the 1.5B layer's
+// 128 x 128 tile, 6% at M = 64); slower for the split-K projections, which
+// keep 64-byte pieces.
 //
 // Tile shapes: 256 x 256 (8 waves) for large M; 128 x 128 (4 waves, two
 // workgroups per CU) and 64 x 128 (2 waves, three per CU, deeper pipeline)
@@ -181,7 +182,9 @@ struct Tile {
 using TileL = Tile<256, 256, 4, 2, 4, 1>;
 using TileLP = Tile<256, 256, 4, 2, 4, 1, true>;    // W pairs: fused gate/up, K a multiple of 64
 using TileM = Tile<128, 128, 2, 2, 4, 2>;
+using TileMP = Tile<128, 128, 2, 2, 4, 2, true>;    // W pairs: fused gate/up
 using TileS = Tile<64, 128, 1, 2, 6, 2>;
+using TileSP = Tile<64, 128, 1, 2, 4, 2, true>;     // W pairs: fused gate/up
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * (KB * 2) + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -590,21 +593,27 @@ void launch_mfma(const bf16_t* A, const WeightSegs& W, int M, int N, int K, int 
                      stream, A, W, M, N, K, kps, tm, tn, splits, part, out);
 }
 
+// The fused gate/up takes the W-pair form CP of a tile when K allows it
+// (measured 4-8% faster); the split-K projections keep C (slower with pairs).
+template <int MODE, class CP, class C>
+void launch_tile(const bf16_t* A, const WeightSegs& W, int M, int N, int K, int splits, float* part,
+                 bf16_t* out, hipStream_t stream) {
+  if constexpr (MODE == 1) {
+    if (K % (2 * KB) == 0) {
+      launch_mfma<MODE, CP>(A, W, M, N, K, splits, part, out, stream);
+      return;
+    }
+  }
+  launch_mfma<MODE, C>(A, W, M, N, K, splits, part, out, stream);
+}
+
 template <int MODE>
 void launch_variant(int variant, const bf16_t* A, const WeightSegs& W, int M, int N, int K,
                     int splits, float* part, bf16_t* out, hipStream_t stream) {
   switch (variant) {
-    case 0:
-      if constexpr (MODE == 1) {
-        if (K % (2 * KB) == 0) {
-          launch_mfma<MODE, TileLP>(A, W, M, N, K, splits, part, out, stream);
-          break;
-        }
-      }
-      launch_mfma<MODE, TileL>(A, W, M, N, K, splits, part, out, stream);
-      break;
-    case 1: launch_mfma<MODE, TileM>(A, W, M, N, K, splits, part, out, stream); break;
-    default: launch_mfma<MODE, TileS>(A, W, M, N, K, splits, part, out, stream); break;
+    case 0: launch_tile<MODE, TileLP, TileL>(A, W, M, N, K, splits, part, out, stream); break;
+    case 1: launch_tile<MODE, TileMP, TileM>(A, W, M, N, K, splits, part, out, stream); break;
+    default: launch_tile<MODE, TileSP, TileS>(A, W, M, N, K, splits, part, out, stream); break;
   }
 }
 
