@@ -111,23 +111,49 @@ def cpu_baseline(w: wl.Workload, T: np.ndarray, min_seconds: float = 10.0, max_r
         oracle.stack_repair(w, [(wnp, K, V)], f, rows, X)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    threads = max(blas, oracle.layer.row_threads())
     what = "all" if len(rows) == len(T) else f"the first {len(rows)} of"
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
     return {"value": round(len(rows) / dt, 3), "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "nproc": os.cpu_count(), "usable_cpus": usable,
+            "cpu_model": cpu_model(),
             "sample": f"{len(times)} one-layer repairs of {w.name} over {what} B={len(T)} rows, "
-                      f"float64 numpy oracle, median {dt:.2f} s, {sum(times):.1f} s total"}
+                      f"float64 numpy oracle ({blas} BLAS threads, attention rows over "
+                      f"{oracle.layer.row_threads()} threads), median {dt:.2f} s, "
+                      f"{sum(times):.1f} s total"}
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def first_selectable(w: wl.Workload) -> int:
+    """First retained-suffix position (only those are selectable): the end of
+    B_1, or 0 for a single-block workload."""
+    s, e = wl.blocks(w)
+    return int(e[0]) if len(s) > 1 else 0
 
 
 class Setup:
-    """Device inputs of one workload (weights and caches of every layer)."""
+    """Device inputs of one workload (weights and caches of every layer), its
+    support and that support's runs, all taken from the library."""
 
     def __init__(self, w: wl.Workload, dws=None):
         import torch
-        import oracle
         import packed_partial_prefill_amd as kvr
-        from tests.gpu_harness import cfg_of, dev_cache, dev_weights, workspace
+        from workloads.device import cfg_of, dev_cache, dev_weights, workspace
         self.w, self.kvr, self.torch = w, kvr, torch
+        self.workspace = workspace
         self.L = w.n_layers
         s, e = wl.blocks(w)
         self.ds, self.de = torch.from_numpy(s).cuda(), torch.from_numpy(e).cuda()
@@ -137,18 +163,22 @@ class Setup:
         self.counts = torch.empty(4, dtype=torch.int32, device="cuda")
         self.flags = torch.from_numpy(wl.initial_flags(w)).cuda()
         self.seams = w.support == "seams"
+        self.first = first_selectable(w)
         if self.seams:
-            n, _, _ = kvr.kvr_build_repair_set(self.ds, self.de, w.n_tokens, w.tau,
+            n, R, _ = kvr.kvr_build_repair_set(self.ds, self.de, w.n_tokens, w.tau,
                                                kvr.KVR_SEAM_ASYMMETRIC, self.dT_all, self.rs,
                                                self.rl, self.counts)
             self.dT = self.dT_all[:n]
         else:
             self.dT = torch.from_numpy(wl.explicit_support(w)).cuda()
+            n, R, _ = kvr.kvr_build_runs(self.dT, w.n_tokens, self.first, self.rs, self.rl,
+                                         self.counts)
         self.T = self.dT.cpu().numpy()
         self.B = len(self.T)
-        starts, lens = oracle.runs(self.T)   # host copy of the runs, for the interval schedule
-        self.runs = [(int(a), int(b)) for a, b in zip(starts, lens)]
-        self.R = len(self.runs)
+        # the support's maximal runs, as the library coalesced them
+        self.runs = [(int(a), int(b)) for a, b in zip(self.rs[:R].cpu().tolist(),
+                                                       self.rl[:R].cpu().tolist())]
+        self.R = R
         if dws is None:
             dws = []
             for li in range(self.L):
@@ -183,11 +213,35 @@ class Setup:
                                  ws, stream=self.stream)
 
     def step_packed(self):
+        """One pass of the hot path: the support and its runs (seam set from
+        the block boundaries, or an explicit support checked and coalesced),
+        then the repair."""
+        kvr = self.kvr
         if self.seams:
-            self.kvr.kvr_build_repair_set(self.ds, self.de, self.w.n_tokens, self.w.tau,
-                                          self.kvr.KVR_SEAM_ASYMMETRIC, self.dT_all, self.rs,
-                                          self.rl, self.counts, sync=False, stream=self.stream)
+            kvr.kvr_build_repair_set(self.ds, self.de, self.w.n_tokens, self.w.tau,
+                                     kvr.KVR_SEAM_ASYMMETRIC, self.dT_all, self.rs, self.rl,
+                                     self.counts, sync=False, stream=self.stream)
+        else:
+            kvr.kvr_build_runs(self.dT, self.w.n_tokens, self.first, self.rs, self.rl,
+                               self.counts, sync=False, stream=self.stream)
         self.repair(self.dT, self.x_out, self.ws)
+
+    def explicit_step(self, T: np.ndarray):
+        """A packed step over another explicit support of the same layer (its
+        own output and workspace), for equal-budget comparisons."""
+        torch, kvr = self.torch, self.kvr
+        dT = torch.from_numpy(np.asarray(T, np.int32)).cuda()
+        rs, rl = torch.empty_like(dT), torch.empty_like(dT)
+        counts = torch.empty(4, dtype=torch.int32, device="cuda")
+        out = torch.empty((len(T), self.w.hidden), dtype=torch.float32, device="cuda")
+        ws = self.workspace(self.cfg, len(T), self.w.n_tokens)
+        n, R, _ = kvr.kvr_build_runs(dT, self.w.n_tokens, self.first, rs, rl, counts)
+
+        def step():
+            kvr.kvr_build_runs(dT, self.w.n_tokens, self.first, rs, rl, counts, sync=False,
+                               stream=self.stream)
+            self.repair(dT, out, ws)
+        return step, R
 
     def step_interval(self):
         """Sequential maximal-interval replay (Budgeted KV-Cache Repair,
@@ -206,6 +260,48 @@ class Setup:
         torch.cuda.synchronize()
         return (time.perf_counter() - t0) * 1e3 / steps
 
+
+
+def flushed_trials(st: "Setup", w: wl.Workload, torch, warmup: int = 10, rounds: int = 20,
+                   flush_mib: int = 512) -> dict:
+    """Median ms per step with the Infinity Cache flushed before every trial
+    (a 512 MiB read), for the workload's support and, on the 7B 16K seam
+    layer, its two equal-budget contiguous companions on the same layer
+    weights and cache (suffix start and matched work), trials of the
+    variants in a random order each round (Budgeted KV-Cache Repair,
+    section 13.3 protocol: ten warmups, twenty interleaved trials, medians)."""
+    import random
+    variants = {"packed": (st.step_packed, st.R)}
+    if w.name == wl.QWEN7_LAYER_SEAMS.name:
+        for comp in (wl.QWEN7_LAYER_CONTIG, wl.QWEN7_LAYER_MATCHED):
+            fn, R = st.explicit_step(wl.explicit_support(comp))
+            variants[comp.support] = (fn, R)
+    scratch = torch.ones((flush_mib << 20) // 4, dtype=torch.int32, device="cuda")
+    for fn, _ in variants.values():
+        for _ in range(warmup):
+            fn()
+    torch.cuda.synchronize()
+    rng = random.Random(1234)
+    times = {k: [] for k in variants}
+    names = list(variants)
+    for _ in range(rounds):
+        rng.shuffle(names)
+        for k in names:
+            scratch.max()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            variants[k][0]()
+            e1.record()
+            e1.synchronize()
+            times[k].append(e0.elapsed_time(e1))
+    del scratch
+    out = {k: {"ms_median": round(float(np.median(v)), 4), "ms_min": round(float(np.min(v)), 4),
+               "R": variants[k][1],
+               "tokens_per_s": round(st.B / (float(np.median(v)) * 1e-3), 1)}
+           for k, v in times.items()}
+    out["protocol"] = (f"{warmup} warmups each, {rounds} rounds of randomly ordered trials, "
+                       f"{flush_mib} MiB read before every trial, HIP events, medians")
+    return out
 
 def run_table18(a) -> int:
     """Packed vs interval-wise refresh at the Table 18 geometry (Qwen3-8B
@@ -260,7 +356,7 @@ def run_inference_bench(a) -> int:
     Infinity Cache is flushed before every trial."""
     import torch
     import packed_partial_prefill_amd as kvr
-    from tests.gpu_harness import cfg_of, dev_cache
+    from workloads.device import cfg_of, dev_cache
     for w in (wl.QWEN7_DECODE_16K, wl.QWEN7_DECODE_32K):
         K0, V0 = wl.kv_cache(w, 0)
         kc, vc = dev_cache(w, K0, V0)
@@ -300,7 +396,7 @@ def run_shift_bench(a) -> int:
     suffix keys, move values and metadata.  Pure HBM stream."""
     import torch
     import packed_partial_prefill_amd as kvr
-    from tests.gpu_harness import cfg_of, dev_cache
+    from workloads.device import cfg_of, dev_cache
     w = wl.QWEN7_SHIFT
     cfg = cfg_of(w)
     a0, d = w.support_start, w.support_len
@@ -449,17 +545,45 @@ def main(argv=None) -> int:
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
                 "traffic": None if traffic is None else round(traffic),
                 "us_per_launch": round(t_dom * 1e6, 2)}
-    t_attn = (per_kernel.get("attn", 0.0) + per_kernel.get("attn_merge", 0.0)) * 1e-6
+
+    # attention and the projections, each timed live in its own pass of K
+    # steps with only its launches bracketed (HIP events on the launch stream)
+    def bracketed(names):
+        ids = [kvr.KERNEL_NAMES.index(n) for n in names]
+        kvr.kvr_timing_begin(sum(1 << i for i in ids))
+        for _ in range(a.steps):
+            step()
+        torch.cuda.synchronize()
+        ms, nl = kvr.kvr_timing_end()
+        return {n: ms[i] * 1e3 / (a.steps * L) for n, i in zip(names, ids) if nl[i]}  # us/layer
+
     attn = None
-    if t_attn > 0 and a.schedule == "packed":
+    t_attn = 0.0
+    if a.schedule == "packed":
+        at = bracketed(["attn", "attn_merge"])
+        t_attn = sum(at.values()) * 1e-6
         gbs = (fc["attn_kv_bytes"] + fc["attn_q_o_bytes"]) / t_attn / 1e9
         tf = fc["attn"] / t_attn / 1e12
-        attn = {"hbm_gbps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        attn = {"us_per_layer": round(t_attn * 1e6, 2),
+                "launches_us": {n: round(v, 2) for n, v in at.items()},
+                "hbm_gbps": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
                 "tflops": round(tf, 2), "mfma_frac": round(tf / peak, 4),
-                "pairs_per_head": fc["pairs"]}
-    gemm_t = sum(per_kernel.get(n, 0.0) for n in ("qkv", "oproj", "gateup", "down")) * 1e-6
+                "pairs_per_head": fc["pairs"], "timing": "live HIP events, attention only"}
+    gm = bracketed(["qkv", "oproj", "gateup", "down"])
+    gemm_t = sum(gm.values()) * 1e-6
     gemm_tf = (fc["qkv"] + fc["oproj"] + fc["gateup"] + fc["down"]) / gemm_t / 1e12 if gemm_t else 0
+    gemm = {"us_per_layer": round(gemm_t * 1e6, 1),
+            "launches_us": {n: round(v, 2) for n, v in gm.items()},
+            "tflops": round(gemm_tf, 1), "mfma_frac": round(gemm_tf / peak, 4),
+            "timing": "live HIP events, projections only"}
 
+    # the pages' protocol with a cold Infinity Cache: ten warmups, then
+    # twenty rounds in which the seam step and its two equal-budget
+    # contiguous companions run in a random order, each trial after a
+    # 512 MiB read flush; medians
+    flushed = None
+    if a.schedule == "packed" and L == 1:
+        flushed = flushed_trials(st, w, torch)
     if a.copy_calib_mib:
         n = a.copy_calib_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device="cuda")
@@ -487,11 +611,11 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": cpu,
         "attn": attn,
+        "gemm": gemm,
         "gemm_mfma_frac": round(gemm_tf / peak, 4),
-        "kernel_us": per_kernel,
+        "flushed": flushed,
+        "kernel_us_instrumented": per_kernel,
         "stack_tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
-        "gemm_us_per_layer": round(gemm_t * 1e6, 1),
-        "attn_us_per_layer": round(t_attn * 1e6, 1),
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -25,9 +25,9 @@
  *   - Host-side validation runs first and returns an error without touching
  *     the device.  A failed HIP call returns KVR_ERR_HIP; the HIP error text
  *     is then in kvr_last_error().
- *   - The cache row index is the global position g_t (the mixed cache is
- *     indexed by global position); RoPE angles and causal visibility both
- *     use it.
+ *   - The cache row index t is the global position g_t unless kvr_meta
+ *     carries a position map (then g_t = gpos[t], strictly increasing);
+ *     RoPE angles and causal visibility both use it.
  */
 #ifndef KVR_H
 #define KVR_H
@@ -103,12 +103,22 @@ typedef struct {
   void *k, *v;
 } kvr_kv;
 
-/* Mixed-cache metadata shared by all layers (m_t has no layer index).
- * flags: device uint8 [n_tokens] (KVR_FLAG_* bits); block_id: device int32
- * [n_tokens] or NULL (only written by KVR_INIT_META). */
+/* Mixed-cache metadata m_t = (type, block id, global position) shared by all
+ * layers (cross-attention reuse page, 6.2; m_t has no layer index).
+ *   flags     device uint8 [n_tokens] (KVR_FLAG_* bits: the type, and
+ *             membership of the spurious-sink set).
+ *   block_id  device int32 [n_tokens] or NULL (only written by KVR_INIT_META).
+ *   gpos      device int32 [n_tokens] or NULL: the global position g_t of
+ *             cache row t, which RoPE and the causal rule of F use (6.2).
+ *             NULL means g_t = t.  A non-NULL map must be non-negative and
+ *             strictly increasing (kvr_check_support verifies it); causal
+ *             visibility g_j <= g_u is then visibility by row, j <= u, and
+ *             the repair rotates row r's query and key at g_{T[r]}.
+ *   n_tokens  N, the number of cache rows. */
 typedef struct {
   uint8_t* flags;
   int32_t* block_id;
+  const int32_t* gpos;
   int32_t n_tokens;
 } kvr_meta;
 
@@ -153,12 +163,43 @@ kvr_status kvr_build_repair_set(const int32_t* d_s, const int32_t* d_e, int32_t 
 /*
  * kvr_check_support - checks an explicit support before execution, as the
  * budgeted-repair page requires (section 13.2 / 7.1): d_T (device int32 [B])
- * strictly increasing and inside [first_selectable, n_tokens).  d_result is
- * a device int32 scratch word.  Synchronises the stream.  Returns KVR_OK or
- * KVR_ERR_BAD_SUPPORT.  B = 0 is valid.
+ * strictly increasing (hence unique) and inside [first_selectable,
+ * n_tokens), the retained suffix being the only selectable part.  d_gpos
+ * (device int32 [n_tokens], or NULL for the identity g_t = t) is the global
+ * position map of kvr_meta (cross-attention reuse page, 6.2); when given it
+ * is checked in the same pass to be non-negative and strictly increasing.
+ * d_result is a device int32 scratch word.  Synchronises the stream.
+ * Returns KVR_OK, KVR_ERR_BAD_SUPPORT (support), or KVR_ERR_INVALID_ARGUMENT
+ * (position map; also for B > n_tokens or NULL / misaligned pointers).
+ * B = 0 is valid.
  */
 kvr_status kvr_check_support(const int32_t* d_T, int32_t B, int32_t n_tokens,
-                             int32_t first_selectable, int32_t* d_result, hipStream_t stream);
+                             int32_t first_selectable, const int32_t* d_gpos,
+                             int32_t* d_result, hipStream_t stream);
+
+/*
+ * kvr_build_runs - checks an explicit support like kvr_check_support and
+ * coalesces it into its maximal runs of consecutive positions, the execution
+ * intervals that Budgeted KV-Cache Repair sorts and coalesces a support into
+ * (section 3.2, Algorithm 1's last step) and that sequential maximal-interval
+ * replay (section 7.1) traverses one at a time.  Seam sets get their runs
+ * from kvr_build_repair_set; this call covers every other support (isolated
+ * tokens, intervals, supports chosen by Semantic-Unit Refresh elsewhere).
+ *
+ *   d_T        device int32 [B], the support (not modified).
+ *   out        out->run_start and out->run_len: device int32 [out->cap]
+ *              each, out->cap >= B; out->counts: device int32 [3] receives
+ *              (B, R, status) with status KVR_OK or KVR_ERR_BAD_SUPPORT (then
+ *              the runs are undefined).  out->T is not used (may be NULL).
+ *   h_counts   host int32 [3] or NULL.  When given, counts are copied back,
+ *              the stream is synchronised and the device status is returned.
+ *              When NULL the call does not synchronise.
+ * Errors (before any device work): B < 0 or B > n_tokens, NULL or
+ * misaligned pointers, cap < B -> INVALID_ARGUMENT.  B = 0 gives R = 0.
+ */
+kvr_status kvr_build_runs(const int32_t* d_T, int32_t B, int32_t n_tokens,
+                          int32_t first_selectable, const kvr_repair_set* out,
+                          int32_t* h_counts, hipStream_t stream);
 
 /*
  * kvr_build_plan - reusable attention plan (Budgeted KV-Cache Repair,
@@ -183,7 +224,8 @@ size_t kvr_workspace_bytes(const kvr_config* cfg, int32_t B, int32_t n_tokens);
  * physical-repair mode (cross-attention reuse page, 6.4):
  *
  *   n = RMSNorm(x) * attn_norm; q, k, v = n Wq^T (+bq), n Wk^T (+bk),
- *   n Wv^T (+bv); RoPE on q, k at each row's position u_r = T[r];
+ *   n Wv^T (+bv); RoPE on q, k at each row's global position
+ *   g_{u_r} (meta->gpos[T[r]], or u_r = T[r] itself when gpos is NULL);
  *   before attention: cache.k[u_r] = k, cache.v[u_r] = v (rounded to
  *   cfg.dtype), flags[u_r] &= ~(LOCAL | SINK)  (Eq. 21; type <- global);
  *   o = softmax_j(<q, k_j>/sqrt(d) + alpha*local_j + beta*sink_j) v_j over

@@ -95,7 +95,7 @@ def check_support(T: Sequence[int], n_tokens: int, first_selectable: int, B: int
     if len(T) != B:
         raise BadSupport(f"support has {len(T)} positions, expected {B}")
     for k, t in enumerate(T):
-        if not first_selectable <= t < n_tokens:
+        if not max(first_selectable, 0) <= t < n_tokens:     # a position is a cache row
             raise BadSupport(f"position {t} outside [{first_selectable}, {n_tokens})")
         if k and T[k - 1] >= t:
             raise BadSupport("support is not strictly increasing")
@@ -125,3 +125,38 @@ def attn_tile_plan(T: Sequence[int], group: int, rows_per_tile: int,
         n_full[t] = (u_min + 1) // kv_tile
         n_total[t] = -(-(u_max + 1) // kv_tile)
     return n_full, n_total
+
+
+def initial_meta(s: Sequence[int], e: Sequence[int], n_tokens: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Load-time metadata of the mixed cache (cross-attention reuse page,
+    6.2, and the sink term of F in 6.4): the first block B_1 was encoded as
+    a true prefix, so its positions are global; every position of a later
+    block was encoded locally, so its type is local; the spurious-sink set
+    S' is the first position s_i of every block after the first (each such
+    block began its own local encoding there).  Returns (flags uint8 [N],
+    block id int32 [N]) with flags bit 0 = local, bit 1 = spurious sink and
+    block ids counted from 0."""
+    validate_blocks(s, e, n_tokens)
+    flags = np.zeros(n_tokens, dtype=np.uint8)
+    block = np.zeros(n_tokens, dtype=np.int32)
+    for i in range(len(s)):
+        for t in range(int(s[i]), int(e[i])):
+            block[t] = i
+            if i >= 1:
+                flags[t] |= 1            # local: not part of the true prefix
+        if i >= 1:
+            flags[int(s[i])] |= 2        # spurious sink: head of a local block
+    return flags, block
+
+
+def check_positions(gpos: Sequence[int], n_tokens: int) -> None:
+    """A global-position map g_t (cross-attention reuse page, 6.2) is usable
+    when it has one entry per cache row, is non-negative and strictly
+    increasing: causal visibility by position (g_j <= g_u) is then a prefix
+    of the rows."""
+    g = list(map(int, gpos))
+    if len(g) != n_tokens:
+        raise ValueError(f"position map has {len(g)} entries, expected {n_tokens}")
+    for t, x in enumerate(g):
+        if x < 0 or (t and g[t - 1] >= x):
+            raise ValueError("position map is not non-negative and strictly increasing")

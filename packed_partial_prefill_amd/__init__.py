@@ -60,7 +60,8 @@ class kvr_kv(C.Structure):
 
 
 class kvr_meta(C.Structure):
-    _fields_ = [("flags", C.c_void_p), ("block_id", C.c_void_p), ("n_tokens", C.c_int32)]
+    _fields_ = [("flags", C.c_void_p), ("block_id", C.c_void_p), ("gpos", C.c_void_p),
+                ("n_tokens", C.c_int32)]
 
 
 class kvr_repair_set(C.Structure):
@@ -73,7 +74,8 @@ _I = C.c_int32
 _sigs = {
     "kvr_build_repair_set": (C.c_int, [_P, _P, _I, _I, _I, C.c_uint32, C.POINTER(kvr_meta),
                                        C.POINTER(kvr_repair_set), _P, _P]),
-    "kvr_check_support": (C.c_int, [_P, _I, _I, _I, _P, _P]),
+    "kvr_check_support": (C.c_int, [_P, _I, _I, _I, _P, _P, _P]),
+    "kvr_build_runs": (C.c_int, [_P, _I, _I, _I, C.POINTER(kvr_repair_set), _P, _P]),
     "kvr_build_plan": (C.c_int, [_P, _I, _I, _P, _P, _P]),
     "kvr_workspace_bytes": (C.c_size_t, [C.POINTER(kvr_config), _I, _I]),
     "kvr_layer_repair": (C.c_int, [C.POINTER(kvr_config), C.POINTER(kvr_layer_weights), kvr_kv,
@@ -147,8 +149,8 @@ def _weights_c(w: dict) -> kvr_layer_weights:
     return kvr_layer_weights(*[_ptr(w.get(n)) for n in names])
 
 
-def _meta_c(flags, n_tokens: int, block_id=None) -> kvr_meta:
-    return kvr_meta(_ptr(flags), _ptr(block_id), n_tokens)
+def _meta_c(flags, n_tokens: int, block_id=None, gpos=None) -> kvr_meta:
+    return kvr_meta(_ptr(flags), _ptr(block_id), _ptr(gpos), n_tokens)
 
 
 # ----------------------------------------------------------------- API
@@ -168,9 +170,26 @@ def kvr_build_repair_set(d_s, d_e, n_tokens: int, tau: int, mode: int, T, run_st
     return (h[0], h[1], h[2]) if h is not None else None
 
 
-def kvr_check_support(d_T, n_tokens: int, first_selectable: int, d_result, stream=None) -> None:
+def kvr_check_support(d_T, n_tokens: int, first_selectable: int, d_result, gpos=None,
+                      stream=None) -> None:
+    """Support strictly increasing inside [first_selectable, n_tokens) and,
+    when given, the global position map non-negative and strictly increasing.
+    Synchronises."""
     _check(_lib.kvr_check_support(_ptr(d_T), d_T.numel(), n_tokens, first_selectable,
-                                  _ptr(d_result), _stream(stream)))
+                                  _ptr(gpos), _ptr(d_result), _stream(stream)))
+
+
+def kvr_build_runs(d_T, n_tokens: int, first_selectable: int, run_start, run_len, counts,
+                   sync: bool = True, stream=None) -> Optional[Tuple[int, int, int]]:
+    """Checks an explicit support and coalesces it into maximal runs.
+    Returns (B, R, status) when ``sync``; otherwise None."""
+    out = kvr_repair_set(None, _ptr(run_start), _ptr(run_len), _ptr(counts),
+                         min(run_start.numel(), run_len.numel()))
+    h = (C.c_int32 * 3)() if sync else None
+    _check(_lib.kvr_build_runs(_ptr(d_T), d_T.numel(), n_tokens, first_selectable, C.byref(out),
+                               C.cast(h, C.c_void_p) if h is not None else None,
+                               _stream(stream)))
+    return (h[0], h[1], h[2]) if h is not None else None
 
 
 def kvr_build_plan(d_T, group: int, d_n_full, d_n_total, stream=None) -> None:
@@ -187,10 +206,10 @@ def kvr_workspace_bytes(cfg: Config, B: int, n_tokens: int) -> int:
 
 
 def kvr_layer_repair(cfg: Config, weights: dict, k_cache, v_cache, flags, d_T, x_in, x_out, ws,
-                     stream=None) -> None:
+                     gpos=None, stream=None) -> None:
     c = cfg.c()
     w = _weights_c(weights)
-    meta = _meta_c(flags, k_cache.shape[0])
+    meta = _meta_c(flags, k_cache.shape[0], gpos=gpos)
     _check(_lib.kvr_layer_repair(C.byref(c), C.byref(w), kvr_kv(_ptr(k_cache), _ptr(v_cache)),
                                  C.byref(meta), _ptr(d_T), d_T.numel(), _ptr(x_in),
                                  x_in.shape[0], _ptr(x_out), _ptr(ws), ws.numel() * ws.element_size(),
@@ -198,14 +217,14 @@ def kvr_layer_repair(cfg: Config, weights: dict, k_cache, v_cache, flags, d_T, x
 
 
 def kvr_stack_repair(cfg: Config, weights: Sequence[dict], caches: Sequence[Tuple], flags, d_T,
-                     x_in, x_out, ws, stream=None) -> None:
+                     x_in, x_out, ws, gpos=None, stream=None) -> None:
     c = cfg.c()
     L = len(weights)
     if len(caches) != L:
         raise ValueError("one (k, v) cache per layer")
     ws_arr = (kvr_layer_weights * L)(*[_weights_c(w) for w in weights])
     kv_arr = (kvr_kv * L)(*[kvr_kv(_ptr(k), _ptr(v)) for k, v in caches])
-    meta = _meta_c(flags, caches[0][0].shape[0])
+    meta = _meta_c(flags, caches[0][0].shape[0], gpos=gpos)
     _check(_lib.kvr_stack_repair(C.byref(c), L, ws_arr, kv_arr, C.byref(meta), _ptr(d_T),
                                  d_T.numel(), _ptr(x_in), x_in.shape[0], _ptr(x_out), _ptr(ws),
                                  ws.numel() * ws.element_size(), _stream(stream)))

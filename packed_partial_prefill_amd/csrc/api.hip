@@ -202,6 +202,8 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
   if (B == 0) return KVR_OK;
   if (!dev_ok(d_T) || !dev_ok(x_in) || !dev_ok(x_out) || !dev_ok(ws) || !dev_ok(meta->flags))
     return fail(KVR_ERR_INVALID_ARGUMENT, "T, x_in, x_out, ws and flags must be non-NULL and 16-byte aligned");
+  if (meta->gpos && !aligned16(meta->gpos))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "meta->gpos not 16-byte aligned");
   const bool gather = (x_in_rows == N) && !(B == N);
   if (gather && x_in == x_out)
     return fail(KVR_ERR_INVALID_ARGUMENT, "x_out may alias x_in only when x_in_rows == B");
@@ -230,8 +232,8 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
 
   // once per call: plan (Eq. 23-24) and RoPE table for the fixed positions
   KVR_RUN(KVR_KERNEL_PLAN, stream, "plan and rope table",
-          kvr::launch_layer_tables(d_T, B, sh.group, n_full, n_total, sh.d, cfg->rope_theta, tab,
-                                   stream));
+          kvr::launch_layer_tables(d_T, meta->gpos, B, sh.group, n_full, n_total, sh.d,
+                                   cfg->rope_theta, tab, stream));
   // gather the selected rows once; RMSNorm for layer 0
   KVR_RUN(KVR_KERNEL_NORM, stream, "gather+norm",
           kvr::launch_gather_norm(dt, x_in, gather ? d_T : nullptr, x_out,
@@ -282,6 +284,67 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
   return KVR_OK;
 }
 
+
+// Argument checks shared by both inference-mode entry points.
+kvr_status check_attention_args(const kvr_config* cfg, const kvr_kv& cache, const uint8_t* flags,
+                                int n_tokens, const float* q, const int32_t* d_pos, int B,
+                                const float* o, kvr::Shape* sh) {
+  kvr_status st = check_heads(cfg, sh);
+  if (st != KVR_OK) return st;
+  if (!std::isfinite(cfg->alpha) || !std::isfinite(cfg->beta))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "alpha and beta must be finite");
+  if (n_tokens <= 0) return fail(KVR_ERR_INVALID_ARGUMENT, "n_tokens must be positive");
+  if (B < 0 || B > n_tokens)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d outside [0, n_tokens=%d]", B, n_tokens);
+  if (B == 0) return KVR_OK;
+  if (!dev_ok(q) || !dev_ok(d_pos) || !dev_ok(o) || !dev_ok(flags) || !dev_ok(cache.k) ||
+      !dev_ok(cache.v))
+    return fail(KVR_ERR_INVALID_ARGUMENT,
+                "q, d_pos, o, flags and cache pointers must be non-NULL and 16-byte aligned");
+  if (static_cast<const void*>(o) == static_cast<const void*>(q))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "o must not alias q");
+  return KVR_OK;
+}
+
+// The launches of inference-mode attention over a workspace at `base`
+// (256-byte aligned, at least L.total bytes).
+kvr_status run_biased_attention(const kvr_config* cfg, const kvr::Shape& sh, const AttnLayout& L,
+                                const kvr_kv& cache, const uint8_t* flags, int n_tokens,
+                                const float* q, const int32_t* d_pos, int B, float* o,
+                                uint8_t* base, hipStream_t stream) {
+  const kvr_dtype dt = cfg->dtype;
+  if (kvr::decode_supported(dt, B, sh)) {
+    // decode sizes: one streaming pass over the cache plus a chunk merge
+    KVR_RUN(KVR_KERNEL_ATTN, stream, "decode attention",
+            kvr::launch_attention_decode(q, d_pos, B, n_tokens, cache.k, cache.v, flags, sh,
+                                         cfg->alpha, cfg->beta, base + L.attn, o, stream));
+    KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "decode merge",
+            kvr::launch_attention_decode_merge(d_pos, B, n_tokens, sh, base + L.attn, o, stream));
+    return KVR_OK;
+  }
+  int32_t* n_full = reinterpret_cast<int32_t*>(base + L.n_full);
+  int32_t* n_total = reinterpret_cast<int32_t*>(base + L.n_total);
+  void* attn_ws = base + L.attn;
+  // float32 storage attends on the caller's queries directly (the row kernel
+  // applies 1/sqrt(d) itself); bf16 takes them scaled and rounded once
+  const void* qk = q;
+  if (dt == KVR_BF16) {
+    qk = base + L.q;
+    KVR_RUN(KVR_KERNEL_QPREP, stream, "query prep",
+            kvr::launch_prep_queries(dt, q, static_cast<size_t>(B) * sh.hq * sh.d,
+                                     kvr::attention_q_scale(dt, sh.d), base + L.q, stream));
+  }
+  KVR_RUN(KVR_KERNEL_PLAN, stream, "plan",
+          kvr::launch_build_plan(d_pos, B, sh.group, n_full, n_total, stream));
+  KVR_RUN(KVR_KERNEL_ATTN, stream, "attention",
+          kvr::launch_attention(dt, qk, cache.k, cache.v, flags, d_pos, B, n_tokens, sh,
+                                cfg->alpha, cfg->beta, n_full, n_total, attn_ws, o, stream));
+  if (kvr::attention_needs_merge(dt))
+    KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "attention merge",
+            kvr::launch_attention_merge(dt, B, n_tokens, sh, n_total, attn_ws, o, true, stream));
+  return KVR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -328,20 +391,49 @@ kvr_status kvr_build_repair_set(const int32_t* d_s, const int32_t* d_e, int32_t 
 }
 
 kvr_status kvr_check_support(const int32_t* d_T, int32_t B, int32_t n_tokens,
-                             int32_t first_selectable, int32_t* d_result, hipStream_t stream) {
+                             int32_t first_selectable, const int32_t* d_gpos,
+                             int32_t* d_result, hipStream_t stream) {
   g_err[0] = '\0';
   if (B < 0 || n_tokens < 0 || B > n_tokens)
     return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d, n_tokens=%d", B, n_tokens);
-  if (!dev_ok(d_result) || (B > 0 && !dev_ok(d_T)))
-    return fail(KVR_ERR_INVALID_ARGUMENT, "d_T / d_result NULL or misaligned");
-  hipError_t e = kvr::launch_check_support(d_T, B, n_tokens, first_selectable, d_result, stream);
+  if (!dev_ok(d_result) || (B > 0 && !dev_ok(d_T)) || (d_gpos && !aligned16(d_gpos)))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "d_T / d_gpos / d_result NULL or misaligned");
+  hipError_t e = kvr::launch_check_support(d_T, B, n_tokens, first_selectable, d_gpos, d_result,
+                                           stream);
   if (e != hipSuccess) return hip_fail(e, "check support");
   int32_t h = 0;
   e = hipMemcpyAsync(&h, d_result, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
   if (e != hipSuccess) return hip_fail(e, "copy result");
   e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_fail(e, "synchronize");
+  if (h == KVR_ERR_BAD_SUPPORT)
+    return fail(KVR_ERR_BAD_SUPPORT, "support not strictly increasing or outside [%d, %d)",
+                first_selectable, n_tokens);
   if (h != KVR_OK)
+    return fail(KVR_ERR_INVALID_ARGUMENT,
+                "global position map not non-negative and strictly increasing");
+  return KVR_OK;
+}
+
+kvr_status kvr_build_runs(const int32_t* d_T, int32_t B, int32_t n_tokens,
+                          int32_t first_selectable, const kvr_repair_set* out,
+                          int32_t* h_counts, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (B < 0 || n_tokens < 0 || B > n_tokens)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d, n_tokens=%d", B, n_tokens);
+  if (!out || !dev_ok(out->run_start) || !dev_ok(out->run_len) || !dev_ok(out->counts) ||
+      (B > 0 && !dev_ok(d_T)))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "d_T / run outputs NULL or misaligned");
+  if (out->cap < B) return fail(KVR_ERR_INVALID_ARGUMENT, "cap %d < B %d", out->cap, B);
+  hipError_t e = kvr::launch_build_runs(d_T, B, n_tokens, first_selectable, out->run_start,
+                                        out->run_len, out->counts, stream);
+  if (e != hipSuccess) return hip_fail(e, "build runs");
+  if (!h_counts) return KVR_OK;
+  e = hipMemcpyAsync(h_counts, out->counts, 3 * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy counts");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "synchronize");
+  if (h_counts[2] != KVR_OK)
     return fail(KVR_ERR_BAD_SUPPORT, "support not strictly increasing or outside [%d, %d)",
                 first_selectable, n_tokens);
   return KVR_OK;
@@ -391,57 +483,15 @@ kvr_status kvr_biased_attention(const kvr_config* cfg, kvr_kv cache, const uint8
                                 hipStream_t stream) {
   g_err[0] = '\0';
   kvr::Shape sh;
-  kvr_status st = check_heads(cfg, &sh);
-  if (st != KVR_OK) return st;
-  if (!std::isfinite(cfg->alpha) || !std::isfinite(cfg->beta))
-    return fail(KVR_ERR_INVALID_ARGUMENT, "alpha and beta must be finite");
-  if (n_tokens <= 0) return fail(KVR_ERR_INVALID_ARGUMENT, "n_tokens must be positive");
-  if (B < 0 || B > n_tokens)
-    return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d outside [0, n_tokens=%d]", B, n_tokens);
-  if (B == 0) return KVR_OK;
-  if (!dev_ok(q) || !dev_ok(d_pos) || !dev_ok(o) || !dev_ok(ws) || !dev_ok(flags) ||
-      !dev_ok(cache.k) || !dev_ok(cache.v))
-    return fail(KVR_ERR_INVALID_ARGUMENT,
-                "q, d_pos, o, ws, flags and cache pointers must be non-NULL and 16-byte aligned");
-  if (static_cast<const void*>(o) == static_cast<const void*>(q))
-    return fail(KVR_ERR_INVALID_ARGUMENT, "o must not alias q");
+  kvr_status st = check_attention_args(cfg, cache, flags, n_tokens, q, d_pos, B, o, &sh);
+  if (st != KVR_OK || B == 0) return st;
+  if (!dev_ok(ws)) return fail(KVR_ERR_INVALID_ARGUMENT, "ws must be non-NULL and 16-byte aligned");
   const AttnLayout L = attn_layout_for(cfg, sh, B, n_tokens);
   uint8_t* base = reinterpret_cast<uint8_t*>(up256(reinterpret_cast<uintptr_t>(ws)));
   const size_t slack = static_cast<size_t>(base - static_cast<uint8_t*>(ws));
   if (ws_bytes < L.total + slack)
     return fail(KVR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total + slack);
-
-  const kvr_dtype dt = cfg->dtype;
-  if (kvr::decode_supported(dt, B, sh)) {
-    // decode sizes: one streaming pass over the cache plus a chunk merge
-    KVR_RUN(KVR_KERNEL_ATTN, stream, "decode attention",
-            kvr::launch_attention_decode(q, d_pos, B, n_tokens, cache.k, cache.v, flags, sh,
-                                         cfg->alpha, cfg->beta, base + L.attn, o, stream));
-    KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "decode merge",
-            kvr::launch_attention_decode_merge(d_pos, B, n_tokens, sh, base + L.attn, o, stream));
-    return KVR_OK;
-  }
-  int32_t* n_full = reinterpret_cast<int32_t*>(base + L.n_full);
-  int32_t* n_total = reinterpret_cast<int32_t*>(base + L.n_total);
-  void* attn_ws = base + L.attn;
-  // float32 storage attends on the caller's queries directly (the row kernel
-  // applies 1/sqrt(d) itself); bf16 takes them scaled and rounded once
-  const void* qk = q;
-  if (dt == KVR_BF16) {
-    qk = base + L.q;
-    KVR_RUN(KVR_KERNEL_QPREP, stream, "query prep",
-            kvr::launch_prep_queries(dt, q, static_cast<size_t>(B) * sh.hq * sh.d,
-                                     kvr::attention_q_scale(dt, sh.d), base + L.q, stream));
-  }
-  KVR_RUN(KVR_KERNEL_PLAN, stream, "plan",
-          kvr::launch_build_plan(d_pos, B, sh.group, n_full, n_total, stream));
-  KVR_RUN(KVR_KERNEL_ATTN, stream, "attention",
-          kvr::launch_attention(dt, qk, cache.k, cache.v, flags, d_pos, B, n_tokens, sh,
-                                cfg->alpha, cfg->beta, n_full, n_total, attn_ws, o, stream));
-  if (kvr::attention_needs_merge(dt))
-    KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "attention merge",
-            kvr::launch_attention_merge(dt, B, n_tokens, sh, n_total, attn_ws, o, true, stream));
-  return KVR_OK;
+  return run_biased_attention(cfg, sh, L, cache, flags, n_tokens, q, d_pos, B, o, base, stream);
 }
 
 kvr_status kvr_shift_cache(const kvr_config* cfg, int32_t n_layers, const kvr_kv* src,

@@ -39,6 +39,49 @@ __device__ int block_exclusive_scan(int v, int* wsum, int* total) {
   return pre + x - v;
 }
 
+// Maximal runs of the sorted positions t_at(0..total-1): T[k] opens a run
+// unless T[k] == T[k-1] + 1 (the execution intervals of "Budgeted KV-Cache
+// Repair", section 3.2).  Writes run_start / run_len and returns R; every
+// thread of the 1024-thread workgroup gets R.  run_len first holds each run's
+// opening index in T, then its length; the openings are also kept in LDS
+// (sOpen) while R <= kBuildLds, else the lengths are fixed up chunk by chunk
+// from global memory between barriers.
+template <class TAt>
+__device__ int emit_runs(TAt t_at, int total, int32_t* __restrict__ run_start,
+                         int32_t* __restrict__ run_len, int* sOpen, int* wsum) {
+  const int tid = threadIdx.x;
+  int nruns = 0;
+  for (int base = 0; base < total; base += blockDim.x) {
+    const int k = base + tid;
+    const int open = (k < total) && (k == 0 || t_at(k) != t_at(k - 1) + 1);
+    int chunk;
+    const int id = nruns + block_exclusive_scan(open, wsum, &chunk);
+    if (open) {
+      run_start[id] = t_at(k);
+      if (id < kBuildLds) sOpen[id] = k;
+      run_len[id] = k;
+    }
+    nruns += chunk;
+  }
+  __threadfence_block();
+  __syncthreads();
+  if (nruns <= kBuildLds) {
+    for (int j = tid; j < nruns; j += blockDim.x)
+      run_len[j] = ((j + 1 < nruns) ? sOpen[j + 1] : total) - sOpen[j];
+  } else {
+    for (int base = 0; base < nruns; base += blockDim.x) {
+      const int j = base + tid;
+      int len = 0;
+      if (j < nruns) len = ((j + 1 < nruns) ? run_len[j + 1] : total) - run_len[j];
+      __syncthreads();
+      if (j < nruns) run_len[j] = len;
+      __threadfence_block();
+      __syncthreads();
+    }
+  }
+  return nruns;
+}
+
 // Positions of block i that belong to T_tau: at most two half-open ranges
 // [a0, a1) (leading window, merged with the trailing one when they touch)
 // and [b0, b1) (trailing window).
@@ -123,37 +166,8 @@ __global__ __launch_bounds__(kBuildThreads) void k_build_repair_set(
   __syncthreads();
   auto t_at = [&](int k) { return lds_t ? sT[k] : T[k]; };
 
-  // 4. maximal runs: T[k] opens a run unless T[k] == T[k-1] + 1.  run_len
-  //    first holds the opening index, then the length.
-  int nruns = 0;
-  for (int base = 0; base < total; base += blockDim.x) {
-    const int k = base + tid;
-    const int open = (k < total) && (k == 0 || t_at(k) != t_at(k - 1) + 1);
-    int chunk;
-    const int id = nruns + block_exclusive_scan(open, wsum, &chunk);
-    if (open) {
-      run_start[id] = t_at(k);
-      if (id < kBuildLds) sOpen[id] = k;
-      run_len[id] = k;
-    }
-    nruns += chunk;
-  }
-  __threadfence_block();
-  __syncthreads();
-  if (nruns <= kBuildLds) {
-    for (int j = tid; j < nruns; j += blockDim.x)
-      run_len[j] = ((j + 1 < nruns) ? sOpen[j + 1] : total) - sOpen[j];
-  } else {
-    for (int base = 0; base < nruns; base += blockDim.x) {
-      const int j = base + tid;
-      int len = 0;
-      if (j < nruns) len = ((j + 1 < nruns) ? run_len[j + 1] : total) - run_len[j];
-      __syncthreads();
-      if (j < nruns) run_len[j] = len;
-      __threadfence_block();
-      __syncthreads();
-    }
-  }
+  // 4. maximal runs
+  const int nruns = emit_runs(t_at, total, run_start, run_len, sOpen, wsum);
   if (tid == 0) { counts[0] = total; counts[1] = nruns; counts[2] = KVR_OK; }
 }
 
@@ -178,18 +192,57 @@ __global__ void k_init_meta(const int32_t* __restrict__ s, const int32_t* __rest
   if (block_id) block_id[t] = lo;
 }
 
-__global__ __launch_bounds__(kBuildThreads) void k_check_support(const int32_t* __restrict__ T,
-                                                                 int B, int n_tokens, int first,
-                                                                 int32_t* __restrict__ result) {
+// An explicit support (any sorted selection, e.g. isolated tokens or a
+// contiguous interval): check it as kvr_check_support does, then coalesce it
+// into its maximal runs.  counts = (B, R, status).
+__global__ __launch_bounds__(kBuildThreads) void k_build_runs(
+    const int32_t* __restrict__ T, int B, int n_tokens, int first,
+    int32_t* __restrict__ run_start, int32_t* __restrict__ run_len,
+    int32_t* __restrict__ counts) {
+  __shared__ int wsum[16];
   __shared__ int s_bad;
-  if (threadIdx.x == 0) s_bad = 0;
+  __shared__ int sOpen[kBuildLds];
+  const int tid = threadIdx.x;
+  if (tid == 0) s_bad = 0;
+  __syncthreads();
+  for (int k = tid; k < B; k += blockDim.x) {
+    const int t = T[k];
+    if (t < first || t < 0 || t >= n_tokens || (k > 0 && T[k - 1] >= t))
+      atomicOr(&s_bad, 1);
+  }
+  __syncthreads();
+  if (s_bad) {
+    if (tid == 0) { counts[0] = B; counts[1] = 0; counts[2] = KVR_ERR_BAD_SUPPORT; }
+    return;
+  }
+  const int nruns = emit_runs([&](int k) { return T[k]; }, B, run_start, run_len, sOpen, wsum);
+  if (tid == 0) { counts[0] = B; counts[1] = nruns; counts[2] = KVR_OK; }
+}
+
+// Support check (strictly increasing, inside [first, n_tokens)) and, when
+// gpos is given, the global-position map: non-negative and strictly
+// increasing over all n_tokens rows, so that causal visibility by global
+// position (g_j <= g_u) is visibility by row (j <= u).
+__global__ __launch_bounds__(kBuildThreads) void k_check_support(
+    const int32_t* __restrict__ T, int B, int n_tokens, int first,
+    const int32_t* __restrict__ gpos, int32_t* __restrict__ result) {
+  __shared__ int s_bad, s_bad_pos;
+  if (threadIdx.x == 0) { s_bad = 0; s_bad_pos = 0; }
   __syncthreads();
   for (int k = threadIdx.x; k < B; k += blockDim.x) {
     const int t = T[k];
-    if (t < first || t >= n_tokens || (k > 0 && T[k - 1] >= t)) atomicOr(&s_bad, 1);
+    if (t < first || t < 0 || t >= n_tokens || (k > 0 && T[k - 1] >= t))
+      atomicOr(&s_bad, 1);
+  }
+  if (gpos) {
+    for (int t = threadIdx.x; t < n_tokens; t += blockDim.x) {
+      const int g = gpos[t];
+      if (g < 0 || (t > 0 && gpos[t - 1] >= g)) atomicOr(&s_bad_pos, 1);
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) result[0] = s_bad ? KVR_ERR_BAD_SUPPORT : KVR_OK;
+  if (threadIdx.x == 0)
+    result[0] = s_bad ? KVR_ERR_BAD_SUPPORT : (s_bad_pos ? KVR_ERR_INVALID_ARGUMENT : KVR_OK);
 }
 
 // Attention plan entry t: first KV tile only partly visible to query tile t
@@ -206,12 +259,15 @@ __device__ __forceinline__ void plan_entry(const int32_t* __restrict__ T, int B,
 }
 
 // cos / sin of g * theta^(-2i/d) for packed row r and frequency i, built in
-// float64 and stored as a float32 pair of the table [B][d/2].
-__device__ __forceinline__ void rope_entry(const int32_t* __restrict__ T, int half, double theta,
-                                           int idx, float2* __restrict__ tab) {
+// float64 and stored as a float32 pair of the table [B][d/2].  g is the
+// row's global position: gpos[T[r]], or T[r] itself when there is no map.
+__device__ __forceinline__ void rope_entry(const int32_t* __restrict__ T,
+                                           const int32_t* __restrict__ gpos, int half,
+                                           double theta, int idx, float2* __restrict__ tab) {
   const int r = idx / half, i = idx - r * half;
   const double inv = pow(theta, -(2.0 * i) / (2.0 * half));
-  const double ang = static_cast<double>(T[r]) * inv;
+  const int g = gpos ? gpos[T[r]] : T[r];
+  const double ang = static_cast<double>(g) * inv;
   double sn, cs;
   sincos(ang, &sn, &cs);
   tab[idx] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
@@ -225,14 +281,15 @@ __global__ void k_build_plan(const int32_t* __restrict__ T, int B, int group, in
 
 // Both tables of a layer call in one launch: plan entries first, then the
 // rope table.
-__global__ void k_layer_tables(const int32_t* __restrict__ T, int B, int group, int n_tiles,
-                               int32_t* __restrict__ n_full, int32_t* __restrict__ n_total,
-                               int half, double theta, float2* __restrict__ tab) {
+__global__ void k_layer_tables(const int32_t* __restrict__ T, const int32_t* __restrict__ gpos,
+                               int B, int group, int n_tiles, int32_t* __restrict__ n_full,
+                               int32_t* __restrict__ n_total, int half, double theta,
+                               float2* __restrict__ tab) {
   const int idx = blockIdx.x * blockDim.x + threadIdx.x;
   if (idx < n_tiles)
     plan_entry(T, B, group, idx, n_full, n_total);
   else if (idx - n_tiles < B * half)
-    rope_entry(T, half, theta, idx - n_tiles, tab);
+    rope_entry(T, gpos, half, theta, idx - n_tiles, tab);
 }
 
 }  // namespace
@@ -256,9 +313,17 @@ hipError_t launch_init_meta(const int32_t* s, const int32_t* e, int m, int n_tok
 }
 
 hipError_t launch_check_support(const int32_t* T, int B, int n_tokens, int first,
-                                int32_t* result, hipStream_t stream) {
+                                const int32_t* gpos, int32_t* result, hipStream_t stream) {
   hipLaunchKernelGGL(k_check_support, dim3(1), dim3(kBuildThreads), 0, stream, T, B, n_tokens,
-                     first, result);
+                     first, gpos, result);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_runs(const int32_t* T, int B, int n_tokens, int first,
+                             int32_t* run_start, int32_t* run_len, int32_t* counts,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(k_build_runs, dim3(1), dim3(kBuildThreads), 0, stream, T, B, n_tokens,
+                     first, run_start, run_len, counts);
   return hipGetLastError();
 }
 
@@ -273,13 +338,13 @@ hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full
   return hipGetLastError();
 }
 
-hipError_t launch_layer_tables(const int32_t* T, int B, int group, int32_t* n_full,
-                              int32_t* n_total, int head_dim, double theta, float2* tab,
-                              hipStream_t stream) {
+hipError_t launch_layer_tables(const int32_t* T, const int32_t* gpos, int B, int group,
+                              int32_t* n_full, int32_t* n_total, int head_dim, double theta,
+                              float2* tab, hipStream_t stream) {
   const int n = plan_tiles(B, group) + B * (head_dim / 2);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_layer_tables, dim3((n + 255) / 256), dim3(256), 0, stream, T, B, group,
-                     plan_tiles(B, group), n_full, n_total, head_dim / 2, theta, tab);
+  hipLaunchKernelGGL(k_layer_tables, dim3((n + 255) / 256), dim3(256), 0, stream, T, gpos, B,
+                     group, plan_tiles(B, group), n_full, n_total, head_dim / 2, theta, tab);
   return hipGetLastError();
 }
 

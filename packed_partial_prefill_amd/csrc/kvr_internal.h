@@ -23,15 +23,20 @@ hipError_t launch_init_meta(const int32_t* s, const int32_t* e, int m, int n_tok
                             const int32_t* counts, uint8_t* flags, int32_t* block_id,
                             hipStream_t stream);
 hipError_t launch_check_support(const int32_t* T, int B, int n_tokens, int first,
-                                int32_t* result, hipStream_t stream);
+                                const int32_t* gpos, int32_t* result, hipStream_t stream);
+// Support check plus maximal runs of an explicit support; counts = (B, R, status).
+hipError_t launch_build_runs(const int32_t* T, int B, int n_tokens, int first,
+                             int32_t* run_start, int32_t* run_len, int32_t* counts,
+                             hipStream_t stream);
 int plan_tiles(int B, int group);
 hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full,
                              int32_t* n_total, hipStream_t stream);
-// launch_build_plan plus the RoPE table (cos, sin of T[r] * theta^(-2i/d) as
-// float32 pairs [B][d/2], computed in float64) in one launch
-hipError_t launch_layer_tables(const int32_t* T, int B, int group, int32_t* n_full,
-                              int32_t* n_total, int head_dim, double theta, float2* tab,
-                              hipStream_t stream);
+// launch_build_plan plus the RoPE table (cos, sin of g_r * theta^(-2i/d) as
+// float32 pairs [B][d/2], computed in float64, g_r = gpos[T[r]] or T[r] when
+// gpos is NULL) in one launch
+hipError_t launch_layer_tables(const int32_t* T, const int32_t* gpos, int B, int group,
+                              int32_t* n_full, int32_t* n_total, int head_dim, double theta,
+                              float2* tab, hipStream_t stream);
 
 // ---- norm.hip ---------------------------------------------------------------
 // x_res[r] = x_in[gather ? T[r] : r]; n_out[r] = RMSNorm(x_res[r]) * gamma.

@@ -16,53 +16,12 @@ import numpy as np
 import torch
 
 import workloads as wl
+from workloads.device import cfg_of, dev_cache, dev_weights, kvr, tdtype, workspace  # noqa: F401
 
 
 def log(msg: str) -> None:
     print(msg, flush=True)
     sys.stdout.flush()
-
-
-def kvr():
-    import packed_partial_prefill_amd as m
-    return m
-
-
-def tdtype(w: wl.Workload):
-    return torch.bfloat16 if w.dtype == "bf16" else torch.float32
-
-
-def cfg_of(w: wl.Workload, **over):
-    m = kvr()
-    c = m.Config(hidden=w.hidden, n_q_heads=w.n_q_heads, n_kv_heads=w.n_kv_heads,
-                 head_dim=w.head_dim, intermediate=w.intermediate, rms_eps=w.rms_eps,
-                 rope_theta=w.rope_theta, alpha=w.alpha, beta=w.beta,
-                 dtype=m.KVR_BF16 if w.dtype == "bf16" else m.KVR_F32)
-    for k, v in over.items():
-        setattr(c, k, v)
-    return c
-
-
-F32_KEYS = ("attn_norm", "mlp_norm", "bq", "bk", "bv")
-
-
-def dev_weights(w: wl.Workload, wnp: Dict[str, np.ndarray]) -> Dict[str, torch.Tensor]:
-    out = {}
-    for k, a in wnp.items():
-        t = torch.from_numpy(np.ascontiguousarray(a))
-        out[k] = (t if k in F32_KEYS else t.to(tdtype(w))).cuda()
-    return out
-
-
-def dev_cache(w: wl.Workload, K: np.ndarray, V: np.ndarray) -> Tuple[torch.Tensor, torch.Tensor]:
-    return (torch.from_numpy(K).to(tdtype(w)).cuda(), torch.from_numpy(V).to(tdtype(w)).cuda())
-
-
-def workspace(cfg, B: int, n_tokens: int) -> torch.Tensor:
-    n = kvr().kvr_workspace_bytes(cfg, B, n_tokens)
-    # all bytes 0xFF (float32 NaN): a kernel that reads workspace it has not
-    # written in the same call shows up as NaN, not as a stale value
-    return torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
 
 
 def build_seams_gpu(w: wl.Workload, tau: Optional[int] = None, asym: bool = True,

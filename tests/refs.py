@@ -32,12 +32,14 @@ def rope_complex(x: torch.Tensor, pos: torch.Tensor, theta: float) -> torch.Tens
     return torch.cat([z.real, z.imag], dim=-1)
 
 
-def full_prefill(cfg, layers: Sequence[Dict[str, np.ndarray]], X: np.ndarray):
+def full_prefill(cfg, layers: Sequence[Dict[str, np.ndarray]], X: np.ndarray, pos=None):
     """Dense causal decoder over all rows of X [N, hidden]; returns the final
-    hidden states and every layer's (K, V) [N, Hkv, d] (post-RoPE keys)."""
+    hidden states and every layer's (K, V) [N, Hkv, d] (post-RoPE keys).
+    ``pos`` (default 0..N-1) are the rows' positions for RoPE; the causal
+    mask is the row order (positions must increase with the row)."""
     N = X.shape[0]
     Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
-    pos = torch.arange(N)
+    pos = torch.arange(N) if pos is None else torch.as_tensor(np.asarray(pos, dtype=np.int64))
     x = _t(X)
     kvs = []
     for w in layers:
@@ -93,9 +95,11 @@ def py_rope(a: List[float], p: int, theta: float) -> List[float]:
     return out
 
 
-def py_layer(cfg, w, K, V, flags, T, X):
+def py_layer(cfg, w, K, V, flags, T, X, pos=None):
     """One packed layer with lists: K, V are lists [N][Hkv][d] (mutated),
-    flags a list of ints (mutated), X a list of packed rows."""
+    flags a list of ints (mutated), X a list of packed rows; ``pos`` maps a
+    row to its RoPE position (default: the row itself)."""
+    P = (lambda t: t) if pos is None else (lambda t: int(pos[t]))
     Hq, Hkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     G = Hq // Hkv
     tolist = lambda a: np.asarray(a, dtype=np.float64).tolist()
@@ -110,8 +114,8 @@ def py_layer(cfg, w, K, V, flags, T, X):
             q = [a + b for a, b in zip(q, tolist(w["bq"]))]
             k = [a + b for a, b in zip(k, tolist(w["bk"]))]
             v = [a + b for a, b in zip(v, tolist(w["bv"]))]
-        Q.append([py_rope(q[h * d:(h + 1) * d], t, cfg.rope_theta) for h in range(Hq)])
-        K[t] = [py_rope(k[g * d:(g + 1) * d], t, cfg.rope_theta) for g in range(Hkv)]
+        Q.append([py_rope(q[h * d:(h + 1) * d], P(t), cfg.rope_theta) for h in range(Hq)])
+        K[t] = [py_rope(k[g * d:(g + 1) * d], P(t), cfg.rope_theta) for g in range(Hkv)]
         V[t] = [v[g * d:(g + 1) * d] for g in range(Hkv)]
         flags[t] = 0
     out = []

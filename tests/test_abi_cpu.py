@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
               "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
               "kvr_attention_workspace_bytes", "kvr_biased_attention", "kvr_shift_cache",
-              "kvr_sur_scores", "kvr_sur_select",
+              "kvr_sur_scores", "kvr_sur_select", "kvr_build_runs",
               "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
         assert n in names
 
@@ -63,11 +63,11 @@ def _w(kvr, **over):
 
 
 def _layer(kvr, cfg=None, w=None, B=4, x_rows=4, n_tokens=512, ws_bytes=1 << 40, T=FAKE,
-           x_in=FAKE, x_out=FAKE + 4096, flags=FAKE):
+           x_in=FAKE, x_out=FAKE + 4096, flags=FAKE, gpos=None):
     lib = kvr.lib()
     cfg = cfg or _cfg(kvr)
     w = w or _w(kvr)
-    meta = kvr.kvr_meta(flags, None, n_tokens)
+    meta = kvr.kvr_meta(flags=flags, block_id=None, gpos=gpos, n_tokens=n_tokens)
     return lib.kvr_layer_repair(C.byref(cfg), C.byref(w), kvr.kvr_kv(FAKE, FAKE), C.byref(meta),
                                 T, B, x_in, x_rows, x_out, FAKE, ws_bytes, None)
 
@@ -91,6 +91,7 @@ def test_layer_repair_rejects_bad_arguments(kvr):
     assert _layer(kvr, w=_w(kvr, wq=None)) == -1
     assert _layer(kvr, w=_w(kvr, bq=FAKE)) == -1           # partial biases
     assert _layer(kvr, ws_bytes=1024) == -6
+    assert _layer(kvr, gpos=FAKE + 4, ws_bytes=1024) == -1   # misaligned position map
     assert _layer(kvr, B=0, x_rows=0) == 0                 # no-op success
     assert _layer(kvr, B=0, x_rows=512) == 0
 
@@ -115,16 +116,30 @@ def test_build_repair_set_host_validation(kvr):
     assert f(mode=8) == -1
     assert f(s=None) == -1
     assert f(mode=3) == -1                                 # INIT_META without meta
-    bad_meta = kvr.kvr_meta(FAKE, None, 9)
+    bad_meta = kvr.kvr_meta(flags=FAKE, block_id=None, gpos=None, n_tokens=9)
     assert f(mode=3, meta=C.byref(bad_meta)) == -1         # meta for another N
 
 
 def test_check_support_and_plan_host_validation(kvr):
     lib = kvr.lib()
-    assert lib.kvr_check_support(FAKE, 5, 4, 0, FAKE, None) == -1
-    assert lib.kvr_check_support(FAKE, 1, 4, 0, None, None) == -1
+    assert lib.kvr_check_support(FAKE, 5, 4, 0, None, FAKE, None) == -1      # B > N
+    assert lib.kvr_check_support(FAKE, 1, 4, 0, None, None, None) == -1      # no result word
+    assert lib.kvr_check_support(FAKE, 1, 4, 0, FAKE + 4, FAKE, None) == -1  # misaligned gpos
     assert lib.kvr_build_plan(FAKE, 4, 0, FAKE, FAKE, None) == -1
     assert lib.kvr_build_plan(FAKE, 0, 7, FAKE, FAKE, None) == 0
+
+
+def test_build_runs_host_validation(kvr):
+    lib = kvr.lib()
+    out = kvr.kvr_repair_set(None, FAKE, FAKE, FAKE, 16)
+    f = lambda T=FAKE, B=4, n=8, o=out: lib.kvr_build_runs(T, B, n, 0, C.byref(o), None, None)
+    assert f(B=-1) == -1
+    assert f(B=9) == -1                                    # B > N
+    assert f(T=None) == -1
+    assert f(T=FAKE + 4) == -1                             # misaligned
+    assert f(B=17, n=40) == -1                             # cap < B
+    no_counts = kvr.kvr_repair_set(None, FAKE, FAKE, None, 16)
+    assert f(o=no_counts) == -1
 
 
 def test_status_strings(kvr):
@@ -136,7 +151,7 @@ def test_python_binding_has_the_c_names(kvr):
     for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
               "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
               "kvr_attention_workspace_bytes", "kvr_biased_attention", "kvr_shift_cache",
-              "kvr_sur_scores", "kvr_sur_select",
+              "kvr_sur_scores", "kvr_sur_select", "kvr_build_runs",
               "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
         assert callable(getattr(kvr, n))
 

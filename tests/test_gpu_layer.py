@@ -14,10 +14,13 @@ pytestmark = pytest.mark.gpu
 
 
 def run_layer_case(w: wl.Workload, T_np=None, x_packed=False, stream=None, check_rows=None,
-                   cfg_over=None):
-    """Runs one layer on the GPU and the oracle; returns the max errors."""
+                   cfg_over=None, gpos=None):
+    """Runs one layer on the GPU and the oracle; returns the max errors.
+    ``gpos``: optional global-position map (int32 [N]) given to both sides."""
     m = kvr()
     cfg = cfg_of(w, **(cfg_over or {}))
+    s_blk, e_blk = wl.blocks(w)
+    flags0 = oracle.initial_meta(s_blk, e_blk, w.n_tokens)[0]
     log(f"[layer] {w.name} dtype={w.dtype} support={w.support} "
         f"B={'seams' if T_np is None else len(T_np)} packed_input={x_packed}")
     if T_np is None and w.support == "seams":
@@ -25,11 +28,16 @@ def run_layer_case(w: wl.Workload, T_np=None, x_packed=False, stream=None, check
     else:
         T_np = wl.explicit_support(w) if T_np is None else np.asarray(T_np, np.int32)
         dT = torch.from_numpy(T_np.astype(np.int32)).cuda()
-        flags = torch.from_numpy(wl.initial_flags(w)).cuda()
+        flags = torch.from_numpy(flags0).cuda()
     T = dT.cpu().numpy().astype(np.int64)
     B = len(T)
-    flags0 = wl.initial_flags(w)
     assert np.array_equal(flags.cpu().numpy(), flags0)
+    dg = None
+    if gpos is not None:
+        oracle.check_positions(gpos, w.n_tokens)
+        dg = torch.from_numpy(np.asarray(gpos, np.int32)).cuda()
+        m.kvr_check_support(dT, w.n_tokens, 0, torch.empty(4, dtype=torch.int32, device="cuda"),
+                            gpos=dg)
     wnp = wl.layer_weights(w, 0)
     K0, V0 = wl.kv_cache(w, 0)
     X = wl.hidden_states(w)
@@ -39,14 +47,14 @@ def run_layer_case(w: wl.Workload, T_np=None, x_packed=False, stream=None, check
     x_in = torch.from_numpy(X[T] if x_packed else X).cuda()
     x_out = torch.empty((B, w.hidden), dtype=torch.float32, device="cuda")
     ws = workspace(cfg, B, w.n_tokens)
-    m.kvr_layer_repair(cfg, dw, kc, vc, flags, dT, x_in, x_out, ws, stream=stream)
+    m.kvr_layer_repair(cfg, dw, kc, vc, flags, dT, x_in, x_out, ws, gpos=dg, stream=stream)
     torch.cuda.synchronize()
 
     c_or = cfg_of(w, **(cfg_over or {}))
     K, V = K0.astype(np.float64), V0.astype(np.float64)
     f = flags0.copy()
     rows = T if check_rows is None else T[:check_rows]
-    y = oracle.stack_repair(c_or, [(wnp, K, V)], f, rows, X)
+    y = oracle.stack_repair(c_or, [(wnp, K, V)], f, rows, X, gpos=gpos)
     n = len(rows)
     errs = {}
     errs["y"] = assert_close(w, cpu(x_out[:n]), y, "packed output")
@@ -57,7 +65,7 @@ def run_layer_case(w: wl.Workload, T_np=None, x_packed=False, stream=None, check
     keep[dT.long()] = False
     assert torch.equal(kc[keep], kc0[keep]) and torch.equal(vc[keep], vc0[keep])
     f_ref = flags0.copy()
-    f_ref[T] &= np.uint8(0xFC)
+    oracle.write_back_flags(f_ref, T)
     assert np.array_equal(flags.cpu().numpy(), f_ref)
     return errs
 
@@ -91,6 +99,26 @@ def test_tiny_f32_edges_single_row_first_position_and_all_rows():
     run_layer_case(wl.TINY.with_(support="explicit"), T_np=np.array([0], np.int32))
     run_layer_case(wl.TINY.with_(support="explicit"), T_np=np.array([511], np.int32))
     run_layer_case(wl.TINY.with_(support="explicit"), T_np=np.arange(512, dtype=np.int32))
+
+
+def test_tiny_f32_global_position_map():
+    """A non-identity global-position map (cross-attention reuse page, 6.2):
+    positions with gaps, as in a cache that lost spans without a Shift; RoPE
+    rotates each repaired row at its mapped position."""
+    N = wl.TINY.n_tokens
+    t = np.arange(N)
+    g = (t + 5 * (t >= 130) + 17 * (t >= 300) + 1000).astype(np.int32)
+    run_layer_case(wl.TINY, gpos=g)
+    # the identity map given explicitly is the default path
+    run_layer_case(wl.TINY, gpos=np.arange(N, dtype=np.int32))
+
+
+def test_bf16_seams_global_position_map():
+    w = wl.Workload("gpos-bf16", 105, hidden=256, n_q_heads=4, n_kv_heads=2, head_dim=128,
+                    intermediate=384, n_layers=1, n_tokens=900, block_size=150, dtype="bf16",
+                    alpha=-1.0, beta=-2.0, tau=6)
+    t = np.arange(w.n_tokens)
+    run_layer_case(w, gpos=(3 * t + 11).astype(np.int32))
 
 
 def test_tiny_bf16_head_dim_128_group_6():

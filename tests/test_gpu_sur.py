@@ -65,10 +65,16 @@ def _check_select(r_np, starts, B, pos0, T, rs, rl, uscore):
         assert len(units) == 1
         u = units.pop()
         a, b = bounds[u]
-        wlen = sum(1 for x in T if a <= x - pos0 < b)
+        # the GPU's positions in the cut unit must be one contiguous window
+        # of the oracle's width, which starts at the GPU's first position
+        g_pos = sorted(int(x) - pos0 - a for x in T if a <= x - pos0 < b)
+        w_pos = sorted(int(x) - pos0 - a for x in want if a <= x - pos0 < b)
+        wlen = len(w_pos)
+        assert wlen > 0 and w_pos == list(range(w_pos[0], w_pos[0] + wlen))
+        assert g_pos == list(range(g_pos[0], g_pos[0] + wlen)), "GPU window not contiguous"
+        assert 0 <= g_pos[0] and g_pos[-1] < b - a
         env = sur.envelope(r_np[a:b])
-        g0 = int(min(x for x in T if a <= x - pos0 < b)) - pos0 - a
-        w0 = int(min(x for x in want if a <= x - pos0 < b)) - pos0 - a
+        g0, w0 = g_pos[0], w_pos[0]
         sg, so = float(np.sum(env[g0:g0 + wlen])), float(np.sum(env[w0:w0 + wlen]))
         log(f"  window tie in unit {u}: gpu start {g0} sum {sg:.8g}, oracle start {w0} sum {so:.8g}")
         assert abs(sg - so) <= 1e-5 * max(1.0, abs(so))

@@ -314,3 +314,88 @@ def test_workload_tiny_layer_runs():
     y = oracle.stack_repair(w, [(wl.layer_weights(w, 0), K, V)], flags, T, X)
     assert y.shape == (24, 256) and np.all(np.isfinite(y))
     assert np.all(flags[T] == 0)
+
+
+# ------------------------------------------------------- global positions g_t
+
+
+def _gapped_positions(N, rng):
+    """A strictly increasing position map with gaps (as a cache that lost
+    spans without being shifted would have)."""
+    return np.cumsum(rng.integers(1, 5, size=N)) + 7
+
+
+def test_identity_position_map_is_bitwise_the_default():
+    c = Cfg()
+    N = 30
+    layers, caches, X = _stack_inputs(12, c, N, 2)
+    T = [10, 11, 20, 29]
+    ca, cb = _copy(caches), _copy(caches)
+    a = oracle.stack_repair(c, [(w, K, V) for w, (K, V) in zip(layers, ca)], mixed_flags(N, 10),
+                            T, X)
+    b = oracle.stack_repair(c, [(w, K, V) for w, (K, V) in zip(layers, cb)], mixed_flags(N, 10),
+                            T, X, gpos=np.arange(N))
+    assert np.array_equal(a, b)
+    for (Ka, Va), (Kb, Vb) in zip(ca, cb):
+        assert np.array_equal(Ka, Kb) and np.array_equal(Va, Vb)
+
+
+def test_position_map_matches_pure_python_brute_force():
+    c = Cfg()
+    N, L = 18, 2
+    rng = np.random.default_rng(13)
+    g = _gapped_positions(N, rng)
+    layers, caches, X = _stack_inputs(13, c, N, L, bias=True)
+    flags = mixed_flags(N, 6)
+    T = [5, 6, 7, 12, 17]
+    cc = _copy(caches)
+    f1 = flags.copy()
+    got = oracle.stack_repair(c, [(w, K, V) for w, (K, V) in zip(layers, cc)], f1, T, X, gpos=g)
+    Kp = [K.tolist() for K, _ in caches]
+    Vp = [V.tolist() for _, V in caches]
+    fp = flags.tolist()
+    xs = [X[t].tolist() for t in T]
+    for li in range(L):
+        xs = refs.py_layer(c, layers[li], Kp[li], Vp[li], fp, T, xs, pos=g)
+    assert np.allclose(got, np.array(xs), atol=1e-11, rtol=1e-11)
+    for li in range(L):
+        assert np.allclose(cc[li][0], np.array(Kp[li]), atol=1e-12)
+
+
+def test_position_map_degeneration_equals_full_prefill_at_those_positions():
+    # a full recompute with alpha = beta = 0 and a gapped position map is a
+    # textbook prefill whose RoPE uses those positions
+    c = Cfg(alpha=0.0, beta=0.0)
+    N, L, blk = 40, 2, 10
+    rng = np.random.default_rng(14)
+    g = _gapped_positions(N, rng)
+    layers, caches, X = _stack_inputs(14, c, N, L, bias=False)
+    cc = _copy(caches)
+    flags = mixed_flags(N, blk)
+    run = lambda TT: oracle.stack_repair(c, [(w, K, V) for w, (K, V) in zip(layers, cc)], flags,
+                                         TT, X, gpos=g)
+    y1 = run(np.arange(blk))
+    y2 = run(np.arange(blk, N))
+    want, kvs = refs.full_prefill(c, layers, X, pos=g)
+    assert np.allclose(y1, want[:blk], atol=1e-11)
+    assert np.allclose(y2, want[blk:], atol=1e-11)
+    for li in range(L):
+        assert np.allclose(cc[li][0], kvs[li][0], atol=1e-11)
+    # and it is not the identity-position prefill
+    other, _ = refs.full_prefill(c, layers, X)
+    assert not np.allclose(y2, other[blk:], atol=1e-6)
+
+
+def test_constant_position_offset_leaves_a_full_recompute_unchanged():
+    # RoPE scores depend only on position differences, so shifting every
+    # position by one constant changes nothing once all keys are recomputed
+    c = Cfg(alpha=0.0, beta=0.0)
+    N = 24
+    layers, caches, X = _stack_inputs(15, c, N, 2)
+    outs = []
+    for off in (0, 1000):
+        cc = _copy(caches)
+        outs.append(oracle.stack_repair(c, [(w, K, V) for w, (K, V) in zip(layers, cc)],
+                                        np.zeros(N, np.uint8), np.arange(N), X,
+                                        gpos=np.arange(N) + off))
+    assert np.allclose(outs[0], outs[1], atol=1e-10)

@@ -163,7 +163,7 @@ def test_isolated_support_is_budgeted_and_non_adjacent():
 
 
 @pytest.mark.parametrize("T,first,B", [([5, 5, 6], 0, 3), ([6, 5], 0, 2), ([2, 9], 3, 2),
-                                        ([3, 10], 3, 2), ([3, 4], 3, 3)])
+                                        ([3, 10], 3, 2), ([3, 4], 3, 3), ([-1, 2], -5, 2)])
 def test_check_support_errors(T, first, B):
     with pytest.raises(oracle.BadSupport):
         oracle.check_support(T, 10, first, B)

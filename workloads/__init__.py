@@ -311,6 +311,14 @@ def layer_weights(w: Workload, layer: int, threads: Optional[int] = None) -> Dic
     return d
 
 
+def budget_count(S: int, percent: float) -> int:
+    """Size of a budgeted support over an S-position suffix: the exact budget
+    min(S, ceil(S * percent / 100)) of Budgeted KV-Cache Repair, section 7.1,
+    Eq. 3, in integers (percent with at most three decimals)."""
+    num = S * int(round(percent * 1000))
+    return min(S, -(-num // 100000))
+
+
 def isolated_support(w: Workload) -> np.ndarray:
     """Budgeted set of pairwise non-adjacent single positions after block 1.
 
@@ -321,8 +329,7 @@ def isolated_support(w: Workload) -> np.ndarray:
     """
     s, e = blocks(w)
     S = w.n_tokens - int(e[0])
-    num = S * int(round(w.budget_percent * 1000))
-    B = min(S, -(-num // 100000))
+    B = budget_count(S, w.budget_percent)
     if B > (S + 1) // 2:
         raise ValueError("budget too large for a non-adjacent support")
     g = np.random.Generator(np.random.PCG64(np.random.SeedSequence(
@@ -427,6 +434,5 @@ def sur_ids(w: SurWorkload) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
 
 
 def sur_budget(w: SurWorkload) -> int:
-    """Exact budget B(S, b) = min(S, ceil(S * b / 100)) (Eq. 3), in integers."""
-    num = w.n_suffix * int(round(w.budget_percent * 1000))
-    return min(w.n_suffix, -(-num // 100000))
+    """Budget of the SUR workload over its suffix (see budget_count)."""
+    return budget_count(w.n_suffix, w.budget_percent)
