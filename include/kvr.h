@@ -306,6 +306,29 @@ kvr_status kvr_biased_attention(const kvr_config* cfg, kvr_kv cache, const uint8
                                 hipStream_t stream);
 
 /*
+ * kvr_biased_attention_noalloc - kvr_biased_attention without a workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops (a decode step per token), harnesses
+ * that forbid hipMalloc.  The call allocates nothing; its scratch is a
+ * static device array of KVR_NOALLOC_SCRATCH_BYTES held by the library on
+ * every GPU it runs on until the process ends (looked up once per device on
+ * the first call there).  Same arguments, results and errors as
+ * kvr_biased_attention, plus KVR_ERR_WORKSPACE when the shape needs more
+ * scratch than that (kvr_attention_workspace_bytes() - 256 >
+ * KVR_NOALLOC_SCRATCH_BYTES).  A bf16 decode call (B * Hq/Hkv <= 64) needs
+ * ceil(N / 256) * Hkv * B * (Hq/Hkv) * (d + 2) * 4 bytes: 0.9 MB at the 7B
+ * shape (Hkv = 4, d = 128) for B = 1 over N = 16384, 16 MB for B = 9 over
+ * N = 32768.  All calls on one GPU share that GPU's scratch, which keeps
+ * the last call's contents: calls that overlap in time on one GPU
+ * (different streams or threads) race and must be serialised by the caller.
+ */
+enum { KVR_NOALLOC_SCRATCH_BYTES = 32 << 20 };
+kvr_status kvr_biased_attention_noalloc(const kvr_config* cfg, kvr_kv cache,
+                                        const uint8_t* flags, int32_t n_tokens, const float* q,
+                                        const int32_t* d_pos, int32_t B, float* o,
+                                        hipStream_t stream);
+
+/*
  * kvr_shift_cache - the Shift step that precedes a repair (Budgeted KV-Cache
  * Repair, section 7.1, Eq. 2): delete positions [del_start, del_start +
  * del_len) of the cached sequence and position-correct the retained suffix.

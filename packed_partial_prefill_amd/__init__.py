@@ -26,6 +26,7 @@ KVR_F32, KVR_BF16 = 0, 1
 KVR_FLAG_LOCAL, KVR_FLAG_SINK = 1, 2
 KVR_SEAM_ASYMMETRIC, KVR_INIT_META = 1, 2
 KVR_ATTN_QROWS, KVR_ATTN_KV_TILE = 128, 64
+KVR_NOALLOC_SCRATCH_BYTES = 32 << 20
 KERNEL_NAMES = ["plan", "norm", "qkv", "rope", "attn", "attn_merge", "oproj", "gateup", "down",
                 "final", "qprep", "shift", "sur_score", "sur_select"]
 KVR_KERNEL_COUNT = len(KERNEL_NAMES)
@@ -86,6 +87,8 @@ _sigs = {
     "kvr_attention_workspace_bytes": (C.c_size_t, [C.POINTER(kvr_config), _I, _I]),
     "kvr_biased_attention": (C.c_int, [C.POINTER(kvr_config), kvr_kv, _P, _I, _P, _P, _I, _P, _P,
                                        C.c_size_t, _P]),
+    "kvr_biased_attention_noalloc": (C.c_int, [C.POINTER(kvr_config), kvr_kv, _P, _I, _P, _P, _I,
+                                               _P, _P]),
     "kvr_shift_cache": (C.c_int, [C.POINTER(kvr_config), _I, C.POINTER(kvr_kv), C.POINTER(kvr_kv),
                                   _P, _P, _P, _P, _I, _I, _I, C.c_uint8, _P]),
     "kvr_sur_scores": (C.c_int, [_P, C.c_int, _I, _I, _P, _I, _P, _I, _P, _P]),
@@ -248,6 +251,16 @@ def kvr_biased_attention(cfg: Config, k_cache, v_cache, flags, q, d_pos, o, ws,
                                      _ptr(flags), k_cache.shape[0], _ptr(q), _ptr(d_pos),
                                      d_pos.numel(), _ptr(o), _ptr(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def kvr_biased_attention_noalloc(cfg: Config, k_cache, v_cache, flags, q, d_pos, o,
+                                 stream=None) -> None:
+    """kvr_biased_attention without a workspace: the library's static
+    per-GPU scratch is used (calls that overlap on one GPU race)."""
+    c = cfg.c()
+    _check(_lib.kvr_biased_attention_noalloc(C.byref(c), kvr_kv(_ptr(k_cache), _ptr(v_cache)),
+                                             _ptr(flags), k_cache.shape[0], _ptr(q), _ptr(d_pos),
+                                             d_pos.numel(), _ptr(o), _stream(stream)))
 
 
 def kvr_shift_cache(cfg: Config, src: Sequence[Tuple], dst: Sequence[Tuple], del_start: int,

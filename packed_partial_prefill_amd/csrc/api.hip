@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "kvr_internal.h"
@@ -345,6 +346,36 @@ kvr_status run_biased_attention(const kvr_config* cfg, const kvr::Shape& sh, con
   return KVR_OK;
 }
 
+// Scratch of kvr_biased_attention_noalloc: a file-scope device array, one
+// copy per GPU, held until the process ends.  Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol); it uses the device address that hipGetSymbolAddress returns,
+// looked up once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[KVR_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+kvr_status noalloc_scratch(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(KVR_ERR_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (reinterpret_cast<uintptr_t>(ptr) & 255u)
+      return fail(KVR_ERR_HIP, "static scratch is not 256-byte aligned");
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return KVR_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -491,6 +522,24 @@ kvr_status kvr_biased_attention(const kvr_config* cfg, kvr_kv cache, const uint8
   const size_t slack = static_cast<size_t>(base - static_cast<uint8_t*>(ws));
   if (ws_bytes < L.total + slack)
     return fail(KVR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total + slack);
+  return run_biased_attention(cfg, sh, L, cache, flags, n_tokens, q, d_pos, B, o, base, stream);
+}
+
+kvr_status kvr_biased_attention_noalloc(const kvr_config* cfg, kvr_kv cache, const uint8_t* flags,
+                                        int32_t n_tokens, const float* q, const int32_t* d_pos,
+                                        int32_t B, float* o, hipStream_t stream) {
+  g_err[0] = '\0';
+  kvr::Shape sh;
+  kvr_status st = check_attention_args(cfg, cache, flags, n_tokens, q, d_pos, B, o, &sh);
+  if (st != KVR_OK || B == 0) return st;
+  const AttnLayout L = attn_layout_for(cfg, sh, B, n_tokens);
+  if (L.total > static_cast<size_t>(KVR_NOALLOC_SCRATCH_BYTES))
+    return fail(KVR_ERR_WORKSPACE,
+                "this call needs %zu bytes of scratch; the static scratch holds %d "
+                "(use kvr_biased_attention with a workspace)",
+                L.total, static_cast<int>(KVR_NOALLOC_SCRATCH_BYTES));
+  uint8_t* base = nullptr;
+  if ((st = noalloc_scratch(&base)) != KVR_OK) return st;
   return run_biased_attention(cfg, sh, L, cache, flags, n_tokens, q, d_pos, B, o, base, stream);
 }
 
