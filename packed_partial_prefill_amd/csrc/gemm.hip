@@ -185,6 +185,11 @@ using TileM = Tile<128, 128, 2, 2, 4, 2>;
 using TileMP = Tile<128, 128, 2, 2, 4, 2, true>;    // W pairs: fused gate/up
 using TileS = Tile<64, 128, 1, 2, 6, 2>;
 using TileSP = Tile<64, 128, 1, 2, 4, 2, true>;     // W pairs: fused gate/up
+// Fused gate/up for 128 < M <= 256: every row of A in one tile, so each
+// weight panel is staged in LDS once (two 128-row tiles each stage it, and
+// a CU holding two of them takes in twice the bytes).
+using TileT = Tile<256, 128, 4, 2, 4, 1>;
+using TileTP = Tile<256, 128, 4, 2, 4, 1, true>;
 
 __device__ __forceinline__ int swz(int row, int chunk) {
   return row * (KB * 2) + ((chunk ^ ((row >> 2) & 3)) << 4);
@@ -613,14 +618,21 @@ void launch_variant(int variant, const bf16_t* A, const WeightSegs& W, int M, in
   switch (variant) {
     case 0: launch_tile<MODE, TileLP, TileL>(A, W, M, N, K, splits, part, out, stream); break;
     case 1: launch_tile<MODE, TileMP, TileM>(A, W, M, N, K, splits, part, out, stream); break;
+    case 3:
+      if constexpr (MODE == 1) {
+        launch_tile<MODE, TileTP, TileT>(A, W, M, N, K, splits, part, out, stream);
+        break;
+      }
+      [[fallthrough]];
     default: launch_tile<MODE, TileSP, TileS>(A, W, M, N, K, splits, part, out, stream); break;
   }
 }
 
 struct VariantGeom { int bm, bn, occupancy; };
-constexpr VariantGeom kGeom[3] = {{TileL::BM, TileL::BN, TileL::occupancy},
+constexpr VariantGeom kGeom[4] = {{TileL::BM, TileL::BN, TileL::occupancy},
                                   {TileM::BM, TileM::BN, TileM::occupancy},
-                                  {TileS::BM, TileS::BN, TileS::occupancy}};
+                                  {TileS::BM, TileS::BN, TileS::occupancy},
+                                  {TileT::BM, TileT::BN, TileT::occupancy}};
 
 }  // namespace
 
@@ -660,6 +672,9 @@ GemmPlan gemm_plan_for(kvr_dtype dt, int M, int N, int K, bool swiglu) {
   const VariantGeom vg = kGeom[variant];
   const long tiles_m = (M + vg.bm - 1) / vg.bm;
   constexpr long kTarget = 256;
+  // fused gate/up with all rows in one 256 x 128 tile (one workgroup per CU)
+  if (swiglu && M > 128 && M <= 256 && (N + kGeom[3].bn / 2 - 1) / (kGeom[3].bn / 2) >= kTarget / 2)
+    return GemmPlan{3, 1, true};
   if (swiglu && tiles_m * ((N + vg.bn / 2 - 1) / (vg.bn / 2)) >= kTarget / 2)
     return GemmPlan{variant, 1, true};
   const long tiles = tiles_m * ((cols + vg.bn - 1) / vg.bn);

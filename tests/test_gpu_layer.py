@@ -151,6 +151,17 @@ def test_bf16_m513_one_row_past_the_small_tiles():
     run_layer_case(w)
 
 
+def test_bf16_fused_gateup_tall_tile_m200():
+    """200 packed rows with a wide MLP (intermediate 8192): the fused gate/up
+    runs on the 256 x 128 tile that holds every row (rows 200..255 clamped on
+    load and masked on store); hidden 320 is an odd number of weight pairs."""
+    w = wl.Workload("tall-gateup-bf16", 106, hidden=320, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                    intermediate=8192, n_layers=1, n_tokens=700, block_size=100, dtype="bf16",
+                    alpha=-1.0, beta=-2.0, support="contiguous", support_start=300,
+                    support_len=200)
+    run_layer_case(w)
+
+
 def test_qwen15_layer_seams():
     run_layer_case(wl.QWEN15_LAYER)
 
