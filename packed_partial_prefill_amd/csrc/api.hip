@@ -72,10 +72,21 @@ struct Launch {
 
 // ---------------------------------------------------------------- config
 // dtype and attention heads: what every entry point reads.
+// The value of a dtype field as its bytes hold it: a C caller may store any
+// int there, and reading a value outside the enumerators through the enum
+// type is undefined in C++.
+int raw_dtype(const kvr_dtype* p) {
+  int v = 0;
+  static_assert(sizeof(kvr_dtype) == sizeof(int), "kvr_dtype is int-sized");
+  std::memcpy(&v, p, sizeof(v));
+  return v;
+}
+
 kvr_status check_heads(const kvr_config* c, kvr::Shape* sh) {
   if (!c) return fail(KVR_ERR_INVALID_ARGUMENT, "cfg is NULL");
-  if (c->dtype != KVR_F32 && c->dtype != KVR_BF16)
-    return fail(KVR_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(c->dtype));
+  const int dt = raw_dtype(&c->dtype);
+  if (dt != KVR_F32 && dt != KVR_BF16)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "unknown dtype %d", dt);
   if (c->n_q_heads <= 0 || c->n_kv_heads <= 0)
     return fail(KVR_ERR_INVALID_ARGUMENT, "non-positive head counts");
   if (c->head_dim != 64 && c->head_dim != 128)
@@ -619,8 +630,8 @@ kvr_status kvr_sur_scores(const void* d_E, kvr_dtype dtype, int32_t vocab, int32
                           const int32_t* d_suffix_ids, int32_t S, const int32_t* d_query_ids,
                           int32_t Q, float* d_r, hipStream_t stream) {
   g_err[0] = '\0';
-  if (dtype != KVR_F32 && dtype != KVR_BF16)
-    return fail(KVR_ERR_INVALID_ARGUMENT, "unknown dtype %d", static_cast<int>(dtype));
+  if (raw_dtype(&dtype) != KVR_F32 && raw_dtype(&dtype) != KVR_BF16)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "unknown dtype %d", raw_dtype(&dtype));
   if (vocab < 1 || S < 0 || Q < 1 || Q > kvr::kSurMaxQuery)
     return fail(KVR_ERR_INVALID_ARGUMENT, "vocab=%d, S=%d, Q=%d (1 <= Q <= %d)", vocab, S, Q,
                 kvr::kSurMaxQuery);
