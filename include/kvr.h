@@ -316,9 +316,11 @@ kvr_status kvr_biased_attention(const kvr_config* cfg, kvr_kv cache, const uint8
  * kvr_biased_attention, plus KVR_ERR_WORKSPACE when the shape needs more
  * scratch than that (kvr_attention_workspace_bytes() - 256 >
  * KVR_NOALLOC_SCRATCH_BYTES).  A bf16 decode call (B * Hq/Hkv <= 64) needs
- * ceil(N / 256) * Hkv * B * (Hq/Hkv) * (d + 2) * 4 bytes: 0.9 MB at the 7B
- * shape (Hkv = 4, d = 128) for B = 1 over N = 16384, 16 MB for B = 9 over
- * N = 32768.  All calls on one GPU share that GPU's scratch, which keeps
+ * at most 256 * B * (Hq/Hkv) * (d + 2) * 4 bytes whatever N (8.5 MB at 64
+ * pairs per KV head, d = 128), so every decode call fits; larger B take the
+ * packed attention path, whose scratch grows with B and N (33 MB for B = 64
+ * over N = 16384 at the 7B shape, beyond the limit).  All calls on one GPU
+ * share that GPU's scratch, which keeps
  * the last call's contents: calls that overlap in time on one GPU
  * (different streams or threads) race and must be serialised by the caller.
  */

@@ -1182,60 +1182,89 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
 
 // ---------------------------------------------------------------------------
 // Inference-mode decode kernel: few pairs per KV head (B * G <= 64), the
-// whole cache streamed once, HBM-bound.
+// cache streamed once, HBM-bound.
 //
-// Workgroup (chunk c, KV head g) owns keys [256c, 256c + 256); each of its 4
-// waves owns one 64-key tile and issues that tile's K and V DMA (32 KB at
-// d = 128) at once, so every CU keeps its workgroup's 128 KB in flight.
-// Queries are read in float32, scaled by log2(e)/sqrt(d) and rounded to bf16
-// on load.  Each wave forms S^T = K Q^T for its tile and all pairs (one or
-// two 32-pair column blocks) as soon as its K slices land (V is still in
-// flight), adds the log2(e)-scaled metadata bias, masks keys past each
-// pair's position, and accumulates O^T = V^T P^T with the same operand
-// layouts as the packed kernel above.  The waves run independently until
-// their 4 (max, sum, O) are merged through LDS; the workgroup writes one
-// partial per pair and k_decode_merge combines the chunks.
+// The keys 0..u_max a launch needs are cut into steps of 128; workgroup
+// (c, g), one of W per KV head g, owns the steps [c * spw, (c + 1) * spw),
+// and wave w of it takes the 32-key sub-tile w of each of its steps.  Every
+// wave streams its own sub-tiles (K and V, 16 KB at d = 128, plus their
+// flag bytes) through a ring of two LDS slots: the next sub-tile is in
+// flight while the current one is used, so a CU keeps up to 128 KB on the
+// way for as long as its range lasts (a long cache no longer takes several
+// rounds of one-shot workgroups, each idling between its loads and the
+// next workgroup's).  Queries are read in float32, scaled by
+// log2(e)/sqrt(d) and rounded to bf16 once.  Per sub-tile a wave forms
+// S^T = K Q^T for all pairs (one or two 32-pair column blocks), adds the
+// log2(e)-scaled metadata bias, masks keys past each pair's position,
+// updates its running (max, sum) and accumulates O^T = V^T P^T, with the
+// operand layouts of the packed kernels (transposing reads for V^T).  LDS
+// reads are inline assembly with explicit waits, so that the DMA into the
+// other slot stays in flight.  At the end the four waves are combined
+// through LDS and the workgroup writes one partial per pair;
+// k_decode_merge combines the workgroups of each KV head.
 // ---------------------------------------------------------------------------
-constexpr int kDecKeys = 4 * kKvTile;   // keys per workgroup
+constexpr int kDecSub = 32;                // keys per wave sub-tile
+constexpr int kDecStep = 4 * kDecSub;      // keys per workgroup step
 constexpr int kDecMaxPairs = 64;
 
 template <int D>
 struct DecLds {
-  static constexpr int kvWave = 2 * kKvTile * D * 2;                 // K and V tile of one wave
-  static constexpr int kv = 4 * kvWave;
+  static constexpr int kBytes = kDecSub * D * 2;                     // K of one sub-tile
+  static constexpr int slot = 2 * kBytes;                            // K then V
+  static constexpr int wave = 2 * slot;                              // two slots per wave
+  static constexpr int kv = 4 * wave;
+  static constexpr int flags = 4 * 2 * kDecSub;                      // flag bytes per slot
   static constexpr int otRow = D + 4;                                // floats per pair row (padded)
   static constexpr int ot = 4 * kDecMaxPairs * otRow * 4;            // O of 4 waves
-  static constexpr int body = kv > ot ? kv : ot;
+  static constexpr int body = kv + flags > ot ? kv + flags : ot;
   static constexpr int ml = 4 * kDecMaxPairs * 2 * 4;
   static constexpr int total = body + ml;
+  static_assert(wave + slot < 65536, "ds offset field");
 };
+
+// Workgroups per KV head and steps per workgroup of a decode launch over
+// n_tokens cached positions: one workgroup per CU in all, each with a
+// contiguous run of steps.
+struct DecGrid {
+  int per_head, spw;
+};
+constexpr int kDecWorkgroups = 256;      // one per CU of an MI355X
+DecGrid decode_grid(int n_tokens, const Shape& sh) {
+  const int steps = (n_tokens + kDecStep - 1) / kDecStep;
+  int per_head = kDecWorkgroups / sh.hkv;
+  if (per_head < 1) per_head = 1;
+  if (per_head > steps) per_head = steps;
+  const int spw = (steps + per_head - 1) / per_head;
+  return DecGrid{(steps + spw - 1) / spw, spw};
+}
 
 template <int D, int NCB>
 __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
     const float* __restrict__ q, const int32_t* __restrict__ pos, int B, int n_tokens,
     const bf16_t* __restrict__ kc, const bf16_t* __restrict__ vc,
     const uint8_t* __restrict__ flags, int Hq, int Hkv, int G, float q_scale, float bias_local,
-    float bias_sink, float* __restrict__ part_o, float* __restrict__ part_ml) {
+    float bias_sink, int spw, float* __restrict__ part_o, float* __restrict__ part_ml) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   using L = DecLds<D>;
-  constexpr int KCH = D / 8;
-  constexpr int ROWS = 1024 / (D * 2);
-  constexpr int KSL = kKvTile / ROWS;              // 1 KB slices per operand per tile
+  constexpr int KCH = D / 8;                       // 16-byte chunks per row
+  constexpr int ROWS = 1024 / (D * 2);             // rows per 1 KB DMA slice
+  constexpr int KSL = kDecSub / ROWS;              // slices per operand per sub-tile
   constexpr int PAIRS = 32 * NCB;
   const int c = blockIdx.x, g = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = B * G;
   const int u_max = pos[B - 1];
-  if (c * kDecKeys > u_max) return;                // whole chunk in every pair's future
-  const int key0 = c * kDecKeys + wave * kKvTile;
-  const bool active = key0 <= u_max;
+  const int nsteps = u_max / kDecStep + 1;         // steps holding a key 0..u_max
+  const int s0 = c * spw;
+  if (s0 >= nsteps) return;                        // every key here is in every pair's future
+  const int s1 = min(nsteps, s0 + spw);
 
-  uint8_t* kb = lds + wave * L::kvWave;
-  uint8_t* vb = kb + kKvTile * D * 2;
+  uint8_t* wbuf = lds + wave * L::wave;            // this wave's two slots
+  uint8_t* fbuf = lds + L::kv + wave * 2 * kDecSub;
   float* ml = reinterpret_cast<float*>(lds + L::body);
 
-  // queries of this lane's pair columns and the flags of key key0 + lane
-  // (issued first, so that one wait below covers them with the K tile)
+  // queries of this lane's pair columns
   float qv[NCB][D / 16][8];
   int ucol[NCB];
 #pragma unroll
@@ -1253,30 +1282,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
       qv[cb][ks][4] = b.x; qv[cb][ks][5] = b.y; qv[cb][ks][6] = b.z; qv[cb][ks][7] = b.w;
     }
   }
-  const uint8_t fl = flags[min(key0 + lane, n_tokens - 1)];
-
-  const size_t kv_row = static_cast<size_t>(Hkv) * D;
-  if (active) {
-    const bf16_t* kg = kc + static_cast<size_t>(g) * D;
-    const bf16_t* vg = vc + static_cast<size_t>(g) * D;
-#pragma unroll
-    for (int j = 0; j < KSL; ++j) {   // K slices, then V slices
-      const int row = j * ROWS + lane / KCH;
-      const int key = min(key0 + row, n_tokens - 1);   // rows past the cache are masked
-      __builtin_amdgcn_global_load_lds(KVR_GLB(kg + key * kv_row + kchunk<D>(row, lane % KCH) * 8),
-                                       KVR_LDS(kb + j * 1024), 16, 0, 0);
-    }
-#pragma unroll
-    for (int j = 0; j < KSL; ++j) {
-      const int row = j * ROWS + lane / KCH;
-      const int key = min(key0 + row, n_tokens - 1);
-      __builtin_amdgcn_global_load_lds(KVR_GLB(vg + key * kv_row + vchunk<D>(row, lane % KCH) * 8),
-                                       KVR_LDS(vb + j * 1024), 16, 0, 0);
-    }
-  }
-  const float bias_mine =
-      ((fl & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((fl & KVR_FLAG_SINK) ? bias_sink : 0.f);
-
   bf16x8_t qf[NCB][D / 16];
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb)
@@ -1285,8 +1290,60 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
 #pragma unroll
       for (int i = 0; i < 8; ++i) qf[cb][ks][i] = static_cast<__bf16>(qv[cb][ks][i] * q_scale);
 
+  // sub-tile j (keys j * kDecStep + wave * kDecSub ..) into slot b: its flag
+  // bytes first (lanes 0..31), then K, then V.  Rows past the cache are
+  // clamped to its last row (those keys are masked).
+  const size_t kv_row = static_cast<size_t>(Hkv) * D;
+  const bf16_t* kg = kc + static_cast<size_t>(g) * D;
+  const bf16_t* vg = vc + static_cast<size_t>(g) * D;
+  auto issue = [&](int j, int b) __attribute__((always_inline)) {
+    const int key0 = j * kDecStep + wave * kDecSub;
+    if (key0 + kDecSub <= n_tokens) {              // 32 flag bytes as 8 dwords
+      if (lane < kDecSub / 4)
+        __builtin_amdgcn_global_load_lds(KVR_GLB(flags + key0 + 4 * lane),
+                                         KVR_LDS(fbuf + b * kDecSub), 4, 0, 0);
+    } else if (lane < kDecSub) {                   // the cache's last sub-tile
+      fbuf[b * kDecSub + lane] = flags[min(key0 + lane, n_tokens - 1)];
+    }
+#pragma unroll
+    for (int sl = 0; sl < KSL; ++sl) {
+      const int row = sl * ROWS + lane / KCH;
+      const int key = min(key0 + row, n_tokens - 1);
+      __builtin_amdgcn_global_load_lds(KVR_GLB(kg + key * kv_row + kchunk<D>(row, lane % KCH) * 8),
+                                       KVR_LDS(wbuf + b * L::slot + sl * 1024), 16, 0, 0);
+    }
+#pragma unroll
+    for (int sl = 0; sl < KSL; ++sl) {
+      const int row = sl * ROWS + lane / KCH;
+      const int key = min(key0 + row, n_tokens - 1);
+      __builtin_amdgcn_global_load_lds(KVR_GLB(vg + key * kv_row + vchunk<D>(row, lane % KCH) * 8),
+                                       KVR_LDS(wbuf + b * L::slot + L::kBytes + sl * 1024), 16, 0,
+                                       0);
+    }
+  };
+  constexpr int kIssued = 2 * KSL + 1;             // vector memory instructions per sub-tile
+
+  // fragment addresses in slot 0 (slot 1 is an immediate offset away)
+  uint32_t klane[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    klane[ks] = lds_addr(wbuf) + (lane & 31) * (D * 2) + (kchunk<D>(lane & 31, ks * 2 + half) << 4);
   const int tr_key = (lane & 15) >> 2;
   const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  uint32_t vlane[2][2][D / 32];                    // [16-key half][8-key group][d block]
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int ins = 0; ins < 2; ++ins)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int key = hs * 16 + 8 * ins + 4 * half + tr_key;
+        const int d = db * 32 + tr_d;
+        vlane[hs][ins][db] = lds_addr(wbuf) + L::kBytes + key * (D * 2) +
+                             (vchunk<D>(key, d >> 3) << 4) + (d & 7) * 2;
+      }
+  const uint32_t flane = lds_addr(fbuf) + (lane & 31);
+
   f32x16_t o[NCB][D / 32];
   float m[NCB], l[NCB];
 #pragma unroll
@@ -1299,85 +1356,111 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
       for (int t = 0; t < 16; ++t) o[cb][db][t] = 0.f;
   }
 
-  if (active) {
-    // the bias of the 32 keys this lane holds scores for (key kl's flags
-    // were loaded by lane kl)
-    float kbias[2][16];
+  // one sub-tile from slot B; `next`: the following sub-tile is in flight
+  // behind it (its K is waited for first, so the scores form while its V
+  // lands)
+  auto consume = [&](auto bc, int j, bool next) __attribute__((always_inline)) {
+    constexpr int Bs = decltype(bc)::value;
+    const int key0 = j * kDecStep + wave * kDecSub;
+    if (next) attn_wait_vmcnt<KSL + kIssued>(); else attn_wait_vmcnt<KSL>();
+    // K fragments and the flag byte of key lane & 31
+    u32x4_t kf[D / 16];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb)
+    for (int ks = 0; ks < D / 16; ++ks) kf[ks] = ds_read_b128<Bs * L::slot>(klane[ks]);
+    uint32_t fl = ds_read_u8<Bs * kDecSub>(flane);
+    lds_wait();
 #pragma unroll
-      for (int t = 0; t < 16; ++t)
-        kbias[sb][t] = __shfl(bias_mine, sb * 32 + 8 * (t >> 2) + 4 * half + (t & 3), 64);
-    attn_wait_vmcnt<KSL>();   // K tile landed (V may still be in flight)
+    for (int ks = 0; ks < D / 16; ++ks) reg_fence(kf[ks]);
+    reg_fence(fl);
+    // bias of key kl (its flag byte was read by lane kl)
+    const float bias_mine =
+        ((fl & KVR_FLAG_LOCAL) ? bias_local : 0.f) + ((fl & KVR_FLAG_SINK) ? bias_sink : 0.f);
+    float kbias[16];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) kbias[t] = __shfl(bias_mine, 8 * (t >> 2) + 4 * half + (t & 3), 64);
+    f32x16_t sc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      f32x16_t s[2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
+      for (int t = 0; t < 16; ++t) sc[cb][t] = 0.f;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) s[sb][t] = 0.f;
-        const int key = sb * 32 + (lane & 31);
-#pragma unroll
-        for (int ks = 0; ks < D / 16; ++ks) {
-          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-              kb + key * (D * 2) + (kchunk<D>(key, ks * 2 + half) << 4));
-          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cb][ks], s[sb], 0, 0, 0);
-        }
-        // bias, then keys past the pair's position masked
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int kl = sb * 32 + 8 * (t >> 2) + 4 * half + (t & 3);
-          const float sv = s[sb][t] + kbias[sb][t];
-          s[sb][t] = (key0 + kl <= ucol[cb]) ? sv : -INFINITY;
-        }
-      }
+      for (int ks = 0; ks < D / 16; ++ks)
+        sc[cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, kf[ks]),
+                                                         qf[cb][ks], sc[cb], 0, 0, 0);
       float mt = -INFINITY;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int t = 0; t < 16; ++t) mt = fmaxf(mt, s[sb][t]);
+      for (int t = 0; t < 16; ++t) {
+        const int kl = 8 * (t >> 2) + 4 * half + (t & 3);
+        const float sv = sc[cb][t] + kbias[t];
+        sc[cb][t] = (key0 + kl <= ucol[cb]) ? sv : -INFINITY;
+        mt = fmaxf(mt, sc[cb][t]);
+      }
       mt = xor32_max(mt);
-      m[cb] = mt;
-      float ls = 0.f;
+      // running maximum (branch-free: a column may have seen no key yet)
+      const float mn = fmaxf(m[cb], mt);
+      const bool none = mn == -INFINITY;
+      const float corr = none ? 1.f : fast_exp2(m[cb] - mn);   // 0 while nothing was seen
+      m[cb] = mn;
+      l[cb] *= corr;
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const float e = mt == -INFINITY ? 0.f : fast_exp2(s[sb][t] - mt);
-          s[sb][t] = e;
-          ls += e;
+        for (int t = 0; t < 16; ++t) o[cb][db][t] *= corr;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        const float e = none ? 0.f : fast_exp2(sc[cb][t] - mn);
+        sc[cb][t] = e;
+        l[cb] += e;
+      }
+    }
+    // V^T fragments
+    if (next) attn_wait_vmcnt<kIssued>(); else attn_wait_vmcnt<0>();
+    u32x2_t vf[2][2][D / 32];
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int ins = 0; ins < 2; ++ins)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) vf[hs][ins][db] = ds_read_tr16<Bs * L::slot>(vlane[hs][ins][db]);
+    lds_wait();
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int ins = 0; ins < 2; ++ins)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) reg_fence(vf[hs][ins][db]);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs) {
+        bf16x8_t pb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(sc[cb][hs * 8 + i]);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const u32x4_t w = {vf[hs][0][db][0], vf[hs][0][db][1], vf[hs][1][db][0], vf[hs][1][db][1]};
+          o[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, w), pb,
+                                                              o[cb][db], 0, 0, 0);
         }
-      l[cb] = xor32_add(ls);
-      if (cb == 0) attn_wait_vmcnt<0>();   // V tile landed
-#pragma unroll
-      for (int sb = 0; sb < 2; ++sb)
-#pragma unroll
-        for (int hs = 0; hs < 2; ++hs) {
-          bf16x8_t pb;
-#pragma unroll
-          for (int i = 0; i < 8; ++i) pb[i] = static_cast<__bf16>(s[sb][hs * 8 + i]);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            s16x4_t x[2];
-#pragma unroll
-            for (int ins = 0; ins < 2; ++ins) {
-              const int key = sb * 32 + hs * 16 + 8 * ins + 4 * half + tr_key;
-              const int d = db * 32 + tr_d;
-              const uint8_t* addr = vb + key * (D * 2) + (vchunk<D>(key, d >> 3) << 4) + (d & 7) * 2;
-              x[ins] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  (__attribute__((address_space(3))) s16x4_t*)(addr));
-            }
-            const s16x4_t x0 = x[0], x1 = x[1];
-            const short av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            bf16x8_t a;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) a[i] = __builtin_bit_cast(__bf16, av[i]);
-            o[cb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb, o[cb][db], 0, 0, 0);
-          }
-        }
+      }
+  };
+
+  // the ring: sub-tile j in slot (j - s0) & 1; before a slot is refilled its
+  // reads are complete (lds_wait in consume, then the compiler barrier)
+  issue(s0, 0);
+  if (s0 + 1 < s1) issue(s0 + 1, 1);
+  for (int j = s0; j < s1; j += 2) {
+    consume(std::integral_constant<int, 0>{}, j, j + 1 < s1);
+    asm volatile("" ::: "memory");
+    if (j + 2 < s1) issue(j + 2, 0);
+    if (j + 1 < s1) {
+      consume(std::integral_constant<int, 1>{}, j + 1, j + 2 < s1);
+      asm volatile("" ::: "memory");
+      if (j + 3 < s1) issue(j + 3, 1);
     }
   }
-  __syncthreads();   // every wave is done with its K / V tile: the LDS is reused below
+  attn_wait_vmcnt<0>();
+  __syncthreads();   // every wave is done with its slots: the LDS is reused below
 
   // per-wave (m, l) and O rows [pair][d] (row stride D + 4 floats; each lane
   // stores its accumulators' 4 consecutive d values as one 16-byte word)
@@ -1385,9 +1468,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int col = cb * 32 + (lane & 31);
+    const float lt = xor32_add(l[cb]);             // both halves' keys
     if (half == 0) {
       ml[(wave * kDecMaxPairs + col) * 2] = m[cb];
-      ml[(wave * kDecMaxPairs + col) * 2 + 1] = l[cb];
+      ml[(wave * kDecMaxPairs + col) * 2 + 1] = lt;
     }
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -1430,55 +1514,60 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
   }
 }
 
-// Combines the chunk partials of one (pair, KV head).  1024 threads: the
-// running maximum is a block reduction over the chunks; then thread (d, sg)
-// accumulates chunks sg, sg + SG, ... (SG = 1024 / D groups, loads unrolled
-// so several are in flight) and the groups are summed through LDS.
+// Combines the workgroup partials of one (pair, KV head).  1024 threads:
+// thread (d, sg) takes the partials sg, sg + SG, ... (SG = 1024 / D groups)
+// with a running maximum, so all of a thread's loads are independent of one
+// another and in flight together (one pass over the partials); the groups
+// are then combined through LDS by the D threads of group 0.
 constexpr int kMergeThreads = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void k_decode_merge(
     const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ pos, int B, int Hq, int Hkv, int G, float* __restrict__ o) {
+    const int32_t* __restrict__ pos, int B, int Hq, int Hkv, int G, int spw,
+    float* __restrict__ o) {
   constexpr int SG = kMergeThreads / D;
-  __shared__ float red[kMergeThreads];
-  __shared__ float redl[kMergeThreads];
+  __shared__ float red_m[kMergeThreads];
+  __shared__ float red_l[kMergeThreads];
+  __shared__ float red_o[kMergeThreads];
   const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int P = B * G;
-  const int ns = pos[B - 1] / kDecKeys + 1;        // chunks that wrote partials
-  const size_t stride = static_cast<size_t>(Hkv) * P;   // slots between chunks
+  const int nsteps = pos[B - 1] / kDecStep + 1;
+  const int ns = (nsteps + spw - 1) / spw;         // workgroups that wrote partials
+  const size_t stride = static_cast<size_t>(Hkv) * P;   // slots between workgroups
   const size_t slot0 = static_cast<size_t>(g) * P + p;
-  float M = -INFINITY;
-  for (int s = tid; s < ns; s += kMergeThreads) M = fmaxf(M, part_ml[(slot0 + s * stride) * 2]);
-  red[tid] = M;
-  __syncthreads();
-  for (int w = kMergeThreads / 2; w > 0; w >>= 1) {
-    if (tid < w) red[tid] = fmaxf(red[tid], red[tid + w]);
-    __syncthreads();
-  }
-  M = red[0];
-  __syncthreads();
   const int d = tid % D, sg = tid / D;
-  float acc = 0.f, l = 0.f;
+  float m = -INFINITY, l = 0.f, acc = 0.f;
 #pragma unroll 4
   for (int s = sg; s < ns; s += SG) {
     const size_t slot = slot0 + s * stride;
-    const float ms = part_ml[slot * 2];
-    const float e = ms == -INFINITY ? 0.f : fast_exp2(ms - M);
-    l += e * part_ml[slot * 2 + 1];
-    acc += e * part_o[slot * D + d];
+    const float ms = part_ml[slot * 2], ls = part_ml[slot * 2 + 1], ov = part_o[slot * D + d];
+    const float mn = fmaxf(m, ms);
+    const bool none = mn == -INFINITY;
+    const float a = none ? 0.f : fast_exp2(m - mn);    // rescale of the sums so far
+    const float b = none ? 0.f : fast_exp2(ms - mn);   // 0 for a partial that saw no key
+    l = l * a + b * ls;
+    acc = acc * a + b * ov;
+    m = mn;
   }
-  red[tid] = acc;
-  redl[tid] = l;
+  red_m[tid] = m;
+  red_l[tid] = l;
+  red_o[tid] = acc;
   __syncthreads();
   if (sg == 0) {
+    float M = -INFINITY;
 #pragma unroll
-    for (int j = 1; j < SG; ++j) {
-      acc += red[tid + j * D];
-      l += redl[tid + j * D];
+    for (int j = 0; j < SG; ++j) M = fmaxf(M, red_m[tid + j * D]);
+    float sum = 0.f, den = 0.f;
+#pragma unroll
+    for (int j = 0; j < SG; ++j) {
+      const float mj = red_m[tid + j * D];
+      const float e = mj == -INFINITY ? 0.f : fast_exp2(mj - M);
+      den += e * red_l[tid + j * D];
+      sum += e * red_o[tid + j * D];
     }
     const int r = p / G, h = g * G + (p - r * G);
-    o[(static_cast<size_t>(r) * Hq + h) * D + d] = acc / l;
+    o[(static_cast<size_t>(r) * Hq + h) * D + d] = sum / den;
   }
 }
 
@@ -1538,8 +1627,8 @@ bool decode_supported(kvr_dtype dt, int B, const Shape& sh) {
 }
 
 size_t decode_workspace_bytes(int B, int n_tokens, const Shape& sh) {
-  const size_t chunks = (n_tokens + kDecKeys - 1) / kDecKeys;
-  return chunks * sh.hkv * B * sh.group * (sh.d + 2) * sizeof(float);
+  const size_t per_head = decode_grid(n_tokens, sh).per_head;
+  return per_head * sh.hkv * B * sh.group * (sh.d + 2) * sizeof(float);
 }
 
 size_t attention_workspace_bytes(kvr_dtype dt, int B, int n_tokens, const Shape& sh) {
@@ -1632,28 +1721,28 @@ hipError_t launch_decode_t(const float* q, const int32_t* pos, int B, int n_toke
     if (e != hipSuccess) return e;
     attr = true;
   }
-  const int chunks = (n_tokens + kDecKeys - 1) / kDecKeys;
+  const DecGrid dg = decode_grid(n_tokens, sh);
   const int P = B * sh.group;
   float* part_o = static_cast<float*>(ws);
-  float* part_ml = part_o + static_cast<size_t>(chunks) * sh.hkv * P * sh.d;
+  float* part_ml = part_o + static_cast<size_t>(dg.per_head) * sh.hkv * P * sh.d;
   const float log2e = 1.4426950408889634f;
-  hipLaunchKernelGGL((k_attn_decode<D, NCB>), dim3(chunks, sh.hkv), dim3(kAttnThreads),
+  hipLaunchKernelGGL((k_attn_decode<D, NCB>), dim3(dg.per_head, sh.hkv), dim3(kAttnThreads),
                      DecLds<D>::total, stream, q, pos, B, n_tokens,
                      static_cast<const bf16_t*>(k_cache), static_cast<const bf16_t*>(v_cache),
                      flags, sh.hq, sh.hkv, sh.group, log2e / sqrtf(static_cast<float>(D)),
-                     alpha * log2e, beta * log2e, part_o, part_ml);
+                     alpha * log2e, beta * log2e, dg.spw, part_o, part_ml);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_decode_merge_t(const int32_t* pos, int B, int n_tokens, const Shape& sh,
                                  void* ws, float* o, hipStream_t stream) {
-  const int chunks = (n_tokens + kDecKeys - 1) / kDecKeys;
+  const DecGrid dg = decode_grid(n_tokens, sh);
   const int P = B * sh.group;
   const float* part_o = static_cast<const float*>(ws);
-  const float* part_ml = part_o + static_cast<size_t>(chunks) * sh.hkv * P * sh.d;
+  const float* part_ml = part_o + static_cast<size_t>(dg.per_head) * sh.hkv * P * sh.d;
   hipLaunchKernelGGL(k_decode_merge<D>, dim3(P, sh.hkv), dim3(kMergeThreads), 0, stream, part_o,
-                     part_ml, pos, B, sh.hq, sh.hkv, sh.group, o);
+                     part_ml, pos, B, sh.hq, sh.hkv, sh.group, dg.spw, o);
   return hipGetLastError();
 }
 }  // namespace

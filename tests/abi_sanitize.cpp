@@ -1,6 +1,7 @@
 // Host-side checks of libkvr's C ABI under AddressSanitizer and
-// UndefinedBehaviorSanitizer.  The library sources are compiled for the host
-// only (no device code) with both sanitizers; this driver calls every entry
+// UndefinedBehaviorSanitizer.  The library sources are compiled with both
+// sanitizers on their host side (the device code is built but never runs
+// here); this driver calls every entry
 // point with arguments that must be rejected before any device work, and a
 // few that reach the HIP runtime (which, without a GPU, reports an error
 // that the library must turn into KVR_ERR_HIP).  Pointers are fake, aligned
@@ -76,7 +77,7 @@ void layer_and_stack() {
   CHECK(layer(nullptr, &w, 4, 4, big, &meta), KVR_ERR_INVALID_ARGUMENT);
   for (int hd : {0, 32, 96, 256}) {
     kvr_config b = cfg(hd);
-    CHECK(layer(&b, &w, 4, 4, big, &meta), hd == 0 ? KVR_ERR_UNSUPPORTED : KVR_ERR_UNSUPPORTED);
+    CHECK(layer(&b, &w, 4, 4, big, &meta), KVR_ERR_UNSUPPORTED);
   }
   {
     kvr_config b = cfg(64, 5, 2);
@@ -256,8 +257,7 @@ void attention_calls() {
         KVR_ERR_INVALID_ARGUMENT);
   CHECK(kvr_biased_attention_noalloc(&c, kv, f, 16384, q, pos, 1, const_cast<float*>(q), nullptr),
         KVR_ERR_INVALID_ARGUMENT);
-  kvr_config wide = cfg(128, 64, 8, 8192, 64, KVR_BF16);
-  CHECK(kvr_biased_attention_noalloc(&wide, kv, f, 32768, q, pos, 8, o, nullptr), KVR_ERR_WORKSPACE);
+  CHECK(kvr_biased_attention_noalloc(&c, kv, f, 16384, q, pos, 64, o, nullptr), KVR_ERR_WORKSPACE);
   CHECK(kvr_biased_attention_noalloc(&c, kv, f, 16384, q, pos, 1, o, nullptr), KVR_ERR_HIP);
 }
 

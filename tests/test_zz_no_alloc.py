@@ -57,18 +57,19 @@ def test_noalloc_matches_workspace_entry_two_calls_shrinking():
 
 def test_noalloc_rejects_shapes_beyond_the_scratch():
     m = kvr()
-    # 8 KV heads, 8 query heads each, B = 8 over N = 32768: 34 MB of decode
-    # partials, more than the static scratch holds
-    N, hkv, d = 32768, 8, 128
-    cfg = m.Config(hidden=8192, n_q_heads=64, n_kv_heads=hkv, head_dim=d, intermediate=64,
-                   alpha=-1.0, beta=-2.0, dtype=m.KVR_BF16)
-    need = m.kvr_attention_workspace_bytes(cfg, 8, N) - 256
+    # 64 query rows of the 7B shape over N = 16384 take the packed attention
+    # path, whose plan, scaled queries and partials need more than the
+    # static scratch holds
+    w = wl.QWEN7_DECODE_16K
+    cfg = cfg_of(w)
+    B, N = 64, w.n_tokens
+    need = m.kvr_attention_workspace_bytes(cfg, B, N) - 256
     assert need > m.KVR_NOALLOC_SCRATCH_BYTES
-    kc = torch.zeros((N, hkv, d), dtype=torch.bfloat16, device="cuda")
+    kc = torch.zeros((N, w.n_kv_heads, w.head_dim), dtype=torch.bfloat16, device="cuda")
     vc = torch.zeros_like(kc)
     flags = torch.zeros(N, dtype=torch.uint8, device="cuda")
-    q = torch.zeros((8, 64, d), dtype=torch.float32, device="cuda")
-    pos = torch.arange(N - 8, N, dtype=torch.int32, device="cuda")
+    q = torch.zeros((B, w.n_q_heads, w.head_dim), dtype=torch.float32, device="cuda")
+    pos = torch.arange(N - B, N, dtype=torch.int32, device="cuda")
     o = torch.empty_like(q)
     with pytest.raises(m.KvrError) as ei:
         m.kvr_biased_attention_noalloc(cfg, kc, vc, flags, q, pos, o)
