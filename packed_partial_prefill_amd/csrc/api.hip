@@ -331,7 +331,7 @@ kvr_status run_biased_attention(const kvr_config* cfg, const kvr::Shape& sh, con
             kvr::launch_attention_decode(q, d_pos, B, n_tokens, cache.k, cache.v, flags, sh,
                                          cfg->alpha, cfg->beta, base + L.attn, o, stream));
     KVR_RUN(KVR_KERNEL_ATTN_MERGE, stream, "decode merge",
-            kvr::launch_attention_decode_merge(d_pos, B, n_tokens, sh, base + L.attn, o, stream));
+            kvr::launch_attention_decode_merge(B, n_tokens, sh, base + L.attn, o, stream));
     return KVR_OK;
   }
   int32_t* n_full = reinterpret_cast<int32_t*>(base + L.n_full);

@@ -1207,6 +1207,19 @@ constexpr int kDecSub = 32;                // keys per wave sub-tile
 constexpr int kDecStep = 4 * kDecSub;      // keys per workgroup step
 constexpr int kDecMaxPairs = 64;
 
+// Global loads the compiler does not know of: the caller waits for them
+// (vmcnt, issue order) and fences their registers before the first use.
+__device__ __forceinline__ u32x4_t untracked_load_b128(const void* p) {
+  u32x4_t r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint32_t untracked_load_b32(const void* p) {
+  uint32_t r;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+
 template <int D>
 struct DecLds {
   static constexpr int kBytes = kDecSub * D * 2;                     // K of one sub-tile
@@ -1254,41 +1267,36 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int P = B * G;
-  const int u_max = pos[B - 1];
-  const int nsteps = u_max / kDecStep + 1;         // steps holding a key 0..u_max
+  // this workgroup's steps [s0, s1max) of the cache (the grid has one per
+  // workgroup, so s0 is a step of the cache); the ones past the last
+  // query's position are dropped once the positions are in
   const int s0 = c * spw;
-  if (s0 >= nsteps) return;                        // every key here is in every pair's future
-  const int s1 = min(nsteps, s0 + spw);
+  const int s1max = min((n_tokens + kDecStep - 1) / kDecStep, s0 + spw);
 
   uint8_t* wbuf = lds + wave * L::wave;            // this wave's two slots
   uint8_t* fbuf = lds + L::kv + wave * 2 * kDecSub;
   float* ml = reinterpret_cast<float*>(lds + L::body);
 
-  // queries of this lane's pair columns
-  float qv[NCB][D / 16][8];
-  int ucol[NCB];
+  // queries of this lane's pair columns and their positions, loaded by
+  // instructions the compiler does not track (its own wait for them would
+  // drain the K/V loads issued after them); they are waited for explicitly,
+  // behind the first sub-tiles, and their registers fenced before use
+  u32x4_t qraw[NCB][D / 16][2];
+  uint32_t uraw[NCB];
+  uint32_t ulast = untracked_load_b32(pos + (B - 1));   // the last query's position
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int p = min(cb * 32 + (lane & 31), P - 1);
     const int r = p / G;
     const int h = g * G + (p - r * G);
-    ucol[cb] = pos[r];
+    uraw[cb] = untracked_load_b32(pos + r);
     const float* qrow = q + (static_cast<size_t>(r) * Hq + h) * D + 8 * half;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const float4 a = *reinterpret_cast<const float4*>(qrow + ks * 16);
-      const float4 b = *reinterpret_cast<const float4*>(qrow + ks * 16 + 4);
-      qv[cb][ks][0] = a.x; qv[cb][ks][1] = a.y; qv[cb][ks][2] = a.z; qv[cb][ks][3] = a.w;
-      qv[cb][ks][4] = b.x; qv[cb][ks][5] = b.y; qv[cb][ks][6] = b.z; qv[cb][ks][7] = b.w;
+      qraw[cb][ks][0] = untracked_load_b128(qrow + ks * 16);
+      qraw[cb][ks][1] = untracked_load_b128(qrow + ks * 16 + 4);
     }
   }
-  bf16x8_t qf[NCB][D / 16];
-#pragma unroll
-  for (int cb = 0; cb < NCB; ++cb)
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) qf[cb][ks][i] = static_cast<__bf16>(qv[cb][ks][i] * q_scale);
 
   // sub-tile j (keys j * kDecStep + wave * kDecSub ..) into slot b: its flag
   // bytes first (lanes 0..31), then K, then V.  Rows past the cache are
@@ -1355,6 +1363,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
 #pragma unroll
       for (int t = 0; t < 16; ++t) o[cb][db][t] = 0.f;
   }
+
+  bf16x8_t qf[NCB][D / 16];                        // scaled queries (set below)
+  int ucol[NCB];                                   // positions of the pair columns
 
   // one sub-tile from slot B; `next`: the following sub-tile is in flight
   // behind it (its K is waited for first, so the scores form while its V
@@ -1446,11 +1457,46 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
   };
 
   // the ring: sub-tile j in slot (j - s0) & 1; before a slot is refilled its
-  // reads are complete (lds_wait in consume, then the compiler barrier)
+  // reads are complete (lds_wait in consume, then the compiler barrier).
+  // The first two sub-tiles go out before the positions are known (they are
+  // inside the cache whatever the positions say); s_hi bounds the sub-tiles
+  // in flight, which can pass s1 when the last query sits early in the cache.
   issue(s0, 0);
-  if (s0 + 1 < s1) issue(s0 + 1, 1);
+  if (s0 + 1 < s1max) issue(s0 + 1, 1);
+  const int s_hi = min(s0 + 2, s1max);
+  // the queries and positions were issued before the sub-tiles in flight
+  if (s_hi - s0 == 2) attn_wait_vmcnt<2 * kIssued>(); else attn_wait_vmcnt<kIssued>();
+  reg_fence(ulast);
+  const int nsteps = __builtin_amdgcn_readfirstlane(static_cast<int>(ulast)) / kDecStep + 1;
+  if (s0 >= nsteps) {
+    // every key here is in every pair's future: an empty partial (maximum
+    // -inf, sum 0; the merge reads no O of it), and no DMA may land after
+    // the exit
+    const size_t slot0 = (static_cast<size_t>(c) * Hkv + g) * P;
+    for (int p = tid; p < P; p += kAttnThreads) {
+      part_ml[(slot0 + p) * 2] = -INFINITY;
+      part_ml[(slot0 + p) * 2 + 1] = 0.f;
+    }
+    attn_wait_vmcnt<0>();
+    return;
+  }
+  const int s1 = min(nsteps, s1max);               // steps holding a key 0..u_max
+  const int s_end = max(s1, s_hi);
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    reg_fence(uraw[cb]);
+    ucol[cb] = static_cast<int>(uraw[cb]);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      reg_fence(qraw[cb][ks][0]);
+      reg_fence(qraw[cb][ks][1]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        qf[cb][ks][i] = static_cast<__bf16>(__uint_as_float(qraw[cb][ks][i >> 2][i & 3]) * q_scale);
+    }
+  }
   for (int j = s0; j < s1; j += 2) {
-    consume(std::integral_constant<int, 0>{}, j, j + 1 < s1);
+    consume(std::integral_constant<int, 0>{}, j, j + 1 < s_end);
     asm volatile("" ::: "memory");
     if (j + 2 < s1) issue(j + 2, 0);
     if (j + 1 < s1) {
@@ -1514,40 +1560,53 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
   }
 }
 
-// Combines the workgroup partials of one (pair, KV head).  1024 threads:
-// thread (d, sg) takes the partials sg, sg + SG, ... (SG = 1024 / D groups)
-// with a running maximum, so all of a thread's loads are independent of one
-// another and in flight together (one pass over the partials); the groups
-// are then combined through LDS by the D threads of group 0.
+// Combines the workgroup partials of one (pair, KV head): every workgroup
+// of the decode grid wrote one (those past the last query's position an
+// empty one), so the count comes from the grid and no position is read.
+// 1024 threads: thread (d, sg) takes the partials sg, sg + SG, ... (SG =
+// 1024 / D groups), kChunk of them per round with their loads in flight
+// together (index clamped, weight zeroed past the last) and a running
+// maximum; the groups are then combined through LDS by group 0.
 constexpr int kMergeThreads = 1024;
 
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void k_decode_merge(
-    const float* __restrict__ part_o, const float* __restrict__ part_ml,
-    const int32_t* __restrict__ pos, int B, int Hq, int Hkv, int G, int spw,
-    float* __restrict__ o) {
+    const float* __restrict__ part_o, const float* __restrict__ part_ml, int ns, int Hq, int Hkv,
+    int G, int P, float* __restrict__ o) {
   constexpr int SG = kMergeThreads / D;
+  constexpr int kChunk = 8;
   __shared__ float red_m[kMergeThreads];
   __shared__ float red_l[kMergeThreads];
   __shared__ float red_o[kMergeThreads];
   const int p = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-  const int P = B * G;
-  const int nsteps = pos[B - 1] / kDecStep + 1;
-  const int ns = (nsteps + spw - 1) / spw;         // workgroups that wrote partials
   const size_t stride = static_cast<size_t>(Hkv) * P;   // slots between workgroups
   const size_t slot0 = static_cast<size_t>(g) * P + p;
   const int d = tid % D, sg = tid / D;
   float m = -INFINITY, l = 0.f, acc = 0.f;
-#pragma unroll 4
-  for (int s = sg; s < ns; s += SG) {
-    const size_t slot = slot0 + s * stride;
-    const float ms = part_ml[slot * 2], ls = part_ml[slot * 2 + 1], ov = part_o[slot * D + d];
-    const float mn = fmaxf(m, ms);
+  for (int s = sg; s < ns; s += SG * kChunk) {
+    float ms[kChunk], ls[kChunk], ov[kChunk];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const size_t slot = slot0 + static_cast<size_t>(min(s + k * SG, ns - 1)) * stride;
+      ms[k] = s + k * SG < ns ? part_ml[slot * 2] : -INFINITY;
+      ls[k] = part_ml[slot * 2 + 1];
+      ov[k] = part_o[slot * D + d];
+    }
+    float mn = m;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) mn = fmaxf(mn, ms[k]);
     const bool none = mn == -INFINITY;
     const float a = none ? 0.f : fast_exp2(m - mn);    // rescale of the sums so far
-    const float b = none ? 0.f : fast_exp2(ms - mn);   // 0 for a partial that saw no key
-    l = l * a + b * ls;
-    acc = acc * a + b * ov;
+    l *= a;
+    acc *= a;
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      // an empty partial adds nothing (its O is not read as a number)
+      const bool empty = ms[k] == -INFINITY;
+      const float b = empty ? 0.f : fast_exp2(ms[k] - mn);
+      l += b * ls[k];
+      acc += empty ? 0.f : b * ov[k];
+    }
     m = mn;
   }
   red_m[tid] = m;
@@ -1735,23 +1794,22 @@ hipError_t launch_decode_t(const float* q, const int32_t* pos, int B, int n_toke
 }
 
 template <int D>
-hipError_t launch_decode_merge_t(const int32_t* pos, int B, int n_tokens, const Shape& sh,
-                                 void* ws, float* o, hipStream_t stream) {
+hipError_t launch_decode_merge_t(int B, int n_tokens, const Shape& sh, void* ws, float* o,
+                                 hipStream_t stream) {
   const DecGrid dg = decode_grid(n_tokens, sh);
   const int P = B * sh.group;
   const float* part_o = static_cast<const float*>(ws);
   const float* part_ml = part_o + static_cast<size_t>(dg.per_head) * sh.hkv * P * sh.d;
   hipLaunchKernelGGL(k_decode_merge<D>, dim3(P, sh.hkv), dim3(kMergeThreads), 0, stream, part_o,
-                     part_ml, pos, B, sh.hq, sh.hkv, sh.group, dg.spw, o);
+                     part_ml, dg.per_head, sh.hq, sh.hkv, sh.group, P, o);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_attention_decode_merge(const int32_t* pos, int B, int n_tokens,
-                                         const Shape& sh, void* ws, float* o,
-                                         hipStream_t stream) {
-  if (sh.d == 128) return launch_decode_merge_t<128>(pos, B, n_tokens, sh, ws, o, stream);
-  return launch_decode_merge_t<64>(pos, B, n_tokens, sh, ws, o, stream);
+hipError_t launch_attention_decode_merge(int B, int n_tokens, const Shape& sh, void* ws,
+                                         float* o, hipStream_t stream) {
+  if (sh.d == 128) return launch_decode_merge_t<128>(B, n_tokens, sh, ws, o, stream);
+  return launch_decode_merge_t<64>(B, n_tokens, sh, ws, o, stream);
 }
 
 hipError_t launch_attention_decode(const float* q, const int32_t* pos, int B, int n_tokens,

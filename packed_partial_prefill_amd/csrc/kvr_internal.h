@@ -132,9 +132,8 @@ hipError_t launch_attention_decode(const float* q, const int32_t* pos, int B, in
                                    const void* k_cache, const void* v_cache,
                                    const uint8_t* flags, const Shape& sh, float alpha, float beta,
                                    void* ws, float* o, hipStream_t stream);
-hipError_t launch_attention_decode_merge(const int32_t* pos, int B, int n_tokens,
-                                         const Shape& sh, void* ws, float* o,
-                                         hipStream_t stream);
+hipError_t launch_attention_decode_merge(int B, int n_tokens, const Shape& sh, void* ws,
+                                         float* o, hipStream_t stream);
 // o_out: [B, Hq, d] in bf16, or float32 when out_f32.
 hipError_t launch_attention_merge(kvr_dtype dt, int B, int n_tokens, const Shape& sh,
                                   const int32_t* plan_n_total, void* ws, void* o_out,
