@@ -178,6 +178,20 @@ kvr_status kvr_check_support(const int32_t* d_T, int32_t B, int32_t n_tokens,
                              int32_t* d_result, hipStream_t stream);
 
 /*
+ * Validation mode.  With KVR_VALIDATE set in the environment to anything but
+ * "0" (read on every call), kvr_layer_repair and kvr_stack_repair run this
+ * check on d_T over [0, n_tokens) together with meta->gpos, and
+ * kvr_biased_attention / kvr_biased_attention_noalloc run it on d_pos, on
+ * the device before any other launch (the result word lives in the
+ * workspace or scratch).  A bad support then returns KVR_ERR_BAD_SUPPORT (a
+ * bad position map KVR_ERR_INVALID_ARGUMENT) with the cache, flags and
+ * outputs untouched.  The check synchronises the stream, so calls made in
+ * validation mode cannot be captured into a HIP graph.  Off by default:
+ * callers that build their supports with kvr_build_repair_set,
+ * kvr_build_runs or kvr_sur_select already hold checked supports.
+ */
+
+/*
  * kvr_build_runs - checks an explicit support like kvr_check_support and
  * coalesces it into its maximal runs of consecutive positions, the execution
  * intervals that Budgeted KV-Cache Repair sorts and coalesces a support into
@@ -235,7 +249,7 @@ size_t kvr_workspace_bytes(const kvr_config* cfg, int32_t B, int32_t n_tokens);
  *   n2 = RMSNorm(h1) * mlp_norm.
  *
  *   d_T        device int32 [B], strictly increasing, in [0, N) (checked by
- *              kvr_check_support, not here).
+ *              kvr_check_support, or here in validation mode).
  *   x_in       device float32 [x_in_rows, hidden]: x_in_rows == B means the
  *              rows are already packed in the order of T; x_in_rows ==
  *              meta->n_tokens means row r is gathered from x_in[T[r]].

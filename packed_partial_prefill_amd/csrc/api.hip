@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <cstdlib>
 #include <mutex>
 #include <vector>
 
@@ -195,6 +196,37 @@ kvr_status check_weights(const kvr_layer_weights& w, int layer) {
   return KVR_OK;
 }
 
+// The device-side support check of kvr_check_support (also run first by the
+// repair and attention entries in validation mode): launch, copy the result
+// word back, synchronise, map it to a status.
+kvr_status check_support_sync(const int32_t* d_T, int B, int n_tokens, int first_selectable,
+                              const int32_t* d_gpos, int32_t* d_result, hipStream_t stream) {
+  hipError_t e = kvr::launch_check_support(d_T, B, n_tokens, first_selectable, d_gpos, d_result,
+                                           stream);
+  if (e != hipSuccess) return hip_fail(e, "check support");
+  int32_t h = 0;
+  e = hipMemcpyAsync(&h, d_result, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e != hipSuccess) return hip_fail(e, "copy result");
+  e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "synchronize");
+  if (h == KVR_ERR_BAD_SUPPORT)
+    return fail(KVR_ERR_BAD_SUPPORT, "support not strictly increasing or outside [%d, %d)",
+                first_selectable, n_tokens);
+  if (h != KVR_OK)
+    return fail(KVR_ERR_INVALID_ARGUMENT,
+                "global position map not non-negative and strictly increasing");
+  return KVR_OK;
+}
+
+// Validation mode: KVR_VALIDATE set in the environment to anything but "0"
+// (read on every call).  The repair and attention entries then check their
+// support (and position map) on the device before any other launch, which
+// synchronises the stream, and return the check's error instead of running.
+bool validate_mode() {
+  const char* v = std::getenv("KVR_VALIDATE");
+  return v && v[0] && !(v[0] == '0' && v[1] == '\0');
+}
+
 kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weights* w,
                      const kvr_kv* caches, const kvr_meta* meta, const int32_t* d_T, int B,
                      const float* x_in, int x_in_rows, float* x_out, void* ws, size_t ws_bytes,
@@ -229,6 +261,11 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
   const size_t slack = static_cast<size_t>(base - static_cast<uint8_t*>(ws));
   if (ws_bytes < L.total + slack)
     return fail(KVR_ERR_WORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, L.total + slack);
+  // (the result word borrows the plan's first slot, written after the check)
+  if (validate_mode() &&
+      (st = check_support_sync(d_T, B, N, 0, meta->gpos, reinterpret_cast<int32_t*>(base + L.n_full),
+                               stream)) != KVR_OK)
+    return st;
 
   const kvr_dtype dt = cfg->dtype;
   float2* tab = reinterpret_cast<float2*>(base + L.tab);
@@ -325,6 +362,13 @@ kvr_status run_biased_attention(const kvr_config* cfg, const kvr::Shape& sh, con
                                 const float* q, const int32_t* d_pos, int B, float* o,
                                 uint8_t* base, hipStream_t stream) {
   const kvr_dtype dt = cfg->dtype;
+  // (the result word borrows the first word of the workspace, written after
+  // the check)
+  kvr_status st;
+  if (validate_mode() &&
+      (st = check_support_sync(d_pos, B, n_tokens, 0, nullptr, reinterpret_cast<int32_t*>(base),
+                               stream)) != KVR_OK)
+    return st;
   if (kvr::decode_supported(dt, B, sh)) {
     // decode sizes: one streaming pass over the cache plus a chunk merge
     KVR_RUN(KVR_KERNEL_ATTN, stream, "decode attention",
@@ -440,22 +484,9 @@ kvr_status kvr_check_support(const int32_t* d_T, int32_t B, int32_t n_tokens,
     return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d, n_tokens=%d", B, n_tokens);
   if (!dev_ok(d_result) || (B > 0 && !dev_ok(d_T)) || (d_gpos && !aligned16(d_gpos)))
     return fail(KVR_ERR_INVALID_ARGUMENT, "d_T / d_gpos / d_result NULL or misaligned");
-  hipError_t e = kvr::launch_check_support(d_T, B, n_tokens, first_selectable, d_gpos, d_result,
-                                           stream);
-  if (e != hipSuccess) return hip_fail(e, "check support");
-  int32_t h = 0;
-  e = hipMemcpyAsync(&h, d_result, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
-  if (e != hipSuccess) return hip_fail(e, "copy result");
-  e = hipStreamSynchronize(stream);
-  if (e != hipSuccess) return hip_fail(e, "synchronize");
-  if (h == KVR_ERR_BAD_SUPPORT)
-    return fail(KVR_ERR_BAD_SUPPORT, "support not strictly increasing or outside [%d, %d)",
-                first_selectable, n_tokens);
-  if (h != KVR_OK)
-    return fail(KVR_ERR_INVALID_ARGUMENT,
-                "global position map not non-negative and strictly increasing");
-  return KVR_OK;
+  return check_support_sync(d_T, B, n_tokens, first_selectable, d_gpos, d_result, stream);
 }
+
 
 kvr_status kvr_build_runs(const int32_t* d_T, int32_t B, int32_t n_tokens,
                           int32_t first_selectable, const kvr_repair_set* out,
