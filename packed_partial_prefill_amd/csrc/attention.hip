@@ -123,6 +123,19 @@ template <int N> __device__ __forceinline__ void attn_wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0xF70);
 }
 
+// Global loads the compiler does not know of: the caller waits for them
+// (vmcnt, issue order) and fences their registers before the first use.
+__device__ __forceinline__ u32x4_t untracked_load_b128(const void* p) {
+  u32x4_t r;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+__device__ __forceinline__ uint32_t untracked_load_b32(const void* p) {
+  uint32_t r;
+  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
+  return r;
+}
+
 template <int D>
 struct AttnLds {
   static constexpr int kBytes = kKvTile * D * 2;   // K tile
@@ -989,13 +1002,20 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     const int pc = min(p, P - 1);
     const int r = pc / G;
     const int h = g * G + (pc - r * G);
-    u = Tpos[r];
+    // The query fragments and the position are loaded by instructions the
+    // compiler does not track, ahead of the piece's first tile, and fenced
+    // after that tile's wait (which they precede in issue order).  With
+    // plain loads the compiler waited for them inside every tile's score
+    // products (it cannot see that they completed in the first tile), and
+    // its count there also held wave 0 on the flag bytes of the tile it
+    // had just issued.
+    uint32_t uraw = untracked_load_b32(Tpos + r);
     {
       const bf16_t* qrow = q + (static_cast<size_t>(r) * Hq + h) * D + 8 * half;
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) qf[ks] = *reinterpret_cast<const bf16x8_t*>(qrow + ks * 16);
+      for (int ks = 0; ks < D / 16; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8_t, untracked_load_b128(qrow + ks * 16));
     }
-    // (the query loads complete with the first tile's wait below)
     if (c0 == 0 && wave == 0 && lane == 0) {
       // the merge's view of this segment: its first workgroup and piece count
       const long long last = tile0 + len - 1;
@@ -1021,6 +1041,10 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     issue(c0, b0);
     if (n > 1) issue(c0 + 1, (b0 + 1) % kPPStages);
     wait_tile(n > 1);
+    reg_fence(uraw);
+    u = static_cast<int>(uraw);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) reg_fence(qf[ks]);
     lds_barrier();
     if (grp == 1) {
       if (n > 2) issue(c0 + 2, (b0 + 2) % kPPStages);
@@ -1206,19 +1230,6 @@ __global__ __launch_bounds__(kAttnThreads) void k_attn_merge(
 constexpr int kDecSub = 32;                // keys per wave sub-tile
 constexpr int kDecStep = 4 * kDecSub;      // keys per workgroup step
 constexpr int kDecMaxPairs = 64;
-
-// Global loads the compiler does not know of: the caller waits for them
-// (vmcnt, issue order) and fences their registers before the first use.
-__device__ __forceinline__ u32x4_t untracked_load_b128(const void* p) {
-  u32x4_t r;
-  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
-__device__ __forceinline__ uint32_t untracked_load_b32(const void* p) {
-  uint32_t r;
-  asm volatile("global_load_dword %0, %1, off" : "=v"(r) : "v"(p) : "memory");
-  return r;
-}
 
 template <int D>
 struct DecLds {

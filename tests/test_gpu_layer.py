@@ -178,7 +178,7 @@ def test_qwen7_layer_16k_contiguous():
 
 @pytest.mark.timeout(600)
 def test_qwen7_layer_16k_matched():
-    run_layer_case(wl.QWEN7_LAYER_MATCHED, check_rows=128)
+    run_layer_case(wl.QWEN7_LAYER_MATCHED)
 
 
 @pytest.mark.timeout(600)
