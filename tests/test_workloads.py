@@ -8,7 +8,7 @@ import workloads as wl
 
 def test_table18_supports_match_the_stated_pair_counts():
     # Budgeted KV-Cache Repair, section 13.3: B = 64, R = 1/4/16, and the
-    # causal pair count sum(u+1) is 65,568 at 2K and 262,176 at 8K.
+    # causal pair count sum(u+1): 65568 for the 2K cache, 262176 for the 8K one.
     for w in wl.TABLE18:
         T = wl.explicit_support(w)
         assert len(T) == 64
