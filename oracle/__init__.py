@@ -33,7 +33,8 @@ the function that takes it; every function here is pinned by tests under
 ``tests/`` (no function is parity-unpinned).
 """
 from .repair_set import (BadBlocks, BadSupport, attn_tile_plan, budget, check_positions,
-                         check_support, initial_meta, runs, seam_set, validate_blocks)
+                         check_support, initial_meta, kv_tile_first_query, runs, seam_set,
+                         validate_blocks)
 from .layer import (FLAG_LOCAL, FLAG_SINK, attention_bias, biased_attention_row,
                     interval_major, layer_repair, rms_norm, rope, silu, stack_repair,
                     write_back_flags)
@@ -42,7 +43,8 @@ from . import sur
 
 __all__ = [
     "BadBlocks", "BadSupport", "attn_tile_plan", "budget", "check_positions",
-    "check_support", "initial_meta", "runs", "seam_set", "validate_blocks", "FLAG_LOCAL",
+    "check_support", "initial_meta", "kv_tile_first_query", "runs", "seam_set",
+    "validate_blocks", "FLAG_LOCAL",
     "FLAG_SINK", "attention_bias", "biased_attention_row", "interval_major", "layer_repair",
     "rms_norm", "rope", "silu", "stack_repair", "write_back_flags", "inference_attention",
     "shift_cache", "sur",

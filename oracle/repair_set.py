@@ -101,6 +101,24 @@ def check_support(T: Sequence[int], n_tokens: int, first_selectable: int, B: int
             raise BadSupport("support is not strictly increasing")
 
 
+def kv_tile_first_query(T: Sequence[int], n_tokens: int, kv_tile: int) -> np.ndarray:
+    """Key-tile-major view of the plan: for each key tile c (keys
+    [c*W, (c+1)*W) of an n_tokens cache), the index of the first packed row r
+    whose position T[r] is at or after the tile's first key -- the first
+    query of a sorted support that sees any key of the tile (every later row
+    sees it too) -- or len(T) when no row reaches the tile.
+
+    This is the inverse of the query-tile plan of Budgeted KV-Cache Repair,
+    section 13.2 (Eq. 24): a query tile touches key tile c exactly when its
+    last row index is at or past first[c].  The index is a left insertion
+    point of c*W into the sorted support (a library search serves as the
+    step).
+    """
+    T = np.asarray(T, dtype=np.int64)
+    n_kv = -(-int(n_tokens) // kv_tile)
+    return np.searchsorted(T, np.arange(n_kv, dtype=np.int64) * kv_tile, side="left").astype(np.int64)
+
+
 def attn_tile_plan(T: Sequence[int], group: int, rows_per_tile: int,
                    kv_tile: int) -> Tuple[np.ndarray, np.ndarray]:
     """Per-query-tile key-tile counts (Budgeted KV-Cache Repair, section 13.2,

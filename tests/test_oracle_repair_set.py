@@ -192,3 +192,35 @@ def test_tile_plan_brute_force_counting():
             full = sum(1 for c in range(N // W + 2) if (c + 1) * W - 1 <= min(us))
             touched = sum(1 for c in range(N // W + 2) if c * W <= max(us))
             assert n_full[t] == full and n_total[t] == touched
+
+
+def test_kv_tile_first_query_brute_force_and_plan_inverse():
+    """The key-tile map against a per-tile scan of the support, and against
+    Eq. 24's n_total: query tile t touches key tile c iff its last row is at
+    or past first[c]."""
+    rng = np.random.default_rng(12)
+    for _ in range(200):
+        N = int(rng.integers(1, 900))
+        B = int(rng.integers(0, min(N, 120) + 1))
+        T = np.sort(rng.choice(N, size=B, replace=False))
+        W = int(rng.choice([16, 64]))
+        first = oracle.kv_tile_first_query(T, N, W)
+        assert len(first) == -(-N // W)
+        for c in range(len(first)):
+            scan = next((r for r in range(B) if T[r] >= c * W), B)
+            assert first[c] == scan
+        if B == 0:
+            continue
+        G = int(rng.integers(1, 8))
+        rows = int(rng.choice([16, 32, 128]))
+        _, n_total = oracle.attn_tile_plan(T, G, rows, W)
+        for t in range(len(n_total)):
+            last_row = (min(B * G, (t + 1) * rows) - 1) // G
+            for c in range(len(first)):
+                assert (c < n_total[t]) == (last_row >= first[c])
+
+
+def test_kv_tile_first_query_edges():
+    assert list(oracle.kv_tile_first_query([], 130, 64)) == [0, 0, 0]
+    assert list(oracle.kv_tile_first_query([0, 63, 64, 200], 256, 64)) == [0, 2, 3, 3]
+    assert list(oracle.kv_tile_first_query([5], 64, 64)) == [0]
