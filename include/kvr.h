@@ -228,6 +228,26 @@ kvr_status kvr_build_runs(const int32_t* d_T, int32_t B, int32_t n_tokens,
 kvr_status kvr_build_plan(const int32_t* d_T, int32_t B, int32_t group, int32_t* d_n_full,
                           int32_t* d_n_total, hipStream_t stream);
 
+/*
+ * kvr_build_tile_map - the key-tile-major view of the same plan: for each
+ * KV_TILE-key tile c of an n_tokens cache, d_first_q[c] is the index of the
+ * first packed row r whose position d_T[r] is at or after the tile's first
+ * key, i.e. the first query of the sorted support that sees any key of the
+ * tile (every later row sees it too), or B when no row reaches the tile.
+ * It inverts Eq. 24 (Budgeted KV-Cache Repair, section 13.2): query tile t
+ * touches key tile c exactly when its last row index is >= d_first_q[c].
+ * The attention kernels walk query tiles with n_full / n_total; this table
+ * serves a traversal by key tile and inspection.
+ *
+ *   d_T        device int32 [B], strictly increasing (checked by
+ *              kvr_check_support, not here); may be NULL when B = 0.
+ *   d_first_q  device int32 [ceil(n_tokens / KV_TILE)].
+ * Errors (before any device work): n_tokens < 1, B < 0 or B > n_tokens,
+ * NULL or misaligned pointers -> INVALID_ARGUMENT.  Does not synchronise.
+ */
+kvr_status kvr_build_tile_map(const int32_t* d_T, int32_t B, int32_t n_tokens,
+                              int32_t* d_first_q, hipStream_t stream);
+
 /* Workspace bytes needed by kvr_layer_repair / kvr_stack_repair for this
  * shape, support size B and context length; 0 on invalid arguments. */
 size_t kvr_workspace_bytes(const kvr_config* cfg, int32_t B, int32_t n_tokens);

@@ -78,6 +78,7 @@ _sigs = {
     "kvr_check_support": (C.c_int, [_P, _I, _I, _I, _P, _P, _P]),
     "kvr_build_runs": (C.c_int, [_P, _I, _I, _I, C.POINTER(kvr_repair_set), _P, _P]),
     "kvr_build_plan": (C.c_int, [_P, _I, _I, _P, _P, _P]),
+    "kvr_build_tile_map": (C.c_int, [_P, _I, _I, _P, _P]),
     "kvr_workspace_bytes": (C.c_size_t, [C.POINTER(kvr_config), _I, _I]),
     "kvr_layer_repair": (C.c_int, [C.POINTER(kvr_config), C.POINTER(kvr_layer_weights), kvr_kv,
                                    C.POINTER(kvr_meta), _P, _I, _P, _I, _P, _P, C.c_size_t, _P]),
@@ -198,6 +199,11 @@ def kvr_build_runs(d_T, n_tokens: int, first_selectable: int, run_start, run_len
 def kvr_build_plan(d_T, group: int, d_n_full, d_n_total, stream=None) -> None:
     _check(_lib.kvr_build_plan(_ptr(d_T), d_T.numel(), group, _ptr(d_n_full), _ptr(d_n_total),
                                _stream(stream)))
+
+
+def kvr_build_tile_map(d_T, n_tokens: int, d_first_q, stream=None) -> None:
+    _check(_lib.kvr_build_tile_map(_ptr(d_T), d_T.numel(), n_tokens, _ptr(d_first_q),
+                                   _stream(stream)))
 
 
 def kvr_workspace_bytes(cfg: Config, B: int, n_tokens: int) -> int:

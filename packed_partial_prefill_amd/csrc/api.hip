@@ -512,6 +512,18 @@ kvr_status kvr_build_runs(const int32_t* d_T, int32_t B, int32_t n_tokens,
   return KVR_OK;
 }
 
+kvr_status kvr_build_tile_map(const int32_t* d_T, int32_t B, int32_t n_tokens,
+                              int32_t* d_first_q, hipStream_t stream) {
+  g_err[0] = '\0';
+  if (n_tokens < 1 || B < 0 || B > n_tokens)
+    return fail(KVR_ERR_INVALID_ARGUMENT, "B=%d, n_tokens=%d", B, n_tokens);
+  if (!dev_ok(d_first_q) || (B > 0 && !dev_ok(d_T)))
+    return fail(KVR_ERR_INVALID_ARGUMENT, "d_T / d_first_q NULL or misaligned");
+  hipError_t e = kvr::launch_tile_map(d_T, B, n_tokens, d_first_q, stream);
+  if (e != hipSuccess) return hip_fail(e, "tile map");
+  return KVR_OK;
+}
+
 kvr_status kvr_build_plan(const int32_t* d_T, int32_t B, int32_t group, int32_t* d_n_full,
                           int32_t* d_n_total, hipStream_t stream) {
   g_err[0] = '\0';

@@ -279,6 +279,21 @@ __global__ void k_build_plan(const int32_t* __restrict__ T, int B, int group, in
   if (t < n_tiles) plan_entry(T, B, group, t, n_full, n_total);
 }
 
+// Key tile c's first packed row: the left insertion point of c * KV_TILE
+// into the sorted support (one thread per key tile, binary search).
+__global__ void k_tile_map(const int32_t* __restrict__ T, int B, int n_kv,
+                           int32_t* __restrict__ first_q) {
+  const int c = blockIdx.x * blockDim.x + threadIdx.x;
+  if (c >= n_kv) return;
+  const long long key0 = static_cast<long long>(c) * KVR_ATTN_KV_TILE;
+  int lo = 0, hi = B;   // first r in [lo, hi) with T[r] >= key0
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (T[mid] < key0) lo = mid + 1; else hi = mid;
+  }
+  first_q[c] = lo;
+}
+
 // Both tables of a layer call in one launch: plan entries first, then the
 // rope table.
 __global__ void k_layer_tables(const int32_t* __restrict__ T, const int32_t* __restrict__ gpos,
@@ -335,6 +350,15 @@ hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full
   if (nt == 0) return hipSuccess;
   hipLaunchKernelGGL(k_build_plan, dim3((nt + 255) / 256), dim3(256), 0, stream, T, B, group, nt,
                      n_full, n_total);
+  return hipGetLastError();
+}
+
+hipError_t launch_tile_map(const int32_t* T, int B, int n_tokens, int32_t* first_q,
+                           hipStream_t stream) {
+  const int n_kv = (n_tokens + KVR_ATTN_KV_TILE - 1) / KVR_ATTN_KV_TILE;
+  if (n_kv == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_tile_map, dim3((n_kv + 255) / 256), dim3(256), 0, stream, T, B, n_kv,
+                     first_q);
   return hipGetLastError();
 }
 

@@ -29,6 +29,9 @@ hipError_t launch_build_runs(const int32_t* T, int B, int n_tokens, int first,
                              int32_t* run_start, int32_t* run_len, int32_t* counts,
                              hipStream_t stream);
 int plan_tiles(int B, int group);
+// first_q[c] (c < ceil(n_tokens / KV_TILE)): first row r with T[r] >= c * KV_TILE.
+hipError_t launch_tile_map(const int32_t* T, int B, int n_tokens, int32_t* first_q,
+                           hipStream_t stream);
 hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full,
                              int32_t* n_total, hipStream_t stream);
 // launch_build_plan plus the RoPE table (cos, sin of g_r * theta^(-2i/d) as

@@ -227,6 +227,10 @@ void index_calls() {
   CHECK(kvr_build_plan(fk<int32_t>(), 0, 7, fk<int32_t>(0x40), fk<int32_t>(0x80), nullptr), KVR_OK);
   CHECK(kvr_build_plan(fk<int32_t>(), 4, 7, nullptr, fk<int32_t>(0x80), nullptr),
         KVR_ERR_INVALID_ARGUMENT);
+  CHECK(kvr_build_tile_map(fk<int32_t>(), 5, 4, fk<int32_t>(0x40), nullptr), KVR_ERR_INVALID_ARGUMENT);
+  CHECK(kvr_build_tile_map(fk<int32_t>(), 0, 0, fk<int32_t>(0x40), nullptr), KVR_ERR_INVALID_ARGUMENT);
+  CHECK(kvr_build_tile_map(fk<int32_t>(), 3, 40, nullptr, nullptr), KVR_ERR_INVALID_ARGUMENT);
+  CHECK(kvr_build_tile_map(fk<int32_t>(4), 3, 40, fk<int32_t>(0x40), nullptr), KVR_ERR_INVALID_ARGUMENT);
 }
 
 void attention_calls() {

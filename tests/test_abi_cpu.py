@@ -23,7 +23,7 @@ def test_header_declares_the_entry_points():
     for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
               "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
               "kvr_attention_workspace_bytes", "kvr_biased_attention", "kvr_shift_cache",
-              "kvr_sur_scores", "kvr_sur_select", "kvr_build_runs",
+              "kvr_sur_scores", "kvr_sur_select", "kvr_build_runs", "kvr_build_tile_map",
               "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
         assert n in names
 
@@ -127,6 +127,10 @@ def test_check_support_and_plan_host_validation(kvr):
     assert lib.kvr_check_support(FAKE, 1, 4, 0, FAKE + 4, FAKE, None) == -1  # misaligned gpos
     assert lib.kvr_build_plan(FAKE, 4, 0, FAKE, FAKE, None) == -1
     assert lib.kvr_build_plan(FAKE, 0, 7, FAKE, FAKE, None) == 0
+    assert lib.kvr_build_tile_map(FAKE, 5, 4, FAKE, None) == -1             # B > N
+    assert lib.kvr_build_tile_map(FAKE, 0, 0, FAKE, None) == -1             # empty cache
+    assert lib.kvr_build_tile_map(FAKE, 3, 40, None, None) == -1            # no output
+    assert lib.kvr_build_tile_map(FAKE + 4, 3, 40, FAKE, None) == -1        # misaligned T
 
 
 def test_build_runs_host_validation(kvr):
@@ -151,7 +155,7 @@ def test_python_binding_has_the_c_names(kvr):
     for n in ("kvr_build_repair_set", "kvr_check_support", "kvr_build_plan",
               "kvr_workspace_bytes", "kvr_layer_repair", "kvr_stack_repair",
               "kvr_attention_workspace_bytes", "kvr_biased_attention", "kvr_shift_cache",
-              "kvr_sur_scores", "kvr_sur_select", "kvr_build_runs",
+              "kvr_sur_scores", "kvr_sur_select", "kvr_build_runs", "kvr_build_tile_map",
               "kvr_status_string", "kvr_last_error", "kvr_timing_begin", "kvr_timing_end"):
         assert callable(getattr(kvr, n))
 

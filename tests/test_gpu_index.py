@@ -116,6 +116,28 @@ def test_plan_matches_oracle():
         assert np.array_equal(nf.cpu().numpy(), rf) and np.array_equal(ntot.cpu().numpy(), rt)
 
 
+def test_tile_map_matches_oracle():
+    """The key-tile map of random, workload and edge supports, bit-exact."""
+    m = kvr()
+    rng = np.random.default_rng(22)
+    cases = []
+    for _ in range(30):
+        N = int(rng.integers(1, 40000))
+        B = int(rng.integers(1, min(N, 3000) + 1))
+        cases.append((np.sort(rng.choice(N, size=B, replace=False)).astype(np.int32), N))
+    for w in (wl.QWEN7_STACK_ISOLATED, wl.QWEN7_LAYER_MATCHED, *wl.TABLE18):
+        cases.append((wl.explicit_support(w).astype(np.int32), w.n_tokens))
+    cases += [(np.arange(0, 64, dtype=np.int32), 100),        # every row in the first tile
+              (np.array([99], dtype=np.int32), 100),           # the last position only
+              (np.zeros(0, dtype=np.int32), 130)]              # empty support
+    for T, N in cases:
+        n_kv = -(-N // m.KVR_ATTN_KV_TILE)
+        out = torch.full((n_kv,), -7, dtype=torch.int32, device="cuda")
+        m.kvr_build_tile_map(torch.from_numpy(T).cuda(), N, out)
+        ref = oracle.kv_tile_first_query(T, N, m.KVR_ATTN_KV_TILE)
+        assert np.array_equal(out.cpu().numpy(), ref), (len(T), N)
+
+
 def test_seam_set_with_more_runs_than_the_lds_holds():
     """40,000 positions in blocks of 4 with tau = 1: about 10,000 runs, so the
     run lengths are fixed up from global memory instead of LDS."""
