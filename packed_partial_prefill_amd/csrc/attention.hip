@@ -1422,19 +1422,27 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
         mt = fmaxf(mt, sc[cb][t]);
       }
       mt = xor32_max(mt);
-      // running maximum (branch-free: a column may have seen no key yet)
-      const float mn = fmaxf(m[cb], mt);
-      const bool none = mn == -INFINITY;
-      const float corr = none ? 1.f : fast_exp2(m[cb] - mn);   // 0 while nothing was seen
-      m[cb] = mn;
-      l[cb] *= corr;
+      // Lazy running maximum: m moves only when the sub-tile exceeds it by
+      // more than 8 (log2 units) or holds the column's first visible key,
+      // so the weights stay below 2^8 and most sub-tiles leave O unscaled
+      // (with two column blocks O lives in accumulation registers, where a
+      // rescale reads, multiplies and writes back every element).  A column
+      // that has seen no key yet keeps m = -inf and weight 0.
+      const bool bump = mt > m[cb] + 8.f || (m[cb] == -INFINITY && mt != -INFINITY);
+      if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+        const float mn = bump ? mt : m[cb];
+        const float corr = m[cb] == -INFINITY ? 0.f : fast_exp2(m[cb] - mn);   // 1 if not bumped
+        m[cb] = mn;
+        l[cb] *= corr;
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int t = 0; t < 16; ++t) o[cb][db][t] *= corr;
+          for (int t = 0; t < 16; ++t) o[cb][db][t] *= corr;
+      }
+      const bool none = m[cb] == -INFINITY;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        const float e = none ? 0.f : fast_exp2(sc[cb][t] - mn);
+        const float e = none ? 0.f : fast_exp2(sc[cb][t] - m[cb]);
         sc[cb][t] = e;
         l[cb] += e;
       }
