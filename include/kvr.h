@@ -195,7 +195,7 @@ kvr_status kvr_check_support(const int32_t* d_T, int32_t B, int32_t n_tokens,
  * kvr_build_runs - checks an explicit support like kvr_check_support and
  * coalesces it into its maximal runs of consecutive positions, the execution
  * intervals that Budgeted KV-Cache Repair sorts and coalesces a support into
- * (section 3.2, Algorithm 1's last step) and that sequential maximal-interval
+ * (section 3.2, the end of Algorithm 1) and that sequential maximal-interval
  * replay (section 7.1) traverses one at a time.  Seam sets get their runs
  * from kvr_build_repair_set; this call covers every other support (isolated
  * tokens, intervals, supports chosen by Semantic-Unit Refresh elsewhere).
@@ -425,10 +425,10 @@ kvr_status kvr_sur_scores(const void* d_E, kvr_dtype dtype, int32_t vocab, int32
 
 /*
  * kvr_sur_select - the selection of Semantic-Unit Refresh under an exact
- * budget (Budgeted KV-Cache Repair, section 7.3 and Algorithm 1, steps
- * 5-9): each unit scores the mean of its four largest token scores (all of
- * them below four); units are ranked by score, the earlier unit winning a
- * tie; whole units are admitted in ranked order while they fit the
+ * budget (Budgeted KV-Cache Repair, section 7.3, the selection part of
+ * Algorithm 1): each unit scores the mean of its four largest token scores
+ * (all of them below four); units are ranked by score, the earlier unit
+ * winning a tie; whole units are admitted in ranked order while they fit the
  * remaining allowance w = budget - |A|; the first that does not fit
  * contributes the width-w window with the largest sum of the forward-decay
  * envelope u_t = max(e^(r_t - r_max), e^(-1/16) u_{t-1}), u_0 = 0 (Eq. 8),

@@ -296,7 +296,7 @@ def kvr_sur_scores(E, dtype: int, suffix_ids, query_ids, r, stream=None) -> None
 
 def kvr_sur_select(r, unit_start, budget: int, pos0: int, unit_scores, T, run_start, run_len,
                    counts, ws, sync: bool = True, stream=None) -> Optional[Tuple[int, int, int]]:
-    """Algorithm 1 steps 5-9: returns (|T|, R, status) when ``sync``."""
+    """The selection part of Algorithm 1: returns (|T|, R, status) when ``sync``."""
     out = kvr_repair_set(_ptr(T), _ptr(run_start), _ptr(run_len), _ptr(counts), T.numel())
     h = (C.c_int32 * 3)() if sync else None
     _check(_lib.kvr_sur_select(_ptr(r), r.numel(), _ptr(unit_start), unit_start.numel(), budget,

@@ -390,7 +390,7 @@ __global__ __launch_bounds__(64 * kUnitWaves) void k_sur_unit_scores(
   if (lane == 0) out[u] = sum / static_cast<float>(take);
 }
 
-// Selection (Algorithm 1, steps 5-9) in one workgroup.
+// Selection (the selection part of Algorithm 1) in one workgroup.
 constexpr int kSelThreads = 1024;
 constexpr int kSurMaxUnits = 8192;
 
