@@ -107,8 +107,9 @@ def select(r: np.ndarray, starts: Sequence[int], B: int, pos0: int = 0) -> np.nd
     """The selection part of Algorithm 1 (section 7.3): rank units, admit
     whole units in ranked order while they fit the remaining allowance
     w = B - |A|; the first unit that does not fit contributes its best
-    width-w envelope window, which fills the allowance exactly; the chosen suffix indices are sorted.  Returns
-    global positions pos0 + i (int32, ascending)."""
+    width-w envelope window, which fills the allowance exactly; the chosen
+    suffix indices are sorted.  Returns global positions pos0 + i (int32,
+    ascending)."""
     r = np.asarray(r, dtype=np.float32)
     S = len(r)
     if not 0 <= B <= S:
