@@ -1058,13 +1058,16 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
       // raised wave priority so that the SIMD's arbiter prefers them to the
       // other wave's softmax
       __builtin_amdgcn_s_setprio(1);
-      if (grp == 0 && i + 2 < n) issue(c0 + i + 2, NEXT2);
       if (i > 0) pv(std::integral_constant<int, PREV>{});
       qk(bc);
       if (grp == 1 && i + 1 < n) wait_tile(i + 2 < n);
       lds_barrier();
-      // softmax (phase 2i + 1 for group A, 2i + 2 for group B)
+      // softmax (phase 2i + 1 for group A, 2i + 2 for group B).  Both groups
+      // issue their DMA here, so that the product phases carry no address
+      // arithmetic (group A's tile i + 2 goes into the stage tile i - 2
+      // left, whose last reads were B's PV in phase 2i - 1).
       __builtin_amdgcn_s_setprio(0);
+      if (grp == 0 && i + 2 < n) issue(c0 + i + 2, NEXT2);
       if (grp == 1 && i + 3 < n) issue(c0 + i + 3, NEXT3);
       softmax(c0 + i);
       if (grp == 0 && i + 1 < n) wait_tile(i + 2 < n);
