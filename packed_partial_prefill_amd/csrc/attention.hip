@@ -1034,10 +1034,11 @@ __global__ __launch_bounds__(kPPThreads, 1) void k_attn_pp(
     // a workgroup barrier.  Group B starts one barrier late (in phase 2i group
     // A takes the products of tile i while group B takes the softmax of tile
     // i - 1) and skips the barrier after its last softmax, so both pass 2n.
-    // The stages are managed per phase for all waves alike: in phase 2i the
-    // waves issue tile i + 2 (into the stage tile i - 2 left, whose last PV was
-    // in phase 2i - 1), and at the end of phase 2i + 1 each waits for its part
-    // of tile i + 1.
+    // Each group issues its part of a tile at the start of a softmax phase:
+    // group A tile i + 2 in phase 2i + 1, group B tile i + 3 in phase 2i + 2
+    // (both into the stage that tile's predecessor by four left, whose last
+    // reads ended a phase earlier), and at the end of phase 2i + 1 every wave
+    // waits for its part of tile i + 1.
     issue(c0, b0);
     if (n > 1) issue(c0 + 1, (b0 + 1) % kPPStages);
     wait_tile(n > 1);
