@@ -473,8 +473,10 @@ const char* kvr_last_error(void);
  * process-wide and not thread-safe.
  */
 enum {
-  KVR_KERNEL_PLAN = 0,      /* plan + RoPE table (once per call)          */
-  KVR_KERNEL_NORM = 1,      /* gather / residual sum + RMSNorm            */
+  KVR_KERNEL_PLAN = 0,      /* attention plan (kvr_biased_attention)     */
+  KVR_KERNEL_NORM = 1,      /* gather / residual sum + RMSNorm (the first
+                               launch of a repair also builds its plan and
+                               RoPE table)                               */
   KVR_KERNEL_QKV = 2,       /* QKV projection GEMM                         */
   KVR_KERNEL_ROPE = 3,      /* RoPE + K/V write-back + flags               */
   KVR_KERNEL_ATTN = 4,      /* packed causal attention                     */

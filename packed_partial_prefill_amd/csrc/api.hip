@@ -279,15 +279,15 @@ kvr_status run_stack(const kvr_config* cfg, int n_layers, const kvr_layer_weight
   void* attn_ws = base + L.attn;
   const int qkv_n = sh.qkv_cols();
 
-  // once per call: plan (Eq. 23-24) and RoPE table for the fixed positions
-  KVR_RUN(KVR_KERNEL_PLAN, stream, "plan and rope table",
-          kvr::launch_layer_tables(d_T, meta->gpos, B, sh.group, n_full, n_total, sh.d,
-                                   cfg->rope_theta, tab, stream));
-  // gather the selected rows once; RMSNorm for layer 0
-  KVR_RUN(KVR_KERNEL_NORM, stream, "gather+norm",
+  // gather the selected rows once; RMSNorm for layer 0; in the same launch,
+  // once per call, the plan (Eq. 23-24) and the RoPE table for the fixed
+  // positions
+  const kvr::LayerTables tabs{d_T,     meta->gpos, B,       sh.group, kvr::plan_tiles(B, sh.group),
+                              n_full,  n_total,    sh.d / 2, cfg->rope_theta, tab};
+  KVR_RUN(KVR_KERNEL_NORM, stream, "gather+norm, plan and rope table",
           kvr::launch_gather_norm(dt, x_in, gather ? d_T : nullptr, x_out,
                                   static_cast<const float*>(w[0].attn_norm), cfg->rms_eps, nbuf, B,
-                                  sh.hidden, stream));
+                                  sh.hidden, &tabs, stream));
   for (int l = 0; l < n_layers; ++l) {
     const kvr_layer_weights& W = w[l];
     kvr::WeightSegs qkv{{W.wq, W.wk, W.wv},

@@ -1,12 +1,14 @@
 // Integer kernels of the repair: the seam set T_tau and its runs, load-time
-// metadata, support validation, the per-query-tile attention plan and the
-// per-row RoPE table.
+// metadata, support validation, the per-query-tile attention plan (the
+// layer path builds it, with the per-row RoPE table, inside its first row
+// kernel: tables.h) and the key-tile map.
 //
 // Seam windows and the asymmetric true-prefix rule: cross-attention reuse
 // specification page, section 6.3.  Runs are the execution intervals of
 // "Budgeted KV-Cache Repair", section 3.2.  Plan: same page, section 13.2,
 // Eq. 23-24.
 #include "kvr_internal.h"
+#include "tables.h"
 
 namespace kvr {
 
@@ -245,34 +247,6 @@ __global__ __launch_bounds__(kBuildThreads) void k_check_support(
     result[0] = s_bad ? KVR_ERR_BAD_SUPPORT : (s_bad_pos ? KVR_ERR_INVALID_ARGUMENT : KVR_OK);
 }
 
-// Attention plan entry t: first KV tile only partly visible to query tile t
-// (n_full) and tiles it needs (n_total).
-__device__ __forceinline__ void plan_entry(const int32_t* __restrict__ T, int B, int group, int t,
-                                           int32_t* __restrict__ n_full,
-                                           int32_t* __restrict__ n_total) {
-  const int P = B * group;
-  const int p0 = t * KVR_ATTN_QROWS;
-  const int p1 = min(P, p0 + KVR_ATTN_QROWS) - 1;
-  const int u_min = T[p0 / group], u_max = T[p1 / group];
-  n_full[t] = (u_min + 1) / KVR_ATTN_KV_TILE;
-  n_total[t] = (u_max + KVR_ATTN_KV_TILE) / KVR_ATTN_KV_TILE;
-}
-
-// cos / sin of g * theta^(-2i/d) for packed row r and frequency i, built in
-// float64 and stored as a float32 pair of the table [B][d/2].  g is the
-// row's global position: gpos[T[r]], or T[r] itself when there is no map.
-__device__ __forceinline__ void rope_entry(const int32_t* __restrict__ T,
-                                           const int32_t* __restrict__ gpos, int half,
-                                           double theta, int idx, float2* __restrict__ tab) {
-  const int r = idx / half, i = idx - r * half;
-  const double inv = pow(theta, -(2.0 * i) / (2.0 * half));
-  const int g = gpos ? gpos[T[r]] : T[r];
-  const double ang = static_cast<double>(g) * inv;
-  double sn, cs;
-  sincos(ang, &sn, &cs);
-  tab[idx] = make_float2(static_cast<float>(cs), static_cast<float>(sn));
-}
-
 __global__ void k_build_plan(const int32_t* __restrict__ T, int B, int group, int n_tiles,
                              int32_t* __restrict__ n_full, int32_t* __restrict__ n_total) {
   const int t = blockIdx.x * blockDim.x + threadIdx.x;
@@ -294,18 +268,6 @@ __global__ void k_tile_map(const int32_t* __restrict__ T, int B, int n_kv,
   first_q[c] = lo;
 }
 
-// Both tables of a layer call in one launch: plan entries first, then the
-// rope table.
-__global__ void k_layer_tables(const int32_t* __restrict__ T, const int32_t* __restrict__ gpos,
-                               int B, int group, int n_tiles, int32_t* __restrict__ n_full,
-                               int32_t* __restrict__ n_total, int half, double theta,
-                               float2* __restrict__ tab) {
-  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx < n_tiles)
-    plan_entry(T, B, group, idx, n_full, n_total);
-  else if (idx - n_tiles < B * half)
-    rope_entry(T, gpos, half, theta, idx - n_tiles, tab);
-}
 
 }  // namespace
 
@@ -359,16 +321,6 @@ hipError_t launch_tile_map(const int32_t* T, int B, int n_tokens, int32_t* first
   if (n_kv == 0) return hipSuccess;
   hipLaunchKernelGGL(k_tile_map, dim3((n_kv + 255) / 256), dim3(256), 0, stream, T, B, n_kv,
                      first_q);
-  return hipGetLastError();
-}
-
-hipError_t launch_layer_tables(const int32_t* T, const int32_t* gpos, int B, int group,
-                              int32_t* n_full, int32_t* n_total, int head_dim, double theta,
-                              float2* tab, hipStream_t stream) {
-  const int n = plan_tiles(B, group) + B * (head_dim / 2);
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_layer_tables, dim3((n + 255) / 256), dim3(256), 0, stream, T, gpos, B,
-                     group, plan_tiles(B, group), n_full, n_total, head_dim / 2, theta, tab);
   return hipGetLastError();
 }
 

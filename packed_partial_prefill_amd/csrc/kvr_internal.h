@@ -34,18 +34,29 @@ hipError_t launch_tile_map(const int32_t* T, int B, int n_tokens, int32_t* first
                            hipStream_t stream);
 hipError_t launch_build_plan(const int32_t* T, int B, int group, int32_t* n_full,
                              int32_t* n_total, hipStream_t stream);
-// launch_build_plan plus the RoPE table (cos, sin of g_r * theta^(-2i/d) as
-// float32 pairs [B][d/2], computed in float64, g_r = gpos[T[r]] or T[r] when
-// gpos is NULL) in one launch
-hipError_t launch_layer_tables(const int32_t* T, const int32_t* gpos, int B, int group,
-                              int32_t* n_full, int32_t* n_total, int head_dim, double theta,
-                              float2* tab, hipStream_t stream);
+// The per-call tables of a layer repair: the attention plan (n_full and
+// n_total of each of n_tiles query tiles) and the RoPE table (cos, sin of
+// g_r * theta^(-2i/d) as float32 pairs [B][half], computed in float64,
+// g_r = gpos[T[r]] or T[r] when gpos is NULL).  Entries 0 .. n_tiles - 1 are
+// plan entries, the next B * half the table's.
+struct LayerTables {
+  const int32_t* T;
+  const int32_t* gpos;
+  int B, group, n_tiles;
+  int32_t* n_full;
+  int32_t* n_total;
+  int half;
+  double theta;
+  float2* tab;
+  int entries() const { return n_tiles + B * half; }
+};
 
 // ---- norm.hip ---------------------------------------------------------------
 // x_res[r] = x_in[gather ? T[r] : r]; n_out[r] = RMSNorm(x_res[r]) * gamma.
+// With tabs, further workgroups of the same launch build those tables.
 hipError_t launch_gather_norm(kvr_dtype dt, const float* x_in, const int32_t* gather_T,
                               float* x_res, const float* gamma, float eps, void* n_out, int B,
-                              int hidden, hipStream_t stream);
+                              int hidden, const LayerTables* tabs, hipStream_t stream);
 // x_res[r] += sum_s part[s][r]; if gamma: n_out[r] = RMSNorm(x_res[r]) * gamma.
 hipError_t launch_residual_norm(kvr_dtype dt, float* x_res, const float* part, int splits,
                                 size_t split_stride, const float* gamma, float eps, void* n_out,

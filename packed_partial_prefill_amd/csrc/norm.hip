@@ -5,6 +5,7 @@
 // thread owns float4 chunks of the row (hidden is a multiple of 64).
 #include "common.h"
 #include "kvr_internal.h"
+#include "tables.h"
 
 namespace kvr {
 
@@ -34,13 +35,19 @@ __device__ __forceinline__ float4 scale4(float4 v, float s, float4 g) {
 // x_res[r] = x_in[gather_T[r]] (or x_in[r]); n_out[r] = RMSNorm(x_res[r]) * gamma.
 // NC = float4 chunks per thread; chunks past the row's end load its last
 // chunk (discarded) so that every load is unconditional and all of them,
-// gamma's included, are in flight together.
+// gamma's included, are in flight together.  Workgroups past the B rows
+// build the call's tables, one entry per thread, in the shadow of the rows.
 template <typename T, int NC>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_gather_norm(
     const float* __restrict__ x_in, const int32_t* __restrict__ gather_T, float* x_res,
-    const float* __restrict__ gamma, float eps, T* __restrict__ n_out, int hidden) {
+    const float* __restrict__ gamma, float eps, T* __restrict__ n_out, int hidden, int B,
+    LayerTables tabs) {
   __shared__ float red[16];
   const int r = blockIdx.x;
+  if (r >= B) {
+    table_entry(tabs, (r - B) * kRowThreads + static_cast<int>(threadIdx.x));
+    return;
+  }
   const int h4 = hidden >> 2;
   const size_t src = gather_T ? static_cast<size_t>(gather_T[r]) : static_cast<size_t>(r);
   const float4* xr = reinterpret_cast<const float4*>(x_in + src * hidden);
@@ -147,29 +154,33 @@ void launch_residual_norm_t(float* x_res, const float* part, int splits, size_t 
 template <typename T, int NC>
 void launch_gather_norm_t(const float* x_in, const int32_t* gather_T, float* x_res,
                           const float* gamma, float eps, T* n_out, int B, int hidden,
-                          hipStream_t stream) {
+                          const LayerTables& tabs, hipStream_t stream) {
   if constexpr (NC < kMaxChunks) {
     if (hidden > 4 * kRowThreads * NC) {
-      launch_gather_norm_t<T, NC + 1>(x_in, gather_T, x_res, gamma, eps, n_out, B, hidden, stream);
+      launch_gather_norm_t<T, NC + 1>(x_in, gather_T, x_res, gamma, eps, n_out, B, hidden, tabs,
+                                      stream);
       return;
     }
   }
-  hipLaunchKernelGGL((k_gather_norm<T, NC>), dim3(B), dim3(kRowThreads), 0, stream, x_in, gather_T,
-                     x_res, gamma, eps, n_out, hidden);
+  const int table_groups = (tabs.entries() + kRowThreads - 1) / kRowThreads;
+  hipLaunchKernelGGL((k_gather_norm<T, NC>), dim3(B + table_groups), dim3(kRowThreads), 0, stream,
+                     x_in, gather_T, x_res, gamma, eps, n_out, hidden, B, tabs);
 }
 
 }  // namespace
 
 hipError_t launch_gather_norm(kvr_dtype dt, const float* x_in, const int32_t* gather_T,
                               float* x_res, const float* gamma, float eps, void* n_out, int B,
-                              int hidden, hipStream_t stream) {
+                              int hidden, const LayerTables* tabs, hipStream_t stream) {
   if (B == 0) return hipSuccess;
+  const LayerTables none{nullptr, nullptr, 0, 1, 0, nullptr, nullptr, 0, 0.0, nullptr};
+  const LayerTables& t = tabs ? *tabs : none;
   if (dt == KVR_BF16)
     launch_gather_norm_t<bf16_t, 1>(x_in, gather_T, x_res, gamma, eps, static_cast<bf16_t*>(n_out),
-                                    B, hidden, stream);
+                                    B, hidden, t, stream);
   else
     launch_gather_norm_t<float, 1>(x_in, gather_T, x_res, gamma, eps, static_cast<float*>(n_out),
-                                   B, hidden, stream);
+                                   B, hidden, t, stream);
   return hipGetLastError();
 }
 
