@@ -624,7 +624,7 @@ constexpr bool kAttnXcdOrder = true;
 constexpr int kSkMinTiles = 4;
 // cost of a piece's prologue and epilogue in KV tiles, charged per segment in
 // the stream-K split (a workgroup with an extra piece takes fewer tiles)
-constexpr int kSkPieceCost = 2;
+constexpr int kSkPieceCost = 3;
 
 template <int D>
 struct PPLds {
