@@ -36,7 +36,8 @@ __device__ __forceinline__ float4 scale4(float4 v, float s, float4 g) {
 // NC = float4 chunks per thread; chunks past the row's end load its last
 // chunk (discarded) so that every load is unconditional and all of them,
 // gamma's included, are in flight together.  Workgroups past the B rows
-// build the call's tables, one entry per thread, in the shadow of the rows.
+// build the call's tables (LayerTables), one entry per thread; they run
+// beside the row workgroups, so the tables need no launch of their own.
 template <typename T, int NC>
 __global__ __launch_bounds__(kRowThreads) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_gather_norm(
     const float* __restrict__ x_in, const int32_t* __restrict__ gather_T, float* x_res,
