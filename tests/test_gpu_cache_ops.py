@@ -80,6 +80,8 @@ def test_inference_alpha_beta_zero_without_metadata_is_plain_attention():
     (32, 8, 128, 2048, list(range(2039, 2048))),     # 36 pairs: two column blocks
     (28, 4, 128, 4096, [100, 3000]),                 # chunks past the last query skipped
     (8, 8, 128, 513, list(range(0, 513, 9))),        # G = 1, 58 pairs
+    (4, 1, 128, 777, [10, 400, 776]),                # one KV head; last step holds 9 keys
+    (12, 2, 128, 20000, list(range(19995, 20000))),  # 30 pairs, 157 steps over 79 workgroups
 ])
 def test_inference_decode_path_shapes(hq, hkv, d, n, pos):
     w = _small(f"inf-decode-{hq}-{hkv}-{d}-{n}", 205, "bf16", hq, hkv, d, n, 128)
