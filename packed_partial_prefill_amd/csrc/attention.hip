@@ -1250,7 +1250,8 @@ struct DecLds {
   static constexpr int ot = 4 * kDecMaxPairs * otRow * 4;            // O of 4 waves
   static constexpr int body = kv + flags > ot ? kv + flags : ot;
   static constexpr int ml = 4 * kDecMaxPairs * 2 * 4;
-  static constexpr int total = body + ml;
+  static constexpr int wt = kDecMaxPairs * 4 * 4;                    // per-pair wave weights
+  static constexpr int total = body + ml + wt;
   static_assert(wave + slot < 65536, "ds offset field");
 };
 
@@ -1561,29 +1562,40 @@ __global__ __launch_bounds__(kAttnThreads, 1) void k_attn_decode(
   const int npairs = min(P, PAIRS);
   const size_t slot0 = (static_cast<size_t>(c) * Hkv + g) * P;
   const float* ot_all = reinterpret_cast<const float*>(lds);
+  // per pair: the four waves' weights exp2(m_w - M) (0 for a wave that saw
+  // no key of it), stored for the O pass, and the partial's maximum and sum
+  float* wt = ml + 4 * kDecMaxPairs * 2;
+  for (int p = tid; p < npairs; p += kAttnThreads) {
+    float mw[4], M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      mw[w] = ml[(w * kDecMaxPairs + p) * 2];
+      M = fmaxf(M, mw[w]);
+    }
+    float e[4], ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      e[w] = mw[w] == -INFINITY ? 0.f : fast_exp2(mw[w] - M);
+      ls += e[w] * ml[(w * kDecMaxPairs + p) * 2 + 1];
+    }
+    *reinterpret_cast<float4*>(wt + p * 4) = make_float4(e[0], e[1], e[2], e[3]);
+    part_ml[(slot0 + p) * 2] = M;
+    part_ml[(slot0 + p) * 2 + 1] = ls;
+  }
+  __syncthreads();
+  // O: every load of an element's pass is independent of the others (one
+  // LDS round trip per element instead of a chain through the maximum)
   for (int idx = tid; idx < npairs * (D / 4); idx += kAttnThreads) {
     const int p = idx / (D / 4), d = (idx - p * (D / 4)) * 4;
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, ml[(w * kDecMaxPairs + p) * 2]);
+    const float4 e4 = *reinterpret_cast<const float4*>(wt + p * 4);
+    const float e[4] = {e4.x, e4.y, e4.z, e4.w};
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    float ls = 0.f;
-    if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mw = ml[(w * kDecMaxPairs + p) * 2];
-        if (mw == -INFINITY) continue;
-        const float e = fast_exp2(mw - M);
-        ls += e * ml[(w * kDecMaxPairs + p) * 2 + 1];
-        const float4 v = *reinterpret_cast<const float4*>(ot_all + (w * kDecMaxPairs + p) * L::otRow + d);
-        acc.x += e * v.x; acc.y += e * v.y; acc.z += e * v.z; acc.w += e * v.w;
-      }
+    for (int w = 0; w < 4; ++w) {
+      const float4 v = *reinterpret_cast<const float4*>(ot_all + (w * kDecMaxPairs + p) * L::otRow + d);
+      acc.x += e[w] * v.x; acc.y += e[w] * v.y; acc.z += e[w] * v.z; acc.w += e[w] * v.w;
     }
     *reinterpret_cast<float4*>(part_o + (slot0 + p) * D + d) = acc;
-    if (d == 0) {
-      part_ml[(slot0 + p) * 2] = M;
-      part_ml[(slot0 + p) * 2 + 1] = ls;
-    }
   }
 }
 
