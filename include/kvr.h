@@ -473,7 +473,7 @@ const char* kvr_last_error(void);
  * process-wide and not thread-safe.
  */
 enum {
-  KVR_KERNEL_PLAN = 0,      /* attention plan (kvr_biased_attention)     */
+  KVR_KERNEL_PLAN = 0,      /* attention plan (kvr_biased_attention, float32) */
   KVR_KERNEL_NORM = 1,      /* gather / residual sum + RMSNorm (the first
                                launch of a repair also builds its plan and
                                RoPE table)                               */
@@ -485,7 +485,8 @@ enum {
   KVR_KERNEL_GATEUP = 7,    /* gate/up GEMM with SwiGLU epilogue           */
   KVR_KERNEL_DOWN = 8,      /* down projection GEMM                        */
   KVR_KERNEL_FINAL = 9,     /* last residual sum into x_out                */
-  KVR_KERNEL_QPREP = 10,    /* query scaling (kvr_biased_attention)        */
+  KVR_KERNEL_QPREP = 10,    /* query scaling and attention plan
+                               (kvr_biased_attention, bf16)                 */
   KVR_KERNEL_SHIFT = 11,    /* Shift re-rotation / move (kvr_shift_cache)  */
   KVR_KERNEL_SUR_SCORE = 12,/* SUR token relevance (kvr_sur_scores)        */
   KVR_KERNEL_SUR_SELECT = 13,/* SUR unit scores + selection (kvr_sur_select) */

@@ -383,15 +383,18 @@ kvr_status run_biased_attention(const kvr_config* cfg, const kvr::Shape& sh, con
   void* attn_ws = base + L.attn;
   // float32 storage attends on the caller's queries directly (the row kernel
   // applies 1/sqrt(d) itself); bf16 takes them scaled and rounded once
+  // (bf16: the query prep launch also builds the attention plan)
   const void* qk = q;
   if (dt == KVR_BF16) {
     qk = base + L.q;
-    KVR_RUN(KVR_KERNEL_QPREP, stream, "query prep",
+    KVR_RUN(KVR_KERNEL_QPREP, stream, "query prep and plan",
             kvr::launch_prep_queries(dt, q, static_cast<size_t>(B) * sh.hq * sh.d,
-                                     kvr::attention_q_scale(dt, sh.d), base + L.q, stream));
+                                     kvr::attention_q_scale(dt, sh.d), base + L.q, d_pos, B,
+                                     sh.group, n_full, n_total, stream));
+  } else {
+    KVR_RUN(KVR_KERNEL_PLAN, stream, "plan",
+            kvr::launch_build_plan(d_pos, B, sh.group, n_full, n_total, stream));
   }
-  KVR_RUN(KVR_KERNEL_PLAN, stream, "plan",
-          kvr::launch_build_plan(d_pos, B, sh.group, n_full, n_total, stream));
   KVR_RUN(KVR_KERNEL_ATTN, stream, "attention",
           kvr::launch_attention(dt, qk, cache.k, cache.v, flags, d_pos, B, n_tokens, sh,
                                 cfg->alpha, cfg->beta, n_full, n_total, attn_ws, o, stream));

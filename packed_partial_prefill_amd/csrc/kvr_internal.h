@@ -97,8 +97,10 @@ hipError_t launch_rope_writeback(kvr_dtype dt, const float* qkv_part, int splits
                                  void* v_cache, uint8_t* flags, hipStream_t stream);
 
 // q_out[i] = q[i] * scale stored in dtype dt (n elements, a multiple of 4).
+// also builds the attention plan (n_full, n_total) of the query positions
 hipError_t launch_prep_queries(kvr_dtype dt, const float* q, size_t n, float scale, void* q_out,
-                               hipStream_t stream);
+                               const int32_t* pos, int B, int group, int32_t* n_full,
+                               int32_t* n_total, hipStream_t stream);
 
 // ---- shift.hip ----------------------------------------------------------------
 constexpr int kShiftMaxLayers = 32;   // layers per launch (kernel-argument arrays)

@@ -10,6 +10,7 @@
 // (cross-attention reuse page, 6.4: write-back sets type <- global).
 #include "common.h"
 #include "kvr_internal.h"
+#include "tables.h"
 
 namespace kvr {
 
@@ -128,11 +129,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 4))
 }
 
 // Queries handed in from outside the repair (inference mode): scaled by the
-// attention kernel's score factor and stored in the cache's dtype.
+// attention kernel's score factor and stored in the cache's dtype.  The
+// workgroups past the queries' build the attention plan of the query
+// positions ("Budgeted KV-Cache Repair", section 13.2, Eq. 23-24), so that
+// it takes no launch of its own.
 template <typename T>
-__global__ __launch_bounds__(kThreads) void k_prep_queries(const float4* __restrict__ q,
-                                                           size_t n4, float scale,
-                                                           T* __restrict__ out) {
+__global__ __launch_bounds__(kThreads) void k_prep_queries(
+    const float4* __restrict__ q, size_t n4, float scale, T* __restrict__ out, unsigned qblocks,
+    const int32_t* __restrict__ pos, int B, int group, int n_tiles, int32_t* __restrict__ n_full,
+    int32_t* __restrict__ n_total) {
+  if (blockIdx.x >= qblocks) {
+    const int t = static_cast<int>(blockIdx.x - qblocks) * kThreads + threadIdx.x;
+    if (t < n_tiles) plan_entry(pos, B, group, t, n_full, n_total);
+    return;
+  }
   const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
   if (i >= n4) return;
   const float4 v = q[i];
@@ -142,16 +152,21 @@ __global__ __launch_bounds__(kThreads) void k_prep_queries(const float4* __restr
 }  // namespace
 
 hipError_t launch_prep_queries(kvr_dtype dt, const float* q, size_t n, float scale, void* q_out,
-                               hipStream_t stream) {
+                               const int32_t* pos, int B, int group, int32_t* n_full,
+                               int32_t* n_total, hipStream_t stream) {
   const size_t n4 = n / 4;
-  if (n4 == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((n4 + kThreads - 1) / kThreads));
+  const int n_tiles = plan_tiles(B, group);
+  const unsigned qblocks = static_cast<unsigned>((n4 + kThreads - 1) / kThreads);
+  const dim3 grid(qblocks + static_cast<unsigned>((n_tiles + kThreads - 1) / kThreads));
+  if (grid.x == 0) return hipSuccess;
   if (dt == KVR_BF16)
     hipLaunchKernelGGL(k_prep_queries<bf16_t>, grid, dim3(kThreads), 0, stream,
-                       reinterpret_cast<const float4*>(q), n4, scale, static_cast<bf16_t*>(q_out));
+                       reinterpret_cast<const float4*>(q), n4, scale, static_cast<bf16_t*>(q_out),
+                       qblocks, pos, B, group, n_tiles, n_full, n_total);
   else
     hipLaunchKernelGGL(k_prep_queries<float>, grid, dim3(kThreads), 0, stream,
-                       reinterpret_cast<const float4*>(q), n4, scale, static_cast<float*>(q_out));
+                       reinterpret_cast<const float4*>(q), n4, scale, static_cast<float*>(q_out),
+                       qblocks, pos, B, group, n_tiles, n_full, n_total);
   return hipGetLastError();
 }
 
